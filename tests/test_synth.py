@@ -1,0 +1,45 @@
+"""The seeded generators: determinism and the stated recipe."""
+import numpy as np
+
+import oracle as O
+from bit_quantized_expert_router_amd import synth
+
+
+def test_blob_deterministic_and_scales_in_range():
+    a = synth.expert_blob(synth.rng_for(0, 0, 1), 3, 1024, 256)
+    b = synth.expert_blob(synth.rng_for(0, 0, 1), 3, 1024, 256)
+    c = synth.expert_blob(synth.rng_for(0, 1, 1), 3, 1024, 256)
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    blob = O.ExpertBlob(a, 3, 1024, 256)
+    for e in range(3):
+        for off, (R, K) in ((0, (256, 1024)), (81920, (256, 1024)), (163840, (1024, 256))):
+            codes, sc = O.decode_matrix(a, e * blob.stride + off, R, K)
+            s = sc.astype(np.float64)
+            assert s.min() >= 0.0099 and s.max() <= 0.0501
+            hist = np.bincount(codes.reshape(-1), minlength=4) / codes.size
+            assert np.all(np.abs(hist - 0.25) < 0.01)
+
+
+def test_bf16_rounding():
+    v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -9], dtype=np.float32)
+    bits = synth.bf16_bits(v)
+    # 1+2^-8 is a tie between 1 and 1+2^-7 -> even (1.0); 1+3*2^-8 -> 1+2^-6
+    assert list(bits) == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x3F80]
+    assert np.array_equal(synth.bf16_to_f32(bits)[[0, 3]], [1.0, -2.5])
+
+
+def test_activations_and_logits_deterministic():
+    x1, v1 = synth.activations(synth.rng_for(1, 0, 2), 4, 3072)
+    x2, v2 = synth.activations(synth.rng_for(1, 0, 2), 4, 3072)
+    assert x1.dtype == np.uint16 and np.array_equal(x1, x2)
+    l1 = synth.router_logits(synth.rng_for(1, 0, 3), v1, 512)
+    l2 = synth.router_logits(synth.rng_for(1, 0, 3), v2, 512)
+    assert l1.dtype == np.float32 and np.array_equal(l1, l2)
+    assert 0.5 < l1.std() < 2.0
+
+
+def test_zipf_logits_skew():
+    lg = synth.zipf_logits(synth.rng_for(2, 0, 3), 4000, 512)
+    ids, _ = O.route_topk(lg, 1)
+    counts = np.bincount(ids[:, 0], minlength=512)
+    assert counts.max() > 10 * np.median(counts[counts > 0])
