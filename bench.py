@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE expert layer on 2-bit weights (one MI355X).
+
+A step is one MoE layer for one batch of synthetic input through the HIP
+library: router top-k (moe_route_topk) then the expert layer.  The headline
+workload is the decode step of one token on a 512-expert layer (top-10 + 1
+shared, hidden 3072, intermediate 768, 2,211,840 bytes per expert); the same
+run also measures verify windows of 2 and 3 tokens and a 1024-token prefill
+chunk (router histogram + grouped expert GEMMs + combine) and reports them in
+the same JSON line.  Weights rotate over 16 distinct layers (about 18 GB) so
+that no step finds its experts in the 256 MB last-level cache.
+
+Prints one JSON line (see the keys below).  `--gpus N` with N > 1 exits with
+an error: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 MFMA, TFLOP/s
+
+E, H, I, K = 512, 3072, 768, 10
+EXPERT_BYTES = 3 * I * H * 5 // 16      # 2,211,840
+MAT_BYTES = I * H * 5 // 16             # 737,280
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--layers", type=int, default=16)
+    ap.add_argument("--prefill-steps", type=int, default=40)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", default="", help="decode1|decode2|decode3|prefill (profiling runs)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this size first (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs the MoE layer on one GPU only; "
+              "--gpus must be 1 (no multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_quantized_expert_router_amd import binding as B
+    from bit_quantized_expert_router_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # ---------------------------------------------------------------- weights
+    t0 = time.time()
+    layers = []
+    for l in range(args.layers):
+        ex = synth.device_expert_blob(E, H, I, synth.torch_seed(1, l, 1), dev)
+        sh = synth.device_expert_blob(1, H, I, synth.torch_seed(1, l, 2), dev)
+        layers.append(B.Layer(ex, sh, E, H, I, synth.expert_stride(H, I)))
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+
+    results = {}
+    prof_kernels = {}
+
+    def timed(fn, n_steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(n_steps):
+            fn(warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n_steps
+
+    def hooked(fn, n_steps, start):
+        """Same steps again with the library's per-kernel hipEvent hooks on."""
+        torch.cuda.synchronize()
+        B.profile_reset()
+        B.profile_enable(True)
+        for i in range(n_steps):
+            fn(start + i)
+        torch.cuda.synchronize()
+        B.profile_enable(False)
+        return {k: v for k, v in B.profile_results().items() if v[0] > 0}
+
+    # ---------------------------------------------------------------- decode
+    def decode_case(T, kind, n_steps, warmup):
+        total = n_steps * 2 + warmup
+        rng = synth.rng_for(1, 100 + T, 0)
+        xd, xv = synth.activations(rng, min(total, 64) * T, H, "bf16")
+        xs = torch.from_numpy(xd.view(np.int16)).view(torch.bfloat16).to(dev).view(-1, T, H)
+        nx = xs.shape[0]
+        if kind == "router":
+            lg = synth.router_logits(rng, np.tile(xv, (1, 1))[: nx * T], E).reshape(nx, T, E)
+            lg = np.concatenate([lg] * ((total + nx - 1) // nx))[:total]
+        else:
+            lg = synth.zipf_logits(rng, total * T, E).reshape(total, T, E)
+        logits = torch.from_numpy(np.ascontiguousarray(lg)).to(dev)
+        ids = torch.empty((total, T, K), dtype=torch.int32, device=dev)
+        wts = torch.empty((total, T, K), dtype=torch.float32, device=dev)
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+        ws = B.workspace(B.MOE_OP_DECODE, T, E, K, H, I, dev)
+
+        def step(i):
+            L = layers[i % len(layers)]
+            B.moe_route_topk(logits[i], K, ids[i], wts[i])
+            B.moe_expert_forward_decode(L, xs[i % nx], ids[i], wts[i], out, None, 0, ws)
+
+        ms = timed(step, n_steps, warmup)
+        kern = hooked(step, n_steps, warmup + n_steps)
+        idh = ids.cpu().numpy()
+        distinct = np.array([len(np.unique(idh[i])) for i in range(total)])
+        slots = distinct[warmup:warmup + n_steps].mean() + 1
+        wbytes = slots * EXPERT_BYTES
+        io = T * H * 2 + T * H * 4 + T * E * 4 + T * K * 8
+        step_bytes = wbytes + io
+        gu = kern.get("decode_gateup_kernel", (1, float("nan")))
+        dn = kern.get("decode_down_kernel", (1, float("nan")))
+        rt = kern.get("route_topk_kernel", (1, float("nan")))
+        gu_ms = gu[1] / gu[0]
+        gu_bytes = slots * 2 * MAT_BYTES + T * H * 2
+        return {
+            "T": T, "routing": kind, "ms_per_layer": ms, "tokens_per_s": T * 1000.0 / ms,
+            "distinct_experts_per_step": float(slots - 1),
+            "algorithmic_bytes_per_step": float(step_bytes),
+            "GBps": step_bytes / ms / 1e6, "hbm_frac": step_bytes / ms / 1e6 / HBM_PEAK_GBS,
+            "kernel_ms": {"route_topk": rt[1] / rt[0], "decode_gateup": gu_ms,
+                          "decode_down": dn[1] / dn[0]},
+            "gateup_bytes_per_launch": float(gu_bytes),
+            "gateup_GBps": gu_bytes / gu_ms / 1e6,
+        }
+
+    # --------------------------------------------------------------- prefill
+    def prefill_case(T, n_steps, warmup):
+        total = n_steps * 2 + warmup
+        rng = synth.rng_for(3, 0, T)
+        nvar = 4
+        xd, xv = synth.activations(rng, nvar * T, H, "bf16")
+        xs = torch.from_numpy(xd.view(np.int16)).view(torch.bfloat16).to(dev).view(nvar, T, H)
+        lgs = [synth.biased_logits(rng, synth.router_logits(rng, xv[v * T:(v + 1) * T], E))
+               for v in range(nvar)]
+        logits = torch.from_numpy(np.stack(lgs)).to(dev)
+        r = {n: torch.empty(s, dtype=dt, device=dev) for n, s, dt in [
+            ("ids", (T, K), torch.int32), ("w", (T, K), torch.float32), ("counts", (E,), torch.int32),
+            ("offsets", (E + 1,), torch.int32), ("sp", (T * K,), torch.int32),
+            ("pp", (T * K,), torch.int32)]}
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+        wsr = B.workspace(B.MOE_OP_ROUTE, T, E, K, H, I, dev)
+        ws = B.workspace(B.MOE_OP_PREFILL, T, E, K, H, I, dev)
+
+        def step(i):
+            L = layers[i % len(layers)]
+            v = i % nvar
+            B.moe_route_topk(logits[v], K, r["ids"], r["w"], r["counts"], r["offsets"], r["sp"],
+                             r["pp"], wsr)
+            B.moe_expert_forward_prefill(L, xs[v], r["ids"], r["w"], r["counts"], r["offsets"],
+                                         r["sp"], r["pp"], out, None, 0, ws)
+
+        ms = timed(step, n_steps, warmup)
+        kern = hooked(step, n_steps, warmup + n_steps)
+        nonempty = []
+        for v in range(nvar):
+            ids_v = torch.topk(logits[v], K, dim=1).indices.cpu().numpy()
+            nonempty.append(len(np.unique(ids_v)))
+        ne = float(np.mean(nonempty))
+        wbytes = (ne + 1) * EXPERT_BYTES
+        step_bytes = wbytes + T * H * 2 + T * H * 4 + T * E * 4
+        flops = (T * K + T) * 2 * 3 * H * I
+        kms = {k.replace("_kernel", ""): v[1] / v[0] for k, v in kern.items()}
+        gemm_ms = kms.get("prefill_gateup", 0) + kms.get("prefill_down", 0)
+        gu_ms = kms.get("prefill_gateup", float("nan"))
+        gu_flops = (T * K + T) * 2 * 2 * H * I
+        gu_bytes = (ne + 1) * 2 * MAT_BYTES + T * H * 2
+        return {
+            "T": T, "routing": "router+bias N(0,0.5)", "ms_per_layer": ms,
+            "tokens_per_s": T * 1000.0 / ms, "nonempty_experts": ne,
+            "algorithmic_bytes_per_step": float(step_bytes), "flops_per_step": float(flops),
+            "GBps": step_bytes / ms / 1e6, "hbm_frac": step_bytes / ms / 1e6 / HBM_PEAK_GBS,
+            "TFLOPs": flops / ms / 1e9, "mfma_frac": flops / ms / 1e9 / MFMA_F16_PEAK_TFLOPS,
+            "kernel_ms": kms, "grouped_gemm_ms": gemm_ms,
+            "gateup_TFLOPs": gu_flops / gu_ms / 1e9, "gateup_GBps": gu_bytes / gu_ms / 1e6,
+        }
+
+    only = args.only
+    if only in ("", "decode1"):
+        results["decode_T1"] = decode_case(1, "router", args.steps, args.warmup)
+    if only in ("", "decode2"):
+        results["decode_T2"] = decode_case(2, "zipf", args.steps // 2, args.warmup)
+    if only in ("", "decode3"):
+        results["decode_T3"] = decode_case(3, "zipf", args.steps // 2, args.warmup)
+    if only in ("", "prefill"):
+        results["prefill_T1024"] = prefill_case(1024, args.prefill_steps, max(4, args.warmup // 4))
+
+    # ------------------------------------------------------------ cpu baseline
+    cpu = None
+    if not args.no_cpu_baseline and only == "":
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    head = results.get("decode_T1") or next(iter(results.values()))
+    line = {
+        "metric": "MoE-layer tokens/s (decode B=1..3, prefill 1024 chunk); HBM GB/s % peak",
+        "value": round(head["tokens_per_s"], 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_layer"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "moe_layer_decode_T1: route + expert layer, 1 token, 512 experts top-10 + 1 shared, "
+                        "hidden 3072, inter 768, Q2 2-bit weights (2,211,840 B/expert), "
+                        f"{args.layers} rotating layers",
+            "tokens_per_step": 1, "experts": E, "top_k": K, "hidden": H, "inter": I,
+            "parallelism": "single_gpu",
+        },
+    }
+    if "decode_T1" in results:
+        d = results["decode_T1"]
+        line["roofline"] = {
+            "bound": "hbm", "kernel": "decode_gateup_kernel",
+            "achieved": round(d["gateup_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(d["gateup_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+            "layer_GBps": round(d["GBps"], 1), "layer_frac": round(d["hbm_frac"], 4),
+        }
+    line["results"] = results
+    if cpu:
+        line["cpu_baseline"] = cpu
+    line["weights_generated_s"] = round(gen_s, 1)
+    print(json.dumps(line))
+
+
+def cpu_baseline(seconds: float):
+    """The fp64 oracle on the host cores, decode of one token on the same
+    workload shape (512 experts top-10 + shared, H 3072, I 768), for a bounded
+    number of steps (about `seconds` of CPU work)."""
+    import oracle as O
+    from bit_quantized_expert_router_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    rng = synth.rng_for(1, 500, 0)
+    steps = 0
+    t0 = time.perf_counter()
+    spent = 0.0
+    while spent < seconds and steps < 64:
+        blob = synth.expert_blob(rng, E, H, I)          # fresh layer: nothing cached
+        sh = synth.expert_blob(rng, 1, H, I)
+        ob = O.ExpertBlob(blob, E, H, I, shared=sh, cache=0)
+        _, xv = synth.activations(rng, 1, H, "bf16")
+        lg = synth.router_logits(rng, xv, E)
+        t1 = time.perf_counter()
+        ids, w = O.route_topk(lg, K)
+        O.moe_layer(xv, ids, w, ob)
+        spent += time.perf_counter() - t1
+        steps += 1
+    return {"value": round(steps / spent, 4), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{steps} decode steps of 1 token (route + 11 experts decoded from the 2-bit "
+                      f"bytes and evaluated in float64), {spent:.1f} s of oracle time; input "
+                      f"generation excluded; cores = BLAS threads"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,303 @@
+// C-ABI entry points: argument validation (everything is checked before the
+// first enqueue), workspace sizing, launch, status codes and the optional
+// hipEvent measurement hooks.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe_q2.h"
+#include "launch.h"
+
+namespace moeq2 {
+namespace {
+
+thread_local std::string g_last_error;
+
+__attribute__((format(printf, 2, 3))) int fail(int status, const char* fmt, ...) {
+  char buf[256];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return MOE_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ------------------------------------------------------ measurement hooks --
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[K_NUM_KERNELS];
+  int64_t launches[K_NUM_KERNELS] = {};
+  double total_ms[K_NUM_KERNELS] = {};
+  std::vector<hipEvent_t> pool;
+
+  hipEvent_t get() {
+    if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void drain(int id) {
+    for (auto& pr : pending[id]) {
+      float ms = 0.0f;
+      if (hipEventSynchronize(pr.second) == hipSuccess &&
+          hipEventElapsedTime(&ms, pr.first, pr.second) == hipSuccess) {
+        total_ms[id] += ms;
+        launches[id] += 1;
+      }
+      pool.push_back(pr.first);
+      pool.push_back(pr.second);
+    }
+    pending[id].clear();
+  }
+};
+
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+
+const char* const kKernelNames[K_NUM_KERNELS] = {
+    "route_topk_kernel",     "route_scan_kernel",     "route_scatter_kernel",
+    "decode_gateup_kernel",  "decode_down_kernel",    "prefill_prep_kernel",
+    "prefill_gateup_kernel", "prefill_down_kernel",   "prefill_combine_kernel"};
+
+bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_BF16; }
+
+int check_layer(const moe_q2_layer* L, int k) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "layer descriptor is NULL");
+  if (!L->experts) return fail(MOE_ERR_INVALID_ARG, "layer->experts is NULL");
+  if (L->num_experts < 1) return fail(MOE_ERR_INVALID_ARG, "num_experts must be >= 1");
+  if (L->num_experts > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "num_experts > 1024");
+  if (L->hidden < 256 || L->inter < 256 || L->hidden % 256 || L->inter % 256)
+    return fail(MOE_ERR_INVALID_ARG, "hidden and inter must be positive multiples of 256");
+  if (L->hidden > MOE_MAX_DIM || L->inter > MOE_MAX_DIM)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden and inter must be <= 8192");
+  const int64_t need = 3LL * L->hidden * L->inter * 5 / 16;
+  if (L->expert_stride < need || L->expert_stride % 256)
+    return fail(MOE_ERR_INVALID_ARG, "expert_stride must be >= 3*H*I*5/16 and a multiple of 256");
+  if (!aligned(L->experts, 256) || (L->shared && !aligned(L->shared, 256)))
+    return fail(MOE_ERR_INVALID_ARG, "expert weights must be 256-byte aligned");
+  if (k < 1) return fail(MOE_ERR_INVALID_ARG, "k must be >= 1");
+  if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k must be <= 16");
+  if (k > L->num_experts) return fail(MOE_ERR_INVALID_ARG, "k must be <= num_experts");
+  return MOE_OK;
+}
+
+LayerArgs layer_args(const moe_q2_layer* L) {
+  LayerArgs a;
+  a.experts = static_cast<const uint8_t*>(L->experts);
+  a.shared = static_cast<const uint8_t*>(L->shared);
+  a.stride = L->expert_stride;
+  a.E = L->num_experts;
+  a.H = L->hidden;
+  a.I = L->inter;
+  return a;
+}
+
+size_t route_workspace(int T, int E, int k) {
+  const size_t chunks = (static_cast<size_t>(T) + kRouteChunkTokens - 1) / kRouteChunkTokens;
+  const size_t rank = (static_cast<size_t>(T) * k * 4 + 255) / 256 * 256;
+  const size_t cnt = (chunks * E * 4 + 255) / 256 * 256;
+  return rank + 2 * cnt;
+}
+
+}  // namespace
+
+ProfileScope::ProfileScope(int kernel_id, hipStream_t s) : id(kernel_id), stream(s), ev0(nullptr) {
+  Profiler& p = prof();
+  if (!p.on) return;
+  std::lock_guard<std::mutex> g(p.mu);
+  hipEvent_t e = p.get();
+  if (e && hipEventRecord(e, s) == hipSuccess) ev0 = e;
+}
+
+ProfileScope::~ProfileScope() {
+  if (!ev0) return;
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  hipEvent_t e1 = p.get();
+  if (e1 && hipEventRecord(e1, stream) == hipSuccess)
+    p.pending[id].emplace_back(static_cast<hipEvent_t>(ev0), e1);
+}
+
+}  // namespace moeq2
+
+using namespace moeq2;
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_workspace_bytes(int32_t op, int32_t T, int32_t E, int32_t k, int32_t H, int32_t I) {
+  if (T < 1 || E < 1 || k < 1 || T > MOE_MAX_TOKENS || k > MOE_MAX_TOPK || E > MOE_MAX_EXPERTS)
+    return 0;
+  switch (op) {
+    case MOE_OP_ROUTE: return route_workspace(T, E, k);
+    case MOE_OP_DECODE:
+      if (T > MOE_MAX_DECODE_TOKENS || H < 256 || I < 256) return 0;
+      return decode_workspace_bytes(T, k, H, I);
+    case MOE_OP_PREFILL:
+      if (H < 256 || I < 256) return 0;
+      return prefill_workspace_bytes(T, E, k, H, I);
+    default: return 0;
+  }
+}
+
+int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                   float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                   int32_t* pair_pos, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID_ARG, "logits, topk_ids and topk_w are required");
+  if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1");
+  if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1");
+  if (k < 1) return fail(MOE_ERR_INVALID_ARG, "k must be >= 1");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E must be <= 1024");
+  if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k must be <= 16");
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "k must be <= E");
+  if (T > MOE_MAX_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "T must be <= 2^22");
+  const int nhist = (counts != nullptr) + (offsets != nullptr) + (sorted_pairs != nullptr) + (pair_pos != nullptr);
+  if (nhist != 0 && nhist != 4)
+    return fail(MOE_ERR_INVALID_ARG, "counts, offsets, sorted_pairs and pair_pos: all or none");
+  const bool hist = nhist == 4;
+  if (hist) {
+    if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is required for the histogram");
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (workspace_bytes < route_workspace(T, E, k))
+      return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)route_workspace(T, E, k));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (!hist) {
+    e = launch_route_topk(logits, T, E, k, topk_ids, topk_w, nullptr, nullptr, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "route_topk launch");
+  }
+  const int chunks = (T + kRouteChunkTokens - 1) / kRouteChunkTokens;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* rank = reinterpret_cast<int32_t*>(ws);
+  const size_t rank_b = (static_cast<size_t>(T) * k * 4 + 255) / 256 * 256;
+  const size_t cnt_b = (static_cast<size_t>(chunks) * E * 4 + 255) / 256 * 256;
+  int32_t* local = reinterpret_cast<int32_t*>(ws + rank_b);
+  int32_t* base = reinterpret_cast<int32_t*>(ws + rank_b + cnt_b);
+  if ((e = launch_route_topk(logits, T, E, k, topk_ids, topk_w, rank, local, s)) != hipSuccess)
+    return hip_fail(e, "route_topk launch");
+  if ((e = launch_route_scan(local, base, E, chunks, T * k, counts, offsets, s)) != hipSuccess)
+    return hip_fail(e, "route_scan launch");
+  if ((e = launch_route_scatter(topk_ids, rank, base, T, k, chunks, sorted_pairs, pair_pos, s)) != hipSuccess)
+    return hip_fail(e, "route_scatter launch");
+  return MOE_OK;
+}
+
+static int check_forward(const moe_q2_layer* layer, const void* x, int32_t x_dtype, int32_t T,
+                         const int32_t* ids, const float* w, int32_t k, const void* out,
+                         int32_t out_dtype, uint32_t flags, void* workspace) {
+  int st = check_layer(layer, k);
+  if (st) return st;
+  if (!x || !ids || !w || !out) return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, topk_w and out are required");
+  if (x == out) return fail(MOE_ERR_INVALID_ARG, "out must not alias x");
+  if (!valid_dtype(x_dtype) || !valid_dtype(out_dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (flags & ~MOE_FLAG_PRENORM_RMS) return fail(MOE_ERR_INVALID_ARG, "unknown flag");
+  if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1");
+  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is required");
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (!aligned(x, 4) || !aligned(out, 4) || !aligned(ids, 4) || !aligned(w, 4))
+    return fail(MOE_ERR_INVALID_ARG, "x, out, topk_ids and topk_w must be 4-byte aligned");
+  return MOE_OK;
+}
+
+int moe_expert_forward_decode(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
+                              int32_t T, const int32_t* topk_ids, const float* topk_w, int32_t k,
+                              const void* residual, void* out, int32_t out_dtype, uint32_t flags,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_forward(layer, x, x_dtype, T, topk_ids, topk_w, k, out, out_dtype, flags, workspace);
+  if (st) return st;
+  if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "decode takes at most 4 tokens");
+  const size_t need = decode_workspace_bytes(T, k, layer->hidden, layer->inter);
+  if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
+  const hipError_t e = launch_decode(layer_args(layer), x, x_dtype == MOE_BF16, T, topk_ids, topk_w, k,
+                                     residual, out, out_dtype == MOE_BF16,
+                                     (flags & MOE_FLAG_PRENORM_RMS) ? 1 : 0, workspace,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "decode launch");
+}
+
+int moe_expert_forward_prefill(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
+                               int32_t T, const int32_t* topk_ids, const float* topk_w, int32_t k,
+                               const int32_t* counts, const int32_t* offsets,
+                               const int32_t* sorted_pairs, const int32_t* pair_pos,
+                               const void* residual, void* out, int32_t out_dtype, uint32_t flags,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_forward(layer, x, x_dtype, T, topk_ids, topk_w, k, out, out_dtype, flags, workspace);
+  if (st) return st;
+  if (!counts || !offsets || !sorted_pairs || !pair_pos)
+    return fail(MOE_ERR_INVALID_ARG, "counts, offsets, sorted_pairs and pair_pos are required");
+  if (T > MOE_MAX_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "T must be <= 2^22");
+  const size_t need = prefill_workspace_bytes(T, layer->num_experts, k, layer->hidden, layer->inter);
+  if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
+  const hipError_t e = launch_prefill(layer_args(layer), x, x_dtype == MOE_BF16, T, topk_ids, topk_w, k,
+                                      counts, offsets, sorted_pairs, pair_pos, residual, out,
+                                      out_dtype == MOE_BF16, (flags & MOE_FLAG_PRENORM_RMS) ? 1 : 0,
+                                      workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "prefill launch");
+}
+
+int moe_profile_enable(int on) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.on = on != 0;
+  return MOE_OK;
+}
+
+int moe_profile_reset(void) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  for (int i = 0; i < K_NUM_KERNELS; ++i) {
+    p.drain(i);
+    p.launches[i] = 0;
+    p.total_ms[i] = 0.0;
+  }
+  return MOE_OK;
+}
+
+int moe_profile_num_kernels(void) { return K_NUM_KERNELS; }
+
+const char* moe_profile_kernel_name(int kernel_id) {
+  if (kernel_id < 0 || kernel_id >= K_NUM_KERNELS) return nullptr;
+  return kKernelNames[kernel_id];
+}
+
+int moe_profile_query(int kernel_id, int64_t* launches, double* total_ms) {
+  if (kernel_id < 0 || kernel_id >= K_NUM_KERNELS || !launches || !total_ms)
+    return fail(MOE_ERR_INVALID_ARG, "bad kernel id or NULL output");
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  p.drain(kernel_id);
+  *launches = p.launches[kernel_id];
+  *total_ms = p.total_ms[kernel_id];
+  return MOE_OK;
+}
+
+}  // extern "C"

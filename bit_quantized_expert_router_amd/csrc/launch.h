@@ -1,0 +1,68 @@
+// Host-side launchers shared between the C-ABI layer (api.cpp) and the
+// kernel translation units.  Internal to the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moeq2 {
+
+// Kernel ids for the measurement hooks (order = moe_profile_kernel_name).
+enum KernelId {
+  K_ROUTE_TOPK = 0,
+  K_ROUTE_SCAN,
+  K_ROUTE_SCATTER,
+  K_DECODE_GATEUP,
+  K_DECODE_DOWN,
+  K_PREFILL_PREP,
+  K_PREFILL_GATEUP,
+  K_PREFILL_DOWN,
+  K_PREFILL_COMBINE,
+  K_NUM_KERNELS
+};
+
+// Records a start event before and a stop event after `launch` when the
+// measurement hooks are on.  Defined in api.cpp.
+struct ProfileScope {
+  ProfileScope(int kernel_id, hipStream_t s);
+  ~ProfileScope();
+  int id;
+  hipStream_t stream;
+  void* ev0;
+};
+
+// ---------------------------------------------------------------- routing --
+constexpr int kRouteChunkTokens = 64;   // tokens per routing workgroup
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                             int32_t* rank, int32_t* local_counts, hipStream_t s);
+hipError_t launch_route_scan(const int32_t* local_counts, int32_t* base, int E, int n_chunks,
+                             int total_pairs, int32_t* counts, int32_t* offsets, hipStream_t s);
+hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const int32_t* base,
+                                int T, int k, int n_chunks, int32_t* sorted_pairs,
+                                int32_t* pair_pos, hipStream_t s);
+
+// ----------------------------------------------------------------- decode --
+struct LayerArgs {
+  const uint8_t* experts;
+  const uint8_t* shared;
+  int64_t stride;
+  int E, H, I;
+};
+
+hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
+                         const int32_t* ids, const float* w, int k, const void* residual,
+                         void* out, int out_bf16, int prenorm, void* ws, hipStream_t s);
+size_t decode_workspace_bytes(int T, int k, int H, int I);
+
+// ---------------------------------------------------------------- prefill --
+constexpr int kGroupRows = 64;          // rows (token-expert pairs) per work item
+
+hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
+                          const int32_t* ids, const float* w, int k, const int32_t* counts,
+                          const int32_t* offsets, const int32_t* sorted_pairs,
+                          const int32_t* pair_pos, const void* residual, void* out,
+                          int out_bf16, int prenorm, void* ws, hipStream_t s);
+size_t prefill_workspace_bytes(int T, int E, int k, int H, int I);
+
+}  // namespace moeq2

@@ -1,0 +1,114 @@
+// Device-side building blocks for gfx950 (CDNA4, wave64).
+//
+// Numeric scheme of the expert kernels
+//   * Weights: a tile lane's 32-bit code word holds 8 codes of block 2i and 8
+//     of block 2i+1 (two bits per nibble).  w & 0x33333333 leaves each code
+//     of block 2i alone in a nibble, i.e. an fp4 (e2m1) number q/2, and
+//     (w >> 2) & 0x33333333 does the same for block 2i+1.  The gfx950
+//     scaled fp4->fp16 conversion with scale 2.0 turns two such nibbles into
+//     two fp16 values q, and one packed fp16 fma q*d - d gives d*(q-1)
+//     exactly (fp16 holds -d, 0, d and 2d exactly).  So each weight costs
+//     about 1.2 VALU operations and the MFMA B operand is the exact weight.
+//   * Activations enter the MFMA as fp16: per token x_hat is multiplied by a
+//     power of two s_t so that max|x_hat*s_t| lies in [0.5, 1); the fp32
+//     accumulators are multiplied back by 1/s_t (exact).
+//   * v_mfma_f32_16x16x32_f16: lane l supplies A[i = l%16][k = 8(l/16) + e]
+//     and B[k = 8(l/16) + e][j = l%16] for e = 0..7 and receives
+//     D[4(l/16) + r][l%16] in accumulator element r.  A and B use the same
+//     (lane group, element) -> k assignment, so the dot products do not
+//     depend on how the hardware orders k inside the instruction.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moeq2 {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTileRows = 16;
+constexpr int kTileCols = 256;
+constexpr int kTileBytes = 1280;
+constexpr int kCodeBytes = 1024;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Four consecutive fp4 code pairs of one nibble word -> 8 fp16 weights d*(q-1).
+__device__ __forceinline__ f16x8 nibbles_to_weights(uint32_t nib, f16x2 dd) {
+  f16x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 2.0f, 0);
+  f16x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 2.0f, 1);
+  f16x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 2.0f, 2);
+  f16x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nib, 2.0f, 3);
+  f16x2 nd = -dd;
+  q0 = __builtin_elementwise_fma(q0, dd, nd);
+  q1 = __builtin_elementwise_fma(q1, dd, nd);
+  q2 = __builtin_elementwise_fma(q2, dd, nd);
+  q3 = __builtin_elementwise_fma(q3, dd, nd);
+  f16x8 r;
+  r[0] = q0[0]; r[1] = q0[1]; r[2] = q1[0]; r[3] = q1[1];
+  r[4] = q2[0]; r[5] = q2[1]; r[6] = q3[0]; r[7] = q3[1];
+  return r;
+}
+
+// Scale of block j (0..7) of the lane's row, from the row's 16 scale bytes.
+__device__ __forceinline__ f16x2 scale_pair(const u32x4& s, int j) {
+  uint32_t w = s[j >> 1];
+  uint32_t h = (j & 1) ? (w >> 16) : (w & 0xFFFFu);
+  uint32_t p = h | (h << 16);
+  return __builtin_bit_cast(f16x2, p);
+}
+
+// B fragment of block j of a tile for this lane: code words `c`, scales `s`.
+__device__ __forceinline__ f16x8 tile_block_weights(const u32x4& c, const u32x4& s, int j) {
+  uint32_t w = c[j >> 1];
+  uint32_t nib = (j & 1) ? ((w >> 2) & 0x33333333u) : (w & 0x33333333u);
+  return nibbles_to_weights(nib, scale_pair(s, j));
+}
+
+// Loads of one tile record for this lane (n = lane % 16, g = lane / 16).
+__device__ __forceinline__ u32x4 load_codes(const uint8_t* rec, int lane) {
+  return *reinterpret_cast<const u32x4*>(rec + 16 * lane);
+}
+__device__ __forceinline__ u32x4 load_scales(const uint8_t* rec, int lane) {
+  return *reinterpret_cast<const u32x4*>(rec + kCodeBytes + 16 * (lane & 15));
+}
+
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+
+// Per-token power-of-two normaliser: returns s with max_abs * s in [0.5, 1)
+// (s = 1 for an all-zero token).
+__device__ __forceinline__ float pow2_normaliser(float max_abs) {
+  if (!(max_abs > 0.0f)) return 1.0f;
+  int e;
+  frexpf(max_abs, &e);
+  return ldexpf(1.0f, -e);
+}
+
+__device__ __forceinline__ float bf16_to_float(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ uint16_t float_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);   // round to nearest even (finite inputs)
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Wave-uniform integer broadcast helper.
+__device__ __forceinline__ int first_lane_value(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace moeq2

@@ -1,0 +1,186 @@
+/*
+ * moe_q2.h -- C ABI of the MI355X (gfx950) routed-MoE expert layer on 2-bit
+ * block-quantized weights.
+ *
+ * The layer is the routed mixture-of-experts block of a 48-layer model with
+ * 512 routed experts per layer, 10 of them active per token plus 1 shared
+ * expert ("Strata 实测：125B MoE 跑在 62 GB 内存的游戏本上", kefong.net,
+ * section 二, model table).  Experts are SwiGLU FFNs whose weights stay in
+ * their 2-bit blocks: Q2_0, an affine codebook with bias -1
+ * ("32GB Mac mini 跑 1250 亿参数 Qwen3.8 Flash Next 实测", blog.devlabs.cc,
+ * section 四, second validation layer), 32 weights per block, one fp16 scale
+ * d per block, w = d * (q - 1).
+ *
+ * Three calls make up one layer:
+ *   moe_route_topk             router top-k + weights (+ token->expert
+ *                              histogram and stable permutation for prefill)
+ *   moe_expert_forward_decode  1..4 tokens (a decode step or a verify window)
+ *   moe_expert_forward_prefill any number of tokens (prompt chunks of 1024
+ *                              or 32768 tokens), grouped by expert
+ *
+ * Conventions for every entry point
+ *   - Pointers marked [device] are device addresses (hipMalloc'd memory or
+ *     torch tensors); [host] pointers are read during the call only.
+ *   - The caller owns all memory, including `workspace`.  The library never
+ *     allocates, frees or synchronises, and never reads device data on the
+ *     host.  Each call only enqueues kernels on `stream` (a hipStream_t passed
+ *     as void*, NULL = the null stream), in stream order.
+ *   - Every argument is validated before anything is enqueued: a non-zero
+ *     status means nothing was enqueued (except MOE_ERR_HIP, which reports a
+ *     failed launch; moe_last_error() gives the detail).
+ *   - Calls are re-entrant; calls that may run concurrently need separate
+ *     workspaces.  Inputs must be finite (NaN/Inf give unspecified results).
+ *   - Results are deterministic: no floating-point atomics, fixed summation
+ *     order; repeated calls on the same inputs give the same bytes.
+ *
+ * Weight layout (one expert = [gate | up | down], gate/up are I x H, down is
+ * H x I; rows are output features, columns the reduction dimension).  A matrix
+ * of R rows x K columns (R % 16 == 0, K % 256 == 0) is a row-tile-major array
+ * of 1280-byte tile records, tile (rt, kt) covering rows 16rt..16rt+15 and
+ * columns 256kt..256kt+255 at record index rt*(K/256) + kt.  Record bytes
+ * 0..1023 hold the 2-bit codes as 64 lanes of 16 bytes: lane L covers tile row
+ * n = L % 16 and column slice g = L / 16; its four little-endian 32-bit words
+ * w_i (i = 0..3) hold blocks 2i and 2i+1 of the tile; nibble m (bits
+ * 4m..4m+3) of w_i holds the code of column 32*(2i) + 8g + m in its low two
+ * bits and that of column 32*(2i+1) + 8g + m in its high two bits.  Bytes
+ * 1024..1279 hold the fp16 scale of (row n, block j) at 1024 + 2*(8n + j).
+ * A matrix takes R*K*5/16 bytes (2.5 bits per weight); gate starts at byte 0
+ * of the expert, up at I*H*5/16, down at 2*I*H*5/16.
+ */
+#ifndef MOE_Q2_H
+#define MOE_Q2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* null pointer, bad size, bad alignment      */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but outside this build's limits      */
+  MOE_ERR_WORKSPACE = -3,    /* workspace smaller than moe_workspace_bytes */
+  MOE_ERR_HIP = -4           /* a kernel launch failed                     */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* x_hat = x * (mean(x^2) + 1e-6)^(-1/2) per token (no weight) before the
+ * experts; the pre-norm of a residual block x + MoE(rmsnorm(x)). */
+#define MOE_FLAG_PRENORM_RMS 1u
+
+enum { MOE_OP_ROUTE = 0, MOE_OP_DECODE = 1, MOE_OP_PREFILL = 2 };
+
+/* Limits of this build (validated): */
+#define MOE_MAX_EXPERTS 1024     /* E                                        */
+#define MOE_MAX_TOPK 16          /* k                                        */
+#define MOE_MAX_DECODE_TOKENS 4  /* T of moe_expert_forward_decode           */
+#define MOE_MAX_DIM 8192         /* H and I (each a multiple of 256)         */
+#define MOE_MAX_TOKENS (1 << 22) /* T of routing and prefill                 */
+
+typedef struct {
+  const void* experts;    /* [device] E experts; expert e at experts + e*expert_stride;
+                             256-byte aligned                                  */
+  const void* shared;     /* [device] the shared expert (same layout), or NULL */
+  int64_t expert_stride;  /* bytes, >= 3*I*H*5/16, multiple of 256             */
+  int32_t num_experts;    /* E, 1..1024                                        */
+  int32_t hidden;         /* H, multiple of 256, <= 8192                       */
+  int32_t inter;          /* I (expert intermediate size), multiple of 256     */
+} moe_q2_layer;
+
+/* Bytes of workspace the given call needs (0 if none).  op is MOE_OP_*; for
+ * MOE_OP_ROUTE the size assumes the histogram outputs are requested. */
+size_t moe_workspace_bytes(int32_t op, int32_t T, int32_t E, int32_t k, int32_t H, int32_t I);
+
+/*
+ * Router (the per-token list of selected experts that the GPU hands to the
+ * expert compute: "RTX PRO 4500 单卡跑 125B MoE", lcz.me/topic/2169, section
+ * 最重要机制, item 1).
+ *   logits   [device] float32 [T, E] row-major router logits.
+ *   topk_ids [device] int32 [T, k]: the k experts with the largest logits,
+ *            compared as exact float32 values (-0.0 == +0.0); equal logits go
+ *            to the lower expert id; slots in descending logit order.
+ *   topk_w   [device] float32 [T, k]: exp(l_j - l_max) / sum over the k
+ *            selected (the softmax over E renormalised over the selection).
+ *   counts, offsets, sorted_pairs, pair_pos: [device] int32 [E], [E+1],
+ *            [T*k], [T*k], all four or none (NULL).  counts[e] = pairs routed
+ *            to e; offsets = exclusive prefix sum; sorted_pairs = pair ids
+ *            p = t*k + j ordered by (expert, p); pair_pos = its inverse.
+ *   workspace [device] >= moe_workspace_bytes(MOE_OP_ROUTE, ...) when the
+ *            histogram is requested (else may be NULL), 256-byte aligned.
+ * Errors: INVALID_ARG for null required pointers, T < 1, k < 1, k > E, a
+ * partial set of histogram outputs; UNSUPPORTED for E > 1024, k > 16,
+ * T > 2^22; WORKSPACE when too small.
+ */
+int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                   int32_t* topk_ids, float* topk_w,
+                   int32_t* counts, int32_t* offsets,
+                   int32_t* sorted_pairs, int32_t* pair_pos,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode-time expert layer for T = 1..4 tokens (one decode step or a verify
+ * window that checks a few drafted tokens at once: "32GB Mac mini ...",
+ * section 一, and "RTX PRO 4500 ...", section 最重要机制, item 3).  Only the
+ * selected experts' weights are read.
+ *   layer     [host] weights descriptor (above).
+ *   x         [device] [T, H] activations, x_dtype MOE_F32 or MOE_BF16.
+ *   topk_ids, topk_w  [device] [T, k] as produced by moe_route_topk.
+ *   residual  [device] [T, H] in out_dtype, or NULL; may alias `out`.
+ *   out       [device] [T, H] in out_dtype; must not alias x:
+ *             out[t] = sum_j topk_w[t,j] * FFN_{topk_ids[t,j]}(x_hat_t)
+ *                      + FFN_shared(x_hat_t) (+ residual[t]),
+ *             FFN(x) = W_down (silu(W_gate x) * (W_up x)).
+ *   flags     0 or MOE_FLAG_PRENORM_RMS.
+ *   workspace [device] >= moe_workspace_bytes(MOE_OP_DECODE, ...), 256-B aligned.
+ * Errors: INVALID_ARG (null pointers, T < 1, k < 1 or > E, stride too small or
+ * unaligned, H or I not multiples of 256, unknown dtype or flag),
+ * UNSUPPORTED (T > 4, E > 1024, k > 16, H or I > 8192), WORKSPACE.
+ */
+int moe_expert_forward_decode(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
+                              int32_t T, const int32_t* topk_ids, const float* topk_w,
+                              int32_t k, const void* residual, void* out, int32_t out_dtype,
+                              uint32_t flags, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * Prefill-time expert layer for a chunk of T tokens, grouped by expert from
+ * the routing histogram (prompts are read in chunks and the experts are
+ * processed block by block: strata-mlx README, section 它是什么; chunk sizes
+ * 1024 and 32768: "Strata 实测 ...", section 四, change 4).
+ * Arguments as for the decode call, plus the four histogram arrays from
+ * moe_route_topk for the same topk_ids.  Computes the same `out`.
+ * Errors: as for decode, with T limited to 1..2^22 instead of 1..4.
+ */
+int moe_expert_forward_prefill(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
+                               int32_t T, const int32_t* topk_ids, const float* topk_w,
+                               int32_t k, const int32_t* counts, const int32_t* offsets,
+                               const int32_t* sorted_pairs, const int32_t* pair_pos,
+                               const void* residual, void* out, int32_t out_dtype,
+                               uint32_t flags, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Text of a status code; detail of the last error on this thread. */
+const char* moe_status_string(int status);
+const char* moe_last_error(void);
+
+/*
+ * Measurement hooks (host-side only; no device memory).  When enabled, every
+ * kernel launch is bracketed by a pair of hipEvents on its stream;
+ * moe_profile_query returns, per kernel id, the number of launches and the
+ * summed event time (it waits for the recorded events).  Ids run
+ * 0..moe_profile_num_kernels()-1; moe_profile_kernel_name names them.
+ */
+int moe_profile_enable(int on);
+int moe_profile_reset(void);
+int moe_profile_num_kernels(void);
+const char* moe_profile_kernel_name(int kernel_id);
+int moe_profile_query(int kernel_id, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_Q2_H */

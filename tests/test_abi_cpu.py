@@ -1,0 +1,139 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/moe_q2.h declares, and rejects bad arguments before any HIP call
+(validation runs first, so these calls never reach the device)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_q2.h")
+LIB = os.path.join(ROOT, "bit_quantized_expert_router_amd", "libmoe_q2.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bit_quantized_expert_router_amd import binding
+    return binding.lib
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", nm, flags=re.M), n
+
+
+def test_binding_lists_all_exports():
+    from bit_quantized_expert_router_amd import binding
+    assert sorted(binding.EXPORTS) == declared_functions()
+
+
+def test_status_strings(lib):
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(-3) == b"MOE_ERR_WORKSPACE"
+
+
+def test_workspace_sizes(lib):
+    from bit_quantized_expert_router_amd import binding as B
+    assert B.moe_workspace_bytes(B.MOE_OP_DECODE, 1, 512, 10, 3072, 768) > 0
+    assert B.moe_workspace_bytes(B.MOE_OP_DECODE, 5, 512, 10, 3072, 768) == 0
+    p = B.moe_workspace_bytes(B.MOE_OP_PREFILL, 1024, 512, 10, 3072, 768)
+    # x16 + h + y at least
+    assert p >= 1024 * 3072 * 2 + 11264 * 768 * 2 + 11264 * 3072 * 2
+    assert B.moe_workspace_bytes(B.MOE_OP_ROUTE, 1024, 512, 10, 3072, 768) >= 1024 * 10 * 4
+
+
+FAKE = 0x100000  # aligned, never dereferenced: validation fails first
+
+
+def route(lib, **kw):
+    a = dict(logits=FAKE, T=4, E=64, k=4, ids=FAKE, w=FAKE, counts=None, offsets=None,
+             sp=None, pp=None, ws=None, wsb=0)
+    a.update(kw)
+    return lib.moe_route_topk(C.c_void_p(a["logits"]), a["T"], a["E"], a["k"], C.c_void_p(a["ids"]),
+                              C.c_void_p(a["w"]), C.c_void_p(a["counts"]), C.c_void_p(a["offsets"]),
+                              C.c_void_p(a["sp"]), C.c_void_p(a["pp"]), C.c_void_p(a["ws"]),
+                              a["wsb"], None)
+
+
+def test_route_validation(lib):
+    assert route(lib, logits=None) == -1
+    assert route(lib, T=0) == -1
+    assert route(lib, k=0) == -1
+    assert route(lib, k=65) == -2      # k > 16 is unsupported
+    assert route(lib, E=2048, k=4) == -2
+    assert route(lib, E=3, k=4) == -1  # k > E
+    assert route(lib, counts=FAKE) == -1   # partial histogram outputs
+    assert route(lib, counts=FAKE, offsets=FAKE, sp=FAKE, pp=FAKE) == -3  # no workspace
+    assert route(lib, counts=FAKE, offsets=FAKE, sp=FAKE, pp=FAKE, ws=FAKE, wsb=16) == -3
+    assert route(lib, counts=FAKE, offsets=FAKE, sp=FAKE, pp=FAKE, ws=FAKE + 4, wsb=1 << 30) == -1
+    assert b"workspace" in lib.moe_last_error()
+
+
+def forward(lib, which, **kw):
+    from bit_quantized_expert_router_amd.binding import _Layer
+    a = dict(experts=FAKE, shared=FAKE, stride=245760, E=64, H=1024, I=256, x=FAKE, xd=0, T=1,
+             ids=FAKE, w=FAKE, k=4, res=None, out=FAKE + 4096, od=0, flags=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    L = _Layer(a["experts"], a["shared"], a["stride"], a["E"], a["H"], a["I"])
+    if which == "decode":
+        return lib.moe_expert_forward_decode(C.byref(L), C.c_void_p(a["x"]), a["xd"], a["T"],
+                                             C.c_void_p(a["ids"]), C.c_void_p(a["w"]), a["k"],
+                                             C.c_void_p(a["res"]), C.c_void_p(a["out"]), a["od"],
+                                             a["flags"], C.c_void_p(a["ws"]), a["wsb"], None)
+    return lib.moe_expert_forward_prefill(C.byref(L), C.c_void_p(a["x"]), a["xd"], a["T"],
+                                          C.c_void_p(a["ids"]), C.c_void_p(a["w"]), a["k"],
+                                          C.c_void_p(a.get("counts", FAKE)), C.c_void_p(a.get("offsets", FAKE)),
+                                          C.c_void_p(a.get("sp", FAKE)), C.c_void_p(a.get("pp", FAKE)),
+                                          C.c_void_p(a["res"]), C.c_void_p(a["out"]), a["od"],
+                                          a["flags"], C.c_void_p(a["ws"]), a["wsb"], None)
+
+
+@pytest.mark.parametrize("which", ["decode", "prefill"])
+def test_forward_validation(lib, which):
+    assert forward(lib, which, experts=None) == -1
+    assert forward(lib, which, x=None) == -1
+    assert forward(lib, which, out=FAKE) == -1          # aliases x
+    assert forward(lib, which, H=1000) == -1            # not a multiple of 256
+    assert forward(lib, which, H=16384, stride=1 << 30) == -2
+    assert forward(lib, which, stride=1000) == -1       # too small
+    assert forward(lib, which, stride=245760 + 128) == -1  # not a multiple of 256
+    assert forward(lib, which, experts=FAKE + 16) == -1    # unaligned weights
+    assert forward(lib, which, k=0) == -1
+    assert forward(lib, which, k=17) == -2
+    assert forward(lib, which, E=3, k=4) == -1
+    assert forward(lib, which, E=2000) == -2
+    assert forward(lib, which, xd=7) == -1
+    assert forward(lib, which, flags=2) == -1
+    assert forward(lib, which, T=0) == -1
+    assert forward(lib, which, ws=None) == -3
+    assert forward(lib, which, wsb=100) == -3
+    assert forward(lib, which, ws=FAKE + 8) == -1
+    if which == "decode":
+        assert forward(lib, which, T=5) == -2
+    else:
+        assert forward(lib, which, counts=None) == -1
+        assert forward(lib, which, T=(1 << 22) + 1) == -2
+
+
+def test_profile_hooks_host_only(lib):
+    from bit_quantized_expert_router_amd import binding as B
+    B.profile_enable(False)
+    B.profile_reset()
+    res = B.profile_results()
+    assert "decode_gateup_kernel" in res and "prefill_gateup_kernel" in res
+    assert all(v == (0, 0.0) for v in res.values())
