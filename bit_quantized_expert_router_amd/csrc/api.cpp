@@ -109,7 +109,7 @@ LayerArgs layer_args(const moe_q2_layer* L) {
 }
 
 size_t route_workspace(int T, int E, int k) {
-  const size_t chunks = (static_cast<size_t>(T) + kRouteChunkTokens - 1) / kRouteChunkTokens;
+  const size_t chunks = (static_cast<size_t>(T) + route_chunk_tokens(T) - 1) / route_chunk_tokens(T);
   const size_t rank = (static_cast<size_t>(T) * k * 4 + 255) / 256 * 256;
   const size_t cnt = (chunks * E * 4 + 255) / 256 * 256;
   return rank + 2 * cnt;
@@ -195,7 +195,7 @@ int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t
     e = launch_route_topk(logits, T, E, k, topk_ids, topk_w, nullptr, nullptr, s);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "route_topk launch");
   }
-  const int chunks = (T + kRouteChunkTokens - 1) / kRouteChunkTokens;
+  const int chunks = (T + route_chunk_tokens(T) - 1) / route_chunk_tokens(T);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int32_t* rank = reinterpret_cast<int32_t*>(ws);
   const size_t rank_b = (static_cast<size_t>(T) * k * 4 + 255) / 256 * 256;
@@ -223,8 +223,8 @@ static int check_forward(const moe_q2_layer* layer, const void* x, int32_t x_dty
   if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1");
   if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is required");
   if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (!aligned(x, 4) || !aligned(out, 4) || !aligned(ids, 4) || !aligned(w, 4))
-    return fail(MOE_ERR_INVALID_ARG, "x, out, topk_ids and topk_w must be 4-byte aligned");
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ids, 4) || !aligned(w, 4))
+    return fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned, topk_ids and topk_w 4-byte aligned");
   return MOE_OK;
 }
 

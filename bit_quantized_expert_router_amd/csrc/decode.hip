@@ -4,23 +4,29 @@
 // Reading the selected experts' weights is what decode time goes to ("Strata
 // 实测 ...", kefong.net, section 四: a higher expert-cache hit rate gave +39 %
 // decode; "RTX PRO 4500 ...", section 最重要机制, item 3: verify windows spread
-// the weight reads over several tokens).  Both kernels are therefore built to
-// stream tile records from HBM with one 16-byte load of codes and one of
-// scales per lane per 16x256 tile, and to keep all arithmetic on the MFMA
-// (tokens are the M dimension, padded to 16) so the cost per weight does
-// not grow with T.
+// the weight reads over several tokens).  Both kernels therefore put every
+// weight load of a wave in flight before anything waits on it, stream each
+// 16x256 tile with one 16-byte load of codes and one of scales per lane, and
+// keep all arithmetic on the MFMA (tokens are the M dimension, padded to 16)
+// so the cost per weight does not grow with T.  Each kernel is sized to run
+// in a single round of workgroups (every workgroup resident at once): on this
+// hardware a kernel's time is its slowest workgroup's dependent-latency chain.
 //
-// Kernel 1 (gate/up + SwiGLU): one workgroup per (slot, 16-row tile of I),
-//   four waves split the H/256 K-tiles.  A slot is a distinct selected expert
-//   (ascending id) or the shared expert (last).  Every workgroup builds the
-//   slot list itself from topk_ids (<= 64 entries) and stages x_hat as fp16 in
-//   LDS with a per-token power-of-two normaliser.  Output: h~[slot][t][I] in
-//   fp16, h~ = w(slot,t) * silu(g) * u * s_t^2 (w = 0 when token t did not
-//   pick the slot's expert; 1 for the shared expert).
-// Kernel 2 (down + weighted combine + shared + residual): one workgroup per
-//   16-row tile of H, four waves split the slots; the MFMA accumulator sums
-//   W_down(e) h~(e) over all slots, so the weighted combine is exact and in a
-//   fixed order; out = acc / s_t^2 (+ residual).
+// Slots: the distinct selected experts in first-occurrence order of topk_ids,
+// then the shared expert.  Pairs: routed pair p = t*k + j, shared pair T*k + t;
+// h~ has one row per pair.
+//
+// Kernel 1 (gate/up + SwiGLU): one workgroup of 8 waves per (slot, two 16-row
+//   tiles of I); 4 waves per row tile split the H/256 K tiles.  Each
+//   workgroup derives the slots from topk_ids with ballots (<= 64 ids), issues
+//   its weight loads, then stages x_hat * s_t as fp16 in LDS (s_t: per-token
+//   power of two, max |x_hat s_t| in [0.5, 1)).  h~[pair][I] (fp16) =
+//   w * silu(g) * u * s_t^2.
+// Kernel 2 (down + weighted combine + shared + residual): one workgroup of 8
+//   waves per 16-row tile of H; the waves split the slots.  h~ is staged in
+//   LDS once per workgroup; the MFMA accumulator sums W_down(e) h~(e) over all
+//   slots, so the weighted combine is exact and in a fixed order;
+//   out = acc / s_t^2 (+ residual).
 #include "launch.h"
 #include "q2_device.h"
 #include "../../include/moe_q2.h"
@@ -29,50 +35,58 @@ namespace moeq2 {
 
 namespace {
 
-constexpr int kMaxSlots = MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK + 1;   // 65
-constexpr int kMaxKtPerWave = MOE_MAX_DIM / kTileCols / 4;             // 8
+constexpr int kMaxSlots = MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK + 1;                   // 65
+constexpr int kMaxPairs = MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK + MOE_MAX_DECODE_TOKENS; // 68
+constexpr int kThreads = 512;            // 8 waves
+constexpr int kWaves = kThreads / kWave;
+constexpr int kXRegChunks = 3;           // x chunks of 8 kept in registers (T*H <= 12288)
+constexpr int kDownBatch = 8;            // weight tiles in flight per wave in kernel 2
+constexpr int kDownStage = 4;            // h~ chunks per thread loaded ahead in kernel 2
 
 struct DecodeHeader {          // start of the workspace, written by block 0 of kernel 1
   int32_t n_slots;
-  int32_t expert[kMaxSlots];   // -1 = shared expert
-  float unscale[MOE_MAX_DECODE_TOKENS];   // 1 / s_t
-  int32_t pad[58];
+  int32_t pad0[3];
+  int32_t expert[kMaxSlots];                       // -1 = shared expert
+  int32_t pidx[kMaxSlots][MOE_MAX_DECODE_TOKENS];  // pair of (slot, token) or -1
+  float unscale[MOE_MAX_DECODE_TOKENS];            // 1 / s_t
+  int32_t pad1[179];
 };
-static_assert(sizeof(DecodeHeader) == 512, "header size");
+static_assert(sizeof(DecodeHeader) == 2048, "header size");
 
 struct DecodeSlots {
   int n;
   int expert[kMaxSlots];
-  float wt[kMaxSlots][MOE_MAX_DECODE_TOKENS];
+  int pidx[kMaxSlots][MOE_MAX_DECODE_TOKENS];
+  float wpair[kMaxPairs];
 };
 
-// Wave 0 builds the distinct selected experts in ascending id order, the
-// shared expert last, and the routing weight of every (slot, token).
+// Wave 0: slots (distinct valid ids in first-occurrence order, then the
+// shared expert), the pair of every (slot, token) and every pair's weight.
+// Ids outside [0, E) are ignored.
 __device__ void build_slots(const int32_t* ids, const float* w, int T, int k, int E,
                             bool has_shared, DecodeSlots& S) {
   const int lane = threadIdx.x & (kWave - 1);
   const int np = T * k;
-  int e = lane < np ? ids[lane] : 0x7FFFFFFF;
-  const bool valid = lane < np && e >= 0 && e < E;   // out-of-range ids are ignored
-  if (!valid) e = 0x7FFFFFFF;
-  bool first = valid;
-  int slot = 0;
-  for (int q = 0; q < np; ++q) {
-    const int eq = __shfl(e, q, kWave);
-    if (q < lane && eq == e) first = false;
-  }
+  const int e = lane < np ? ids[lane] : -1;
+  const float wl = lane < np ? w[lane] : 0.0f;
+  const bool valid = lane < np && e >= 0 && e < E;
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t same = match_lanes(valid ? e : 0, valid, nbits);
+  const uint64_t below = (1ull << lane) - 1ull;
+  const bool first = valid && (same & below) == 0;
   const uint64_t fm = __ballot(first);
-  for (int q = 0; q < np; ++q) {
-    const int eq = __shfl(e, q, kWave);
-    if (((fm >> q) & 1ull) && eq < e) ++slot;
-  }
   const int nd = __popcll(fm);
-  for (int i = lane; i < kMaxSlots * MOE_MAX_DECODE_TOKENS; i += kWave)
-    (&S.wt[0][0])[i] = 0.0f;
+  const int slot = valid ? __popcll(fm & ((1ull << __builtin_ctzll(same)) - 1ull)) : 0;
+  for (int i = lane; i < kMaxSlots * MOE_MAX_DECODE_TOKENS; i += kWave) (&S.pidx[0][0])[i] = -1;
   __builtin_amdgcn_wave_barrier();
   if (first) S.expert[slot] = e;
-  if (valid) S.wt[slot][lane / k] = w[lane];
-  if (has_shared && lane < T) S.wt[nd][lane] = 1.0f;
+  if (valid) S.pidx[slot][lane / k] = lane;
+  if (lane < np) S.wpair[lane] = valid ? wl : 0.0f;
+  if (has_shared && lane < T) {
+    S.pidx[nd][lane] = np + lane;
+    S.wpair[np + lane] = 1.0f;
+  }
   if (lane == 0) {
     if (has_shared) S.expert[nd] = -1;
     S.n = nd + (has_shared ? 1 : 0);
@@ -83,95 +97,190 @@ __device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e)
   return e < 0 ? L.shared : L.experts + static_cast<int64_t>(e) * L.stride;
 }
 
-__global__ __launch_bounds__(256) void decode_gateup_kernel(
-    LayerArgs L, const void* __restrict__ x, int x_bf16, int T, const int32_t* __restrict__ ids,
+// x chunk c (8 consecutive values of the row-major [T][H] input): raw load
+// (two 16-byte vectors; the second is unused for bf16) and conversion.
+template <bool BF16>
+__device__ __forceinline__ void load_x_raw(const void* x, int c, u32x4 (&r)[2]) {
+  if (BF16) {
+    r[0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + 8 * c);
+  } else {
+    r[0] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + 8 * c);
+    r[1] = *reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + 8 * c + 4);
+  }
+}
+template <bool BF16>
+__device__ __forceinline__ void x_raw_to_float(const u32x4 (&r)[2], float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (BF16) {
+      v[2 * i] = __uint_as_float(r[0][i] << 16);
+      v[2 * i + 1] = __uint_as_float(r[0][i] & 0xFFFF0000u);
+    } else {
+      v[i] = __uint_as_float(r[0][i]);
+      v[4 + i] = __uint_as_float(r[1][i]);
+    }
+  }
+}
+
+template <int KTW, bool BF16>   // K tiles per wave: ceil(H / 256 / 4); x dtype
+__global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
+    LayerArgs L, const void* __restrict__ x, int T, const int32_t* __restrict__ ids,
     const float* __restrict__ w, int k, int prenorm, uint8_t* __restrict__ ws) {
   extern __shared__ __align__(16) uint8_t dyn[];
   _Float16* xs = reinterpret_cast<_Float16*>(dyn);              // [T][H]
   __shared__ DecodeSlots S;
-  __shared__ float s_stat[4][MOE_MAX_DECODE_TOKENS][2];
+  __shared__ float s_stat[kWaves][MOE_MAX_DECODE_TOKENS][2];
   __shared__ float s_mul[MOE_MAX_DECODE_TOKENS];
   __shared__ float s_uns[MOE_MAX_DECODE_TOKENS];
-  __shared__ f32x4 s_red[4][2][16];
+  __shared__ f32x4 s_red[kWaves][2][16];
 
   const int H = L.H, I = L.I;
-  const int RT = I / kTileRows;
-  const int slot = blockIdx.x / RT;
-  const int rt = blockIdx.x % RT;
+  const int RP = I / (2 * kTileRows);        // row-tile pairs
+  const int slot = blockIdx.x / RP;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
+  const int rt = 2 * (blockIdx.x % RP) + (wid >> 2);
+  const int kq = wid & 3;
+
+  // x into registers first (independent of the routing)
+  const int nch = T * H / 8;
+  const bool xreg = nch <= kThreads * kXRegChunks;
+  u32x4 xr[kXRegChunks][2];
+  if (xreg) {
+#pragma unroll
+    for (int q = 0; q < kXRegChunks; ++q)
+      load_x_raw<BF16>(x, min(static_cast<int>(threadIdx.x) + kThreads * q, nch - 1), xr[q]);
+  }
 
   if (wid == 0) build_slots(ids, w, T, k, L.E, L.shared != nullptr, S);
   __syncthreads();
-  // block 0 always writes the header the down kernel reads (even with no slots)
-  if (slot >= S.n && blockIdx.x != 0) return;
+  const bool active = slot < S.n;
+  if (!active && blockIdx.x != 0) return;    // block 0 always writes the header
+
+  // ---- weight loads of this row tile (gate and up), K split over 4 waves
+  const int KT = H / kTileCols;
+  const int64_t mat = static_cast<int64_t>(I) * H * 5 / 16;
+  u32x4 cg[KTW], sg[KTW], cu[KTW], su[KTW];
+  if (active) {
+    const uint8_t* gate = expert_base(L, S.expert[slot]) + static_cast<int64_t>(rt) * KT * kTileBytes;
+    const uint8_t* up = gate + mat;
+#pragma unroll
+    for (int i = 0; i < KTW; ++i) {
+      const int kt = min(kq + 4 * i, KT - 1);
+      cg[i] = load_codes(gate + kt * kTileBytes, lane);
+      cu[i] = load_codes(up + kt * kTileBytes, lane);
+      sg[i] = load_scales(gate + kt * kTileBytes, lane);
+      su[i] = load_scales(up + kt * kTileBytes, lane);
+    }
+  }
 
   // ---- per-token statistics and the fp16 copy of x_hat * s_t ------------
-  for (int t = 0; t < T; ++t) {
-    float ss = 0.0f, mx = 0.0f;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) {
-      const size_t o = static_cast<size_t>(t) * H + i;
-      const float v = x_bf16 ? bf16_to_float(static_cast<const uint16_t*>(x)[o])
-                             : static_cast<const float*>(x)[o];
-      ss += v * v;
-      mx = fmaxf(mx, fabsf(v));
+  // (token of chunk c: c / (H/8), by comparisons; T <= 4)
+  const int cpt = H / 8;
+  auto token_of = [&](int c) { return (c >= cpt) + (c >= 2 * cpt) + (c >= 3 * cpt); };
+  float ss[MOE_MAX_DECODE_TOKENS] = {0.f, 0.f, 0.f, 0.f};
+  float mx[MOE_MAX_DECODE_TOKENS] = {0.f, 0.f, 0.f, 0.f};
+  auto accum = [&](int c, const float (&v)[8]) {
+    const int t = token_of(c);
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { a += v[i] * v[i]; b = fmaxf(b, fabsf(v[i])); }
+#pragma unroll
+    for (int q = 0; q < MOE_MAX_DECODE_TOKENS; ++q) {
+      ss[q] += (q == t) ? a : 0.0f;
+      mx[q] = (q == t) ? fmaxf(mx[q], b) : mx[q];
     }
-    ss = wave_sum(ss);
-    mx = wave_max(mx);
-    if (lane == 0) { s_stat[wid][t][0] = ss; s_stat[wid][t][1] = mx; }
+  };
+  if (xreg) {
+#pragma unroll
+    for (int q = 0; q < kXRegChunks; ++q) {
+      const int c = threadIdx.x + kThreads * q;
+      if (c < nch) {
+        float v[8];
+        x_raw_to_float<BF16>(xr[q], v);
+        accum(c, v);
+      }
+    }
+  } else {
+    for (int c = threadIdx.x; c < nch; c += kThreads) {
+      u32x4 r[2];
+      float v[8];
+      load_x_raw<BF16>(x, c, r);
+      x_raw_to_float<BF16>(r, v);
+      accum(c, v);
+    }
   }
-  __syncthreads();
-  if (threadIdx.x < T) {
-    const int t = threadIdx.x;
-    float ss = 0.0f, mx = 0.0f;
-    for (int q = 0; q < 4; ++q) { ss += s_stat[q][t][0]; mx = fmaxf(mx, s_stat[q][t][1]); }
-    const float r = prenorm ? 1.0f / sqrtf(ss / static_cast<float>(H) + 1e-6f) : 1.0f;
-    const float s = pow2_normaliser(mx * r);
-    s_mul[t] = r;
-    s_uns[t] = s;
-  }
-  __syncthreads();
   for (int t = 0; t < T; ++t) {
-    const float r = s_mul[t], s = s_uns[t];
-    for (int i = threadIdx.x; i < H; i += blockDim.x) {
-      const size_t o = static_cast<size_t>(t) * H + i;
-      const float v = x_bf16 ? bf16_to_float(static_cast<const uint16_t*>(x)[o])
-                             : static_cast<const float*>(x)[o];
-      xs[t * H + i] = static_cast<_Float16>((v * r) * s);
+    const float a = wave_sum(ss[t]);
+    const float b = wave_max(mx[t]);
+    if (lane == 0) { s_stat[wid][t][0] = a; s_stat[wid][t][1] = b; }
+  }
+  __syncthreads();
+  // every thread derives the per-token multipliers itself (no second barrier)
+  float rmul[MOE_MAX_DECODE_TOKENS], smul[MOE_MAX_DECODE_TOKENS];
+#pragma unroll
+  for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
+    float a = 0.0f, b = 0.0f;
+    if (t < T) {
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) { a += s_stat[q][t][0]; b = fmaxf(b, s_stat[q][t][1]); }
+    }
+    rmul[t] = prenorm ? 1.0f / sqrtf(a / static_cast<float>(H) + 1e-6f) : 1.0f;
+    smul[t] = pow2_normaliser(b * rmul[t]);
+  }
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) { s_mul[t] = rmul[t]; s_uns[t] = smul[t]; }
+  }
+  auto put = [&](int c, const float (&v)[8]) {
+    const int t = token_of(c);
+    float r = rmul[0], s = smul[0];
+#pragma unroll
+    for (int q = 1; q < MOE_MAX_DECODE_TOKENS; ++q) { r = (q == t) ? rmul[q] : r; s = (q == t) ? smul[q] : s; }
+    f16x8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>((v[i] * r) * s);
+    *reinterpret_cast<f16x8*>(xs + 8 * c) = h;
+  };
+  if (xreg) {
+#pragma unroll
+    for (int q = 0; q < kXRegChunks; ++q) {
+      const int c = threadIdx.x + kThreads * q;
+      if (c < nch) {
+        float v[8];
+        x_raw_to_float<BF16>(xr[q], v);
+        put(c, v);
+      }
+    }
+  } else {
+    for (int c = threadIdx.x; c < nch; c += kThreads) {
+      u32x4 r[2];
+      float v[8];
+      load_x_raw<BF16>(x, c, r);
+      x_raw_to_float<BF16>(r, v);
+      put(c, v);
     }
   }
   if (blockIdx.x == 0) {
     DecodeHeader* hdr = reinterpret_cast<DecodeHeader*>(ws);
-    if (threadIdx.x < T) hdr->unscale[threadIdx.x] = 1.0f / s_uns[threadIdx.x];
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t)
+        if (t < T) hdr->unscale[t] = 1.0f / smul[t];
+    }
+    for (int i = threadIdx.x; i < S.n * MOE_MAX_DECODE_TOKENS; i += kThreads)
+      (&hdr->pidx[0][0])[i] = (&S.pidx[0][0])[i];
     if (threadIdx.x < S.n) hdr->expert[threadIdx.x] = S.expert[threadIdx.x];
     if (threadIdx.x == 0) hdr->n_slots = S.n;
   }
   __syncthreads();
-  if (slot >= S.n) return;
+  if (!active) return;
 
-  // ---- gate and up tiles of this row tile, K split over the 4 waves ------
-  const uint8_t* eb = expert_base(L, S.expert[slot]);
-  const int64_t mat = static_cast<int64_t>(I) * H * 5 / 16;
-  const int KT = H / kTileCols;
-  const uint8_t* gate = eb + static_cast<int64_t>(rt) * KT * kTileBytes;
-  const uint8_t* up = gate + mat;
-
-  u32x4 cg[kMaxKtPerWave], sg[kMaxKtPerWave], cu[kMaxKtPerWave], su[kMaxKtPerWave];
-#pragma unroll
-  for (int i = 0; i < kMaxKtPerWave; ++i) {
-    const int kt = wid + 4 * i;
-    if (kt < KT) {
-      cg[i] = load_codes(gate + kt * kTileBytes, lane);
-      sg[i] = load_scales(gate + kt * kTileBytes, lane);
-      cu[i] = load_codes(up + kt * kTileBytes, lane);
-      su[i] = load_scales(up + kt * kTileBytes, lane);
-    }
-  }
   const int m = lane & 15, g = lane >> 4;
   f32x4 acc_g = {0.f, 0.f, 0.f, 0.f}, acc_u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < kMaxKtPerWave; ++i) {
-    const int kt = wid + 4 * i;
+  for (int i = 0; i < KTW; ++i) {
+    const int kt = kq + 4 * i;
     if (kt < KT) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -184,25 +293,45 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(
   }
   if (lane < 16) { s_red[wid][0][lane] = acc_g; s_red[wid][1][lane] = acc_u; }
   __syncthreads();
-  if (wid == 0 && lane < 16) {
-    f32x4 G = s_red[0][0][lane], U = s_red[0][1][lane];
-    for (int q = 1; q < 4; ++q) { G += s_red[q][0][lane]; U += s_red[q][1][lane]; }
+  if (kq == 0 && lane < 16) {
+    f32x4 G = s_red[wid][0][lane], U = s_red[wid][1][lane];
+    for (int q = 1; q < 4; ++q) { G += s_red[wid + q][0][lane]; U += s_red[wid + q][1][lane]; }
     _Float16* hout = reinterpret_cast<_Float16*>(ws + sizeof(DecodeHeader));
     const int row = rt * kTileRows + lane;
     for (int t = 0; t < T; ++t) {
+      const int p = S.pidx[slot][t];
+      if (p < 0) continue;
       const float s = s_uns[t];
       const float u = 1.0f / s;
       const float gv = G[t] * u, uv = U[t] * u;
-      const float h = S.wt[slot][t] * silu(gv) * uv * (s * s);
-      hout[(static_cast<size_t>(slot) * T + t) * I + row] = static_cast<_Float16>(h);
+      const float h = S.wpair[p] * silu(gv) * uv * (s * s);
+      hout[static_cast<size_t>(p) * I + row] = static_cast<_Float16>(h);
     }
   }
 }
 
-__global__ __launch_bounds__(256) void decode_down_kernel(
-    LayerArgs L, int T, const void* __restrict__ residual, void* __restrict__ out, int out_bf16,
-    const uint8_t* __restrict__ ws) {
-  __shared__ f32x4 s_red[4][16];
+template <int KTW>
+hipError_t launch_gateup(const LayerArgs& L, int grid, size_t lds, hipStream_t s, const void* x,
+                         int x_bf16, int T, const int32_t* ids, const float* w, int k, int prenorm,
+                         uint8_t* ws) {
+  if (x_bf16)
+    hipLaunchKernelGGL((decode_gateup_kernel<KTW, true>), dim3(grid), dim3(kThreads), lds, s, L, x,
+                       T, ids, w, k, prenorm, ws);
+  else
+    hipLaunchKernelGGL((decode_gateup_kernel<KTW, false>), dim3(grid), dim3(kThreads), lds, s, L, x,
+                       T, ids, w, k, prenorm, ws);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kThreads) void decode_down_kernel(
+    LayerArgs L, int T, int k, const void* __restrict__ residual, void* __restrict__ out,
+    int out_bf16, const uint8_t* __restrict__ ws, int stage_lds) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  _Float16* hs = reinterpret_cast<_Float16*>(dyn);     // [T*k + T][I] when staged
+  __shared__ int s_expert[kMaxSlots];
+  __shared__ int s_pidx[kMaxSlots][MOE_MAX_DECODE_TOKENS];
+  __shared__ int s_n;
+  __shared__ f32x4 s_red[kWaves][16];
   const DecodeHeader* hdr = reinterpret_cast<const DecodeHeader*>(ws);
   const _Float16* hin = reinterpret_cast<const _Float16*>(ws + sizeof(DecodeHeader));
   const int H = L.H, I = L.I;
@@ -211,37 +340,84 @@ __global__ __launch_bounds__(256) void decode_down_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const int m = lane & 15, g = lane >> 4;
-  const int n_slots = hdr->n_slots;
+
+  if (threadIdx.x < kMaxSlots) s_expert[threadIdx.x] = hdr->expert[threadIdx.x];
+  if (threadIdx.x < kMaxSlots * MOE_MAX_DECODE_TOKENS)
+    (&s_pidx[0][0])[threadIdx.x] = (&hdr->pidx[0][0])[threadIdx.x];
+  if (threadIdx.x == 0) s_n = hdr->n_slots;
+  __syncthreads();
+  const int n_slots = s_n;
   const int64_t mat = static_cast<int64_t>(I) * H * 5 / 16;
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int nwork = ((n_slots - wid + 3) / 4) * KT;   // (slot, kt) pairs of this wave
-  for (int it = 0; it < nwork; it += 2) {
-    u32x4 c[2], sc[2];
-    f16x8 a[2][8];
+  // h~ of all pairs: loads issued now (L2), stored to LDS below
+  const int hch = (T * k + T) * I / 8;
+  u32x4 hreg[kDownStage];
+  if (stage_lds) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int wi = it + b;
-      if (wi < nwork) {
-        const int slot = wid + 4 * (wi / KT);
-        const int kt = wi % KT;
-        const uint8_t* rec = expert_base(L, hdr->expert[slot]) + 2 * mat +
-                             (static_cast<int64_t>(rt) * KT + kt) * kTileBytes;
+    for (int q = 0; q < kDownStage; ++q)
+      hreg[q] = *reinterpret_cast<const u32x4*>(hin + 8 * min(static_cast<int>(threadIdx.x) + kThreads * q, hch - 1));
+  }
+
+  // records of this wave: (slot, kt) for slots wid, wid+8, ...
+  const int nwork = ((n_slots - wid + kWaves - 1) / kWaves) * KT;
+  auto rec_of = [&](int wi) {
+    wi = min(wi, nwork - 1);
+    const int slot = wid + kWaves * (wi / KT);
+    const int kt = wi % KT;
+    return expert_base(L, s_expert[slot]) + 2 * mat + (static_cast<int64_t>(rt) * KT + kt) * kTileBytes;
+  };
+  u32x4 c[kDownBatch], sc[kDownBatch];
+  if (nwork > 0) {
+#pragma unroll
+    for (int b = 0; b < kDownBatch; ++b) {
+      const uint8_t* rec = rec_of(b);
+      c[b] = load_codes(rec, lane);
+      sc[b] = load_scales(rec, lane);
+    }
+  }
+  if (stage_lds) {
+#pragma unroll
+    for (int q = 0; q < kDownStage; ++q) {
+      const int ch = threadIdx.x + kThreads * q;
+      if (ch < hch) *reinterpret_cast<u32x4*>(hs + 8 * ch) = hreg[q];
+    }
+    for (int ch0 = threadIdx.x + kThreads * kDownStage; ch0 < hch; ch0 += 4 * kThreads) {
+      u32x4 r[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        r[u] = *reinterpret_cast<const u32x4*>(hin + 8 * min(ch0 + kThreads * u, hch - 1));
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (ch0 + kThreads * u < hch) *reinterpret_cast<u32x4*>(hs + 8 * (ch0 + kThreads * u)) = r[u];
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const _Float16* hsrc = stage_lds ? hs : hin;
+  for (int b0 = 0; b0 < nwork; b0 += kDownBatch) {
+    if (b0 > 0) {
+#pragma unroll
+      for (int b = 0; b < kDownBatch; ++b) {
+        const uint8_t* rec = rec_of(b0 + b);
         c[b] = load_codes(rec, lane);
         sc[b] = load_scales(rec, lane);
-        const _Float16* hrow = hin + (static_cast<size_t>(slot) * T + m) * I + kt * kTileCols + 8 * g;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-          a[b][j] = (m < T) ? *reinterpret_cast<const f16x8*>(hrow + 32 * j) : z;
-        }
       }
     }
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      if (it + b < nwork) {
+    for (int b = 0; b < kDownBatch; ++b) {
+      const int wi = b0 + b;
+      if (wi < nwork) {
+        const int slot = wid + kWaves * (wi / KT);
+        const int kt = wi % KT;
+        const int p = (m < T) ? s_pidx[slot][m] : -1;
+        const _Float16* arow = hsrc + static_cast<size_t>(p < 0 ? 0 : p) * I + kt * kTileCols + 8 * g;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc = mfma16(a[b][j], tile_block_weights(c[b], sc[b], j), acc);
+        for (int j = 0; j < 8; ++j) {
+          f16x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+          if (p >= 0) a = *reinterpret_cast<const f16x8*>(arow + 32 * j);
+          acc = mfma16(a, tile_block_weights(c[b], sc[b], j), acc);
+        }
       }
     }
   }
@@ -249,7 +425,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(
   __syncthreads();
   if (wid == 0 && lane < 16) {
     f32x4 Y = s_red[0][lane];
-    for (int q = 1; q < 4; ++q) Y += s_red[q][lane];
+    for (int q = 1; q < kWaves; ++q) Y += s_red[q][lane];
     const int row = rt * kTileRows + lane;
     for (int t = 0; t < T; ++t) {
       const float u = hdr->unscale[t];
@@ -266,12 +442,14 @@ __global__ __launch_bounds__(256) void decode_down_kernel(
   }
 }
 
+constexpr size_t kDownLdsLimit = 96 * 1024;
+
 }  // namespace
 
 size_t decode_workspace_bytes(int T, int k, int H, int I) {
   (void)H;
-  const size_t slots = static_cast<size_t>(T) * k + 1;
-  const size_t h = slots * T * I * sizeof(_Float16);
+  const size_t pairs = static_cast<size_t>(T) * k + T;
+  const size_t h = pairs * I * sizeof(_Float16);
   return sizeof(DecodeHeader) + (h + 255) / 256 * 256;
 }
 
@@ -279,19 +457,33 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
                          const int32_t* ids, const float* w, int k, const void* residual,
                          void* out, int out_bf16, int prenorm, void* ws, hipStream_t s) {
   const int slots_max = T * k + (L.shared ? 1 : 0);
-  const int RT = L.I / kTileRows;
-  const size_t lds = static_cast<size_t>(T) * L.H * sizeof(_Float16);
+  const int RP = L.I / (2 * kTileRows);
+  const size_t lds1 = static_cast<size_t>(T) * L.H * sizeof(_Float16);
+  const int ktw = (L.H / kTileCols + 3) / 4;
+  hipError_t e;
   {
     ProfileScope prof(K_DECODE_GATEUP, s);
-    hipLaunchKernelGGL(decode_gateup_kernel, dim3(slots_max * RT), dim3(256), lds, s, L, x,
-                       x_bf16, T, ids, w, k, prenorm, static_cast<uint8_t*>(ws));
+    uint8_t* w8 = static_cast<uint8_t*>(ws);
+    const int grid = slots_max * RP;
+    switch (ktw) {
+      case 1: e = launch_gateup<1>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
+      case 2: e = launch_gateup<2>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
+      case 3: e = launch_gateup<3>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
+      case 4: e = launch_gateup<4>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
+      case 5: e = launch_gateup<5>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
+      case 6: e = launch_gateup<6>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
+      case 7: e = launch_gateup<7>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
+      default: e = launch_gateup<8>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
+    }
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const size_t pairs_max = static_cast<size_t>(T) * k + T;
+  const size_t lds2 = pairs_max * L.I * sizeof(_Float16);
+  const int stage = lds2 <= kDownLdsLimit ? 1 : 0;
   {
     ProfileScope prof(K_DECODE_DOWN, s);
-    hipLaunchKernelGGL(decode_down_kernel, dim3(L.H / kTileRows), dim3(256), 0, s, L, T, residual,
-                       out, out_bf16, static_cast<const uint8_t*>(ws));
+    hipLaunchKernelGGL(decode_down_kernel, dim3(L.H / kTileRows), dim3(kThreads), stage ? lds2 : 0,
+                       s, L, T, k, residual, out, out_bf16, static_cast<const uint8_t*>(ws), stage);
   }
   return hipGetLastError();
 }

@@ -32,7 +32,10 @@ struct ProfileScope {
 };
 
 // ---------------------------------------------------------------- routing --
-constexpr int kRouteChunkTokens = 64;   // tokens per routing workgroup
+constexpr int kRouteMaxChunkTokens = 256;
+// Tokens per routing workgroup: 64 up to 4096 tokens, 256 above (fewer
+// chunk counts to scan).
+inline __host__ __device__ int route_chunk_tokens(int T) { return T <= 4096 ? 64 : 256; }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              int32_t* rank, int32_t* local_counts, hipStream_t s);

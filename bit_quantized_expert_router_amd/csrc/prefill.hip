@@ -10,16 +10,19 @@
 //
 // Kernels (all enqueued on the caller's stream, no host round trip):
 //   prep     token t: x_hat = x (* rsqrt(mean x^2 + 1e-6)), times a power of
-//            two s_t (max |x_hat s_t| in [0.5, 1)), stored fp16 [T][H]; the
-//            last workgroup turns `counts` into the work-item list.
-//   gateup   work item x 64-row block of I: A = the item's gathered x rows
-//            (fp16, staged in LDS, double buffered per 256-column K tile), B =
-//            the expert's gate and up tiles dequantized in registers (each
-//            weight is dequantized once per item and used by every M tile),
+//            two s_t (max |x_hat s_t| in [0.5, 1)), stored fp16 [T][H]; one
+//            workgroup turns `counts` into the work-item list, the others
+//            write each sorted row's token and routing weight.
+//   gateup   work item x 128-row block of I, 8 waves (one 16-row tile of
+//            gate and of up each): A = the item's gathered x rows (fp16,
+//            staged in LDS, double buffered per 256-column K tile), B = the
+//            expert's gate and up tiles dequantized in registers (each weight
+//            is dequantized once per item and used by every M tile; a 3-deep
+//            register ring keeps two K tiles of weights in flight),
 //            v_mfma_f32_16x16x32_f16, SwiGLU epilogue:
 //            h~[row] = w * silu(g) * u * s_t^2  (fp16, sorted-row order).
-//   down     work item x 256-row block of H: A = h~ rows (LDS), B = down
-//            tiles; y~[row] = W_down h~ (fp16).
+//   down     work item x 256-row block of H, 8 waves x 2 row tiles: A = h~
+//            rows (LDS), B = down tiles; y~[row] = W_down h~ (fp16).
 //   combine  token t: out = (sum_j y~[pair_pos[t,j]] + y~[shared row]) / s_t^2
 //            (+ residual), j ascending: fixed order, no atomics.
 // Workgroup ids are remapped so that consecutive logical ids (the row blocks
@@ -33,14 +36,18 @@ namespace moeq2 {
 
 namespace {
 
+constexpr int kThreads = 512;               // 8 waves
 constexpr int kLdsStride = kTileCols + 8;   // halves per LDS row (pad: no bank conflicts)
-constexpr int kGateupRowsPerBlock = 64;     // 4 waves x 16 rows of I (gate and up)
-constexpr int kDownRowsPerBlock = 256;      // 4 waves x 4 x 16 rows of H
+constexpr int kGateupRowsPerBlock = 128;    // 8 waves x 16 rows of I (gate and up)
+constexpr int kDownRowsPerBlock = 256;      // 8 waves x 2 x 16 rows of H
+constexpr int kAChunks = kGroupRows * kTileCols / 8 / kThreads;   // 16-byte A chunks per thread (4)
 
 struct PrefillWs {
   int32_t* hdr;        // [0] = number of work items
   int4* items;         // {expert, row0, nrows, 0}
   float* unscale;      // [T]  1 / s_t
+  int32_t* row_tok;    // [rows] token of each sorted row
+  float* row_w;        // [rows] routing weight of each sorted row (1 for the shared expert)
   _Float16* x16;       // [T][H]
   _Float16* h;         // [rows][I]
   _Float16* y;         // [rows][H]
@@ -60,6 +67,8 @@ __host__ __device__ inline PrefillWs carve(void* base, int T, int E, int k, int 
   w.hdr = reinterpret_cast<int32_t*>(p); p += 256;
   w.items = reinterpret_cast<int4*>(p); p += align256(sizeof(int4) * max_items(T, E, k));
   w.unscale = reinterpret_cast<float*>(p); p += align256(sizeof(float) * T);
+  w.row_tok = reinterpret_cast<int32_t*>(p); p += align256(sizeof(int32_t) * rows);
+  w.row_w = reinterpret_cast<float*>(p); p += align256(sizeof(float) * rows);
   w.x16 = reinterpret_cast<_Float16*>(p); p += align256(sizeof(_Float16) * static_cast<size_t>(T) * H);
   w.h = reinterpret_cast<_Float16*>(p); p += align256(sizeof(_Float16) * rows * I);
   w.y = reinterpret_cast<_Float16*>(p);
@@ -78,12 +87,14 @@ __device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e)
 // --------------------------------------------------------------------- prep --
 __global__ __launch_bounds__(256) void prefill_prep_kernel(
     LayerArgs L, const void* __restrict__ x, int x_bf16, int T, int k, int prenorm,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int item_cap,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pairs, const float* __restrict__ topk_w, int item_cap,
     PrefillWs ws) {
   __shared__ float s_a[4], s_b[4];
   __shared__ int s_scan[256];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int H = L.H, E = L.E;
+  const int P = T * k;
   if (blockIdx.x < T) {
     const int t = blockIdx.x;
     float ss = 0.0f, mx = 0.0f;
@@ -109,11 +120,24 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     if (threadIdx.x == 0) ws.unscale[t] = 1.0f / s;
     return;
   }
-  // ---- last workgroup: work items from the histogram --------------------
+  if (blockIdx.x > T) {
+    // token and weight of every sorted row (an invalid entry contributes nothing)
+    const int r = (blockIdx.x - T - 1) * 256 + threadIdx.x;
+    if (r < P) {
+      const int p = sorted_pairs[r];
+      const bool ok = p >= 0 && p < P;
+      ws.row_tok[r] = ok ? p / k : 0;
+      ws.row_w[r] = ok ? topk_w[p] : 0.0f;
+    } else if (r < P + T) {
+      ws.row_tok[r] = r - P;
+      ws.row_w[r] = 1.0f;
+    }
+    return;
+  }
+  // ---- work items from the histogram -----------------------------------
   // (rows of expert e: [offsets[e], offsets[e] + counts[e]) clipped to
   // [0, T*k), so inconsistent histogram arrays cannot send any later kernel
   // outside its buffers)
-  const int P = T * k;
   const int nexp = E + (L.shared ? 1 : 0);
   const int per = (nexp + 255) / 256;
   auto rows_of = [&](int e, int& r0, int& n) {
@@ -156,234 +180,253 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
   if (threadIdx.x == 255) ws.hdr[0] = min(s_scan[255], item_cap);
 }
 
-// ------------------------------------------------------------------ gate/up --
-__global__ __launch_bounds__(256) void prefill_gateup_kernel(
-    LayerArgs L, int T, int k, const int32_t* __restrict__ sorted_pairs,
-    const float* __restrict__ topk_w, PrefillWs ws) {
-  __shared__ __align__(16) _Float16 s_a[2][kGroupRows * kLdsStride];
-  __shared__ int s_tok[kGroupRows];
-  __shared__ float s_w[kGroupRows];
-  __shared__ float s_u[kGroupRows];
-  const int H = L.H, I = L.I, E = L.E;
-  const int RB = I / kGateupRowsPerBlock;
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int item = logical / RB;
-  const int rb = logical % RB;
-  if (item >= ws.hdr[0]) return;
-  const int4 it = ws.items[item];
-  const int e = it.x, row0 = it.y, nrows = it.z;
-  const int P = T * k;
-  if (threadIdx.x < nrows) {
-    const int r = row0 + threadIdx.x;
-    int t;
-    float wt;
-    if (e < E) {
-      const int p = sorted_pairs[r];
-      const bool ok = p >= 0 && p < P;   // an invalid entry contributes nothing
-      t = ok ? p / k : 0;
-      wt = ok ? topk_w[p] : 0.0f;
-    } else {
-      t = r - P;
-      wt = 1.0f;
+// A tile staging: up to 64 rows x 256 columns of fp16, kAChunks 16-byte
+// chunks per thread (chunk c -> row c/32, column 8*(c%32)); rows at or beyond
+// nrows are not stored (their MFMA output rows are never written).  Rows are
+// given as element offsets into one global array, so every load stays a
+// global (not flat) load.
+struct ATile {
+  u32x4 r[kAChunks];
+  __device__ __forceinline__ void load(const _Float16* __restrict__ base, const int64_t* rowoff,
+                                       int nrows, int kt) {
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i) {
+      const int c = threadIdx.x + kThreads * i;
+      const int row = c >> 5, c8 = c & 31;
+      r[i] = *reinterpret_cast<const u32x4*>(base + rowoff[min(row, nrows - 1)] + kt * kTileCols + c8 * 8);
     }
-    s_tok[threadIdx.x] = t;
-    s_w[threadIdx.x] = wt;
-    s_u[threadIdx.x] = ws.unscale[t];
   }
-  __syncthreads();
+  __device__ __forceinline__ void store(_Float16* buf, int nrows) const {
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i) {
+      const int c = threadIdx.x + kThreads * i;
+      const int row = c >> 5, c8 = c & 31;
+      if (row < nrows) *reinterpret_cast<u32x4*>(buf + row * kLdsStride + c8 * 8) = r[i];
+    }
+  }
+};
 
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+// One K tile of the gate/up product for NMT 16-row M tiles.
+template <int NMT>
+__device__ __forceinline__ void gateup_ktile(const u32x4 (&b)[4], const _Float16* abuf, int m, int g,
+                                             f32x4 (&acc_g)[4], f32x4 (&acc_u)[4]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const f16x8 bg = tile_block_weights(b[0], b[1], j);
+    const f16x8 bu = tile_block_weights(b[2], b[3], j);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const f16x8 a = *reinterpret_cast<const f16x8*>(abuf + (mt * 16 + m) * kLdsStride + 32 * j + 8 * g);
+      acc_g[mt] = mfma16(a, bg, acc_g[mt]);
+      acc_u[mt] = mfma16(a, bu, acc_u[mt]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ gate/up --
+template <int NMT>
+__device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs& ws, int e, int row0,
+                                            int nrows, int rt, _Float16 (*s_a)[kGroupRows * kLdsStride],
+                                            const int64_t* s_off, const float* s_w, const float* s_u) {
+  const int H = L.H, I = L.I;
+  const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
-  const int nmt = (nrows + 15) / 16;
   const int KT = H / kTileCols;
-  const int rt = rb * 4 + wid;
   const int64_t mat = static_cast<int64_t>(I) * H * 5 / 16;
   const uint8_t* gate = expert_base(L, e) + static_cast<int64_t>(rt) * KT * kTileBytes;
   const uint8_t* up = gate + mat;
-
-  // A tile staging: 64 rows x 32 chunks of 8 halves; thread owns 8 chunks
-  u32x4 areg[8];
-  auto load_a = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int row = c >> 5, c8 = c & 31;
-      if (row < nrows)
-        areg[i] = *reinterpret_cast<const u32x4*>(ws.x16 + static_cast<size_t>(s_tok[row]) * H + kt * kTileCols + c8 * 8);
-    }
+  auto load_b = [&](u32x4 (&b)[4], int kt) {
+    kt = min(kt, KT - 1);
+    b[0] = load_codes(gate + kt * kTileBytes, lane);
+    b[1] = load_scales(gate + kt * kTileBytes, lane);
+    b[2] = load_codes(up + kt * kTileBytes, lane);
+    b[3] = load_scales(up + kt * kTileBytes, lane);
   };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int row = c >> 5, c8 = c & 31;
-      if (row < nrows) *reinterpret_cast<u32x4*>(&s_a[buf][row * kLdsStride + c8 * 8]) = areg[i];
-    }
-  };
-
-  u32x4 cg, sg, cu, su, ncg, nsg, ncu, nsu;
-  load_a(0);
-  cg = load_codes(gate, lane); sg = load_scales(gate, lane);
-  cu = load_codes(up, lane); su = load_scales(up, lane);
-  store_a(0);
+  // two fixed register sets: while one K tile is multiplied, the next one's
+  // weights are in flight (no register copies, so no early waits)
+  u32x4 bA[4], bB[4];
+  load_b(bA, 0);
+  load_b(bB, 1);
+  ATile A;
+  A.load(ws.x16, s_off, nrows, 0);
+  A.store(s_a[0], nrows);
   __syncthreads();
 
   f32x4 acc_g[4], acc_u[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) { acc_g[i] = f32x4{0.f, 0.f, 0.f, 0.f}; acc_u[i] = acc_g[i]; }
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    if (more) {
-      load_a(kt + 1);
-      const uint8_t* gn = gate + (kt + 1) * kTileBytes;
-      const uint8_t* un = up + (kt + 1) * kTileBytes;
-      ncg = load_codes(gn, lane); nsg = load_scales(gn, lane);
-      ncu = load_codes(un, lane); nsu = load_scales(un, lane);
-    }
-    const _Float16* abuf = s_a[kt & 1];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const f16x8 bg = tile_block_weights(cg, sg, j);
-      const f16x8 bu = tile_block_weights(cu, su, j);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (mt < nmt) {
-          const f16x8 a = *reinterpret_cast<const f16x8*>(abuf + (mt * 16 + m) * kLdsStride + 32 * j + 8 * g);
-          acc_g[mt] = mfma16(a, bg, acc_g[mt]);
-          acc_u[mt] = mfma16(a, bu, acc_u[mt]);
-        }
-      }
-    }
-    if (more) {
-      store_a((kt + 1) & 1);
-      cg = ncg; sg = nsg; cu = ncu; su = nsu;
-    }
+  // K tiles in pairs, branch-free: loads past the last tile are clamped to
+  // it (cache hits) so every iteration has the same shape.
+  const int npairs = KT / 2;
+  for (int p = 0; p < npairs; ++p) {
+    const int kt = 2 * p;
+    A.load(ws.x16, s_off, nrows, kt + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    gateup_ktile<NMT>(bA, s_a[0], m, g, acc_g, acc_u);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(bA, kt + 2);
+    A.store(s_a[1], nrows);
+    __syncthreads();
+    A.load(ws.x16, s_off, nrows, min(kt + 2, KT - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    gateup_ktile<NMT>(bB, s_a[1], m, g, acc_g, acc_u);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(bB, kt + 3);
+    A.store(s_a[0], nrows);
     __syncthreads();
   }
+  if (KT & 1) gateup_ktile<NMT>(bA, s_a[0], m, g, acc_g, acc_u);
 
   const int col = rt * 16 + m;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    if (mt < nmt) {
+  for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = mt * 16 + 4 * g + r;
-        if (rl < nrows) {
-          const float u = s_u[rl];
-          const float s = 1.0f / u;
-          const float gv = acc_g[mt][r] * u, uv = acc_u[mt][r] * u;
-          const float h = s_w[rl] * silu(gv) * uv * (s * s);
-          ws.h[static_cast<size_t>(row0 + rl) * I + col] = static_cast<_Float16>(h);
-        }
+    for (int r = 0; r < 4; ++r) {
+      const int rl = mt * 16 + 4 * g + r;
+      if (rl < nrows) {
+        const float u = s_u[rl];
+        const float s = 1.0f / u;
+        const float gv = acc_g[mt][r] * u, uv = acc_u[mt][r] * u;
+        const float h = s_w[rl] * silu(gv) * uv * (s * s);
+        ws.h[static_cast<size_t>(row0 + rl) * I + col] = static_cast<_Float16>(h);
       }
     }
   }
 }
 
-// --------------------------------------------------------------------- down --
-__global__ __launch_bounds__(256) void prefill_down_kernel(LayerArgs L, PrefillWs ws) {
+__global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, PrefillWs ws) {
   __shared__ __align__(16) _Float16 s_a[2][kGroupRows * kLdsStride];
-  const int H = L.H, I = L.I;
-  const int RB = H / kDownRowsPerBlock;
+  __shared__ int64_t s_off[kGroupRows];
+  __shared__ float s_w[kGroupRows];
+  __shared__ float s_u[kGroupRows];
+  const int RB = L.I / kGateupRowsPerBlock;
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
   const int item = logical / RB;
   const int rb = logical % RB;
   if (item >= ws.hdr[0]) return;
   const int4 it = ws.items[item];
   const int e = it.x, row0 = it.y, nrows = it.z;
+  if (threadIdx.x < nrows) {
+    const int t = ws.row_tok[row0 + threadIdx.x];
+    s_off[threadIdx.x] = static_cast<int64_t>(t) * L.H;
+    s_w[threadIdx.x] = ws.row_w[row0 + threadIdx.x];
+    s_u[threadIdx.x] = ws.unscale[t];
+  }
+  __syncthreads();
+  const int rt = rb * 8 + static_cast<int>(threadIdx.x >> 6);
+  switch ((nrows + 15) / 16) {
+    case 1: gateup_body<1>(L, ws, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+    case 2: gateup_body<2>(L, ws, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+    case 3: gateup_body<3>(L, ws, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+    default: gateup_body<4>(L, ws, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+  }
+}
 
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+// --------------------------------------------------------------------- down --
+template <int NMT>
+__device__ __forceinline__ void down_ktile(const u32x4 (&b)[4], const _Float16* abuf, int m, int g,
+                                           f32x4 (&acc)[2][4]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    f16x8 a[NMT];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      a[mt] = *reinterpret_cast<const f16x8*>(abuf + (mt * 16 + m) * kLdsStride + 32 * j + 8 * g);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const f16x8 bq = tile_block_weights(b[2 * q], b[2 * q + 1], j);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) acc[q][mt] = mfma16(a[mt], bq, acc[q][mt]);
+    }
+  }
+}
+
+template <int NMT>
+__device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& ws, int e, int row0,
+                                          int nrows, int rt0, _Float16 (*s_a)[kGroupRows * kLdsStride],
+                                          const int64_t* s_off) {
+  const int H = L.H, I = L.I;
+  const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
-  const int nmt = (nrows + 15) / 16;
   const int KT = I / kTileCols;
   const int64_t mat = static_cast<int64_t>(I) * H * 5 / 16;
-  const int rt0 = rb * 16 + wid * 4;
   const uint8_t* down = expert_base(L, e) + 2 * mat + static_cast<int64_t>(rt0) * KT * kTileBytes;
-
-  u32x4 areg[8];
-  auto load_a = [&](int kt) {
+  auto load_b = [&](u32x4 (&b)[4], int kt) {
+    kt = min(kt, KT - 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int row = c >> 5, c8 = c & 31;
-      if (row < nrows)
-        areg[i] = *reinterpret_cast<const u32x4*>(ws.h + static_cast<size_t>(row0 + row) * I + kt * kTileCols + c8 * 8);
+    for (int q = 0; q < 2; ++q) {
+      const uint8_t* rec = down + (static_cast<int64_t>(q) * KT + kt) * kTileBytes;
+      b[2 * q] = load_codes(rec, lane);
+      b[2 * q + 1] = load_scales(rec, lane);
     }
   };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = threadIdx.x + 256 * i;
-      const int row = c >> 5, c8 = c & 31;
-      if (row < nrows) *reinterpret_cast<u32x4*>(&s_a[buf][row * kLdsStride + c8 * 8]) = areg[i];
-    }
-  };
-
-  u32x4 c[4], sc[4], nc[4], nsc[4];
-  load_a(0);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint8_t* rec = down + static_cast<int64_t>(q) * KT * kTileBytes;
-    c[q] = load_codes(rec, lane);
-    sc[q] = load_scales(rec, lane);
-  }
-  store_a(0);
+  u32x4 bA[4], bB[4];
+  load_b(bA, 0);
+  load_b(bB, 1);
+  ATile A;
+  A.load(ws.h, s_off, nrows, 0);
+  A.store(s_a[0], nrows);
   __syncthreads();
 
-  f32x4 acc[4][4];
+  f32x4 acc[2][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    if (more) {
-      load_a(kt + 1);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint8_t* rec = down + (static_cast<int64_t>(q) * KT + kt + 1) * kTileBytes;
-        nc[q] = load_codes(rec, lane);
-        nsc[q] = load_scales(rec, lane);
-      }
-    }
-    const _Float16* abuf = s_a[kt & 1];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      f16x8 a[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        if (mt < nmt) a[mt] = *reinterpret_cast<const f16x8*>(abuf + (mt * 16 + m) * kLdsStride + 32 * j + 8 * g);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f16x8 b = tile_block_weights(c[q], sc[q], j);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          if (mt < nmt) acc[q][mt] = mfma16(a[mt], b, acc[q][mt]);
-      }
-    }
-    if (more) {
-      store_a((kt + 1) & 1);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { c[q] = nc[q]; sc[q] = nsc[q]; }
-    }
+  const int npairs = KT / 2;
+  for (int p = 0; p < npairs; ++p) {
+    const int kt = 2 * p;
+    A.load(ws.h, s_off, nrows, kt + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    down_ktile<NMT>(bA, s_a[0], m, g, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(bA, kt + 2);
+    A.store(s_a[1], nrows);
+    __syncthreads();
+    A.load(ws.h, s_off, nrows, min(kt + 2, KT - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    down_ktile<NMT>(bB, s_a[1], m, g, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(bB, kt + 3);
+    A.store(s_a[0], nrows);
     __syncthreads();
   }
+  if (KT & 1) down_ktile<NMT>(bA, s_a[0], m, g, acc);
 
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < 2; ++q) {
     const int col = (rt0 + q) * 16 + m;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if (mt < nmt) {
+    for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rl = mt * 16 + 4 * g + r;
-          if (rl < nrows) ws.y[static_cast<size_t>(row0 + rl) * H + col] = static_cast<_Float16>(acc[q][mt][r]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int rl = mt * 16 + 4 * g + r;
+        if (rl < nrows) ws.y[static_cast<size_t>(row0 + rl) * H + col] = static_cast<_Float16>(acc[q][mt][r]);
       }
     }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, PrefillWs ws) {
+  __shared__ __align__(16) _Float16 s_a[2][kGroupRows * kLdsStride];
+  __shared__ int64_t s_off[kGroupRows];
+  const int RB = L.H / kDownRowsPerBlock;
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int item = logical / RB;
+  const int rb = logical % RB;
+  if (item >= ws.hdr[0]) return;
+  const int4 it = ws.items[item];
+  const int e = it.x, row0 = it.y, nrows = it.z;
+  if (threadIdx.x < kGroupRows) s_off[threadIdx.x] = static_cast<int64_t>(row0 + threadIdx.x) * L.I;
+  __syncthreads();
+  const int rt0 = rb * 16 + static_cast<int>(threadIdx.x >> 6) * 2;
+  switch ((nrows + 15) / 16) {
+    case 1: down_body<1>(L, ws, e, row0, nrows, rt0, s_a, s_off); break;
+    case 2: down_body<2>(L, ws, e, row0, nrows, rt0, s_a, s_off); break;
+    case 3: down_body<3>(L, ws, e, row0, nrows, rt0, s_a, s_off); break;
+    default: down_body<4>(L, ws, e, row0, nrows, rt0, s_a, s_off); break;
   }
 }
 
@@ -428,6 +471,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(
 size_t prefill_workspace_bytes(int T, int E, int k, int H, int I) {
   const size_t rows = static_cast<size_t>(T) * k + T;
   return 256 + align256(sizeof(int4) * max_items(T, E, k)) + align256(sizeof(float) * T) +
+         align256(sizeof(int32_t) * rows) + align256(sizeof(float) * rows) +
          align256(sizeof(_Float16) * static_cast<size_t>(T) * H) + align256(sizeof(_Float16) * rows * I) +
          align256(sizeof(_Float16) * rows * H);
 }
@@ -440,25 +484,27 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
   (void)ids;
   const PrefillWs ws = carve(wsp, T, L.E, k, L.H, L.I);
   const int nitems = max_items(T, L.E, k);
+  const long long rows = static_cast<long long>(T) * k + T;
   hipError_t e;
   {
+    const int grid = T + 1 + static_cast<int>((rows + 255) / 256);
     ProfileScope prof(K_PREFILL_PREP, s);
-    hipLaunchKernelGGL(prefill_prep_kernel, dim3(T + 1), dim3(256), 0, s, L, x, x_bf16, T, k,
-                       prenorm, counts, offsets, nitems, ws);
+    hipLaunchKernelGGL(prefill_prep_kernel, dim3(grid), dim3(256), 0, s, L, x, x_bf16, T, k,
+                       prenorm, counts, offsets, sorted_pairs, w, nitems, ws);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
     const long long nb = static_cast<long long>(nitems) * (L.I / kGateupRowsPerBlock);
     const int grid = static_cast<int>((nb + 7) / 8 * 8);
     ProfileScope prof(K_PREFILL_GATEUP, s);
-    hipLaunchKernelGGL(prefill_gateup_kernel, dim3(grid), dim3(256), 0, s, L, T, k, sorted_pairs, w, ws);
+    hipLaunchKernelGGL(prefill_gateup_kernel, dim3(grid), dim3(kThreads), 0, s, L, ws);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
     const long long nb = static_cast<long long>(nitems) * (L.H / kDownRowsPerBlock);
     const int grid = static_cast<int>((nb + 7) / 8 * 8);
     ProfileScope prof(K_PREFILL_DOWN, s);
-    hipLaunchKernelGGL(prefill_down_kernel, dim3(grid), dim3(256), 0, s, L, ws);
+    hipLaunchKernelGGL(prefill_down_kernel, dim3(grid), dim3(kThreads), 0, s, L, ws);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {

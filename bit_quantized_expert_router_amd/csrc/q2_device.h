@@ -99,13 +99,28 @@ __device__ __forceinline__ uint16_t float_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+}  // namespace moeq2
+
+// Wavefront reductions of the ROCm device library (DPP based, fixed order).
+extern "C" __device__ float __ockl_wfred_add_f32(float);
+extern "C" __device__ float __ockl_wfred_max_f32(float);
+extern "C" __device__ uint32_t __ockl_wfred_max_u32(uint32_t);
+
+namespace moeq2 {
+
+__device__ __forceinline__ float wave_sum(float v) { return __ockl_wfred_add_f32(v); }
+__device__ __forceinline__ float wave_max(float v) { return __ockl_wfred_max_f32(v); }
+
+// Bit mask of the lanes (among `active`) whose value equals this lane's;
+// values must be < 2^nbits.  nbits ballots, no shuffles.
+__device__ __forceinline__ uint64_t match_lanes(int v, bool active, int nbits) {
+  uint64_t same = __ballot(active);
+  for (int b = 0; b < nbits; ++b) {
+    const int bit = (v >> b) & 1;
+    const uint64_t bb = __ballot(active && bit);
+    same &= bit ? bb : ~bb;
+  }
+  return same;
 }
 
 // Wave-uniform integer broadcast helper.

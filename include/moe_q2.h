@@ -126,7 +126,8 @@ int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
  * section 一, and "RTX PRO 4500 ...", section 最重要机制, item 3).  Only the
  * selected experts' weights are read.
  *   layer     [host] weights descriptor (above).
- *   x         [device] [T, H] activations, x_dtype MOE_F32 or MOE_BF16.
+ *   x         [device] [T, H] activations, x_dtype MOE_F32 or MOE_BF16;
+ *             16-byte aligned (as are out and residual).
  *   topk_ids, topk_w  [device] [T, k] as produced by moe_route_topk.
  *   residual  [device] [T, H] in out_dtype, or NULL; may alias `out`.
  *   out       [device] [T, H] in out_dtype; must not alias x:

@@ -277,3 +277,57 @@ def test_prefill_1024_biased_sampled(B, layer_full):
 
 def test_prefill_32768_zipf_sampled(B, layer_full):
     _sampled_prefill(B, layer_full, 32768, "zipf", 1, n_sample=8, flags=1)
+
+
+def test_graph_replay_matches_eager(B, layer_full):
+    """route + decode and route + prefill captured in one HIP graph, replayed
+    several times with eager work and synchronisations in between; every
+    replay must give the eager bytes."""
+    L = layer_full
+    rng = synth.rng_for(1, 7, 50)
+    xd, xv = synth.activations(rng, 64 + 2, 3072, "bf16")
+    x_dec = dev_x(xd[:2], "bf16")
+    x_pre = dev_x(xd[2:], "bf16")
+    lg_dec = dev(synth.zipf_logits(rng, 2, 512))
+    lg_pre = dev(synth.zipf_logits(rng, 64, 512))
+    rd = {n: torch.empty(s, dtype=d, device="cuda") for n, s, d in [
+        ("ids", (2, 10), torch.int32), ("w", (2, 10), torch.float32)]}
+    rp = {n: torch.empty(s, dtype=d, device="cuda") for n, s, d in [
+        ("ids", (64, 10), torch.int32), ("w", (64, 10), torch.float32), ("counts", (512,), torch.int32),
+        ("offsets", (513,), torch.int32), ("sp", (640,), torch.int32), ("pp", (640,), torch.int32)]}
+    out_d = torch.empty((2, 3072), dtype=torch.float32, device="cuda")
+    out_p = torch.empty((64, 3072), dtype=torch.float32, device="cuda")
+    ws_d = B.workspace(B.MOE_OP_DECODE, 2, 512, 10, 3072, 768)
+    ws_r = B.workspace(B.MOE_OP_ROUTE, 64, 512, 10, 3072, 768)
+    ws_p = B.workspace(B.MOE_OP_PREFILL, 64, 512, 10, 3072, 768)
+
+    def step():
+        B.moe_route_topk(lg_dec, 10, rd["ids"], rd["w"])
+        B.moe_expert_forward_decode(L.dev, x_dec, rd["ids"], rd["w"], out_d, None, 0, ws_d)
+        B.moe_route_topk(lg_pre, 10, rp["ids"], rp["w"], rp["counts"], rp["offsets"], rp["sp"],
+                         rp["pp"], ws_r)
+        B.moe_expert_forward_prefill(L.dev, x_pre, rp["ids"], rp["w"], rp["counts"], rp["offsets"],
+                                     rp["sp"], rp["pp"], out_p, None, 0, ws_p)
+
+    step()
+    torch.cuda.synchronize()
+    ref_d, ref_p = out_d.clone(), out_p.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                     # warm the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        out_d.zero_()
+        out_p.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_d, ref_d), f"decode replay {r}"
+        assert torch.equal(out_p, ref_p), f"prefill replay {r}"
+        del junk
