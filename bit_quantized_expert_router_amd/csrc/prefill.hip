@@ -37,10 +37,8 @@ namespace moeq2 {
 namespace {
 
 constexpr int kThreads = 512;               // 8 waves
-constexpr int kLdsStride = kTileCols + 8;   // halves per LDS row (pad: no bank conflicts)
 constexpr int kGateupRowsPerBlock = 128;    // 8 waves x 16 rows of I (gate and up)
 constexpr int kDownRowsPerBlock = 256;      // 8 waves x 2 x 16 rows of H
-constexpr int kAChunks = kGroupRows * kTileCols / 8 / kThreads;   // 16-byte A chunks per thread (4)
 
 struct PrefillWs {
   int32_t* hdr;        // [0] = number of work items
@@ -180,35 +178,45 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
   if (threadIdx.x == 255) ws.hdr[0] = min(s_scan[255], item_cap);
 }
 
-// A tile staging: up to 64 rows x 256 columns of fp16, kAChunks 16-byte
-// chunks per thread (chunk c -> row c/32, column 8*(c%32)); rows at or beyond
-// nrows are not stored (their MFMA output rows are never written).  Rows are
-// given as element offsets into one global array, so every load stays a
-// global (not flat) load.
+// A tile staging, fragment-major: the MFMA A fragment of (block j, M tile
+// mt) -- 64 lanes x 8 halves, lane = m + 16 g holding row 16 mt + m, columns
+// 32 j + 8 g .. + 7 of the K tile -- is stored as 1 KB of consecutive 16-byte
+// slots at ((4 j + mt) * 64 + lane) * 16 bytes.  Wave w loads block j = w
+// (8 waves = 8 blocks of a 256-column K tile), one 16-byte global load per
+// M tile, and stores it to its own slot, so the stores and the fragment reads
+// are both conflict-free and need no padding.  Rows are given as element
+// offsets into one global array (loads stay global, not flat); rows at or
+// beyond nrows repeat the last row (their outputs are never written).
+constexpr int kFragHalves = 64 * 8;                 // one fragment
+constexpr int kATileHalves = 8 * 4 * kFragHalves;   // 8 blocks x 4 M tiles = 32 KB
+
+template <int NMT>
 struct ATile {
-  u32x4 r[kAChunks];
+  u32x4 r[NMT];
   __device__ __forceinline__ void load(const _Float16* __restrict__ base, const int64_t* rowoff,
                                        int nrows, int kt) {
+    const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < kAChunks; ++i) {
-      const int c = threadIdx.x + kThreads * i;
-      const int row = c >> 5, c8 = c & 31;
-      r[i] = *reinterpret_cast<const u32x4*>(base + rowoff[min(row, nrows - 1)] + kt * kTileCols + c8 * 8);
-    }
+    for (int mt = 0; mt < NMT; ++mt)
+      r[mt] = *reinterpret_cast<const u32x4*>(base + rowoff[min(mt * 16 + m, nrows - 1)] +
+                                              kt * kTileCols + 32 * j + 8 * g);
   }
-  __device__ __forceinline__ void store(_Float16* buf, int nrows) const {
+  __device__ __forceinline__ void store(_Float16* buf) const {
+    const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < kAChunks; ++i) {
-      const int c = threadIdx.x + kThreads * i;
-      const int row = c >> 5, c8 = c & 31;
-      if (row < nrows) *reinterpret_cast<u32x4*>(buf + row * kLdsStride + c8 * 8) = r[i];
-    }
+    for (int mt = 0; mt < NMT; ++mt)
+      *reinterpret_cast<u32x4*>(buf + ((4 * j + mt) * 64 + lane) * 8) = r[mt];
   }
 };
 
+__device__ __forceinline__ f16x8 a_frag(const _Float16* buf, int j, int mt, int lane) {
+  return *reinterpret_cast<const f16x8*>(buf + ((4 * j + mt) * 64 + lane) * 8);
+}
+
 // One K tile of the gate/up product for NMT 16-row M tiles.
 template <int NMT>
-__device__ __forceinline__ void gateup_ktile(const u32x4 (&b)[4], const _Float16* abuf, int m, int g,
+__device__ __forceinline__ void gateup_ktile(const u32x4 (&b)[4], const _Float16* abuf, int lane,
                                              f32x4 (&acc_g)[4], f32x4 (&acc_u)[4]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -216,7 +224,7 @@ __device__ __forceinline__ void gateup_ktile(const u32x4 (&b)[4], const _Float16
     const f16x8 bu = tile_block_weights(b[2], b[3], j);
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
-      const f16x8 a = *reinterpret_cast<const f16x8*>(abuf + (mt * 16 + m) * kLdsStride + 32 * j + 8 * g);
+      const f16x8 a = a_frag(abuf, j, mt, lane);
       acc_g[mt] = mfma16(a, bg, acc_g[mt]);
       acc_u[mt] = mfma16(a, bu, acc_u[mt]);
     }
@@ -226,7 +234,7 @@ __device__ __forceinline__ void gateup_ktile(const u32x4 (&b)[4], const _Float16
 // ------------------------------------------------------------------ gate/up --
 template <int NMT>
 __device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs& ws, int e, int row0,
-                                            int nrows, int rt, _Float16 (*s_a)[kGroupRows * kLdsStride],
+                                            int nrows, int rt, _Float16 (*s_a)[kATileHalves],
                                             const int64_t* s_off, const float* s_w, const float* s_u) {
   const int H = L.H, I = L.I;
   const int lane = threadIdx.x & 63;
@@ -247,9 +255,9 @@ __device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs&
   u32x4 bA[4], bB[4];
   load_b(bA, 0);
   load_b(bB, 1);
-  ATile A;
+  ATile<NMT> A;
   A.load(ws.x16, s_off, nrows, 0);
-  A.store(s_a[0], nrows);
+  A.store(s_a[0]);
   __syncthreads();
 
   f32x4 acc_g[4], acc_u[4];
@@ -263,20 +271,20 @@ __device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs&
     const int kt = 2 * p;
     A.load(ws.x16, s_off, nrows, kt + 1);
     __builtin_amdgcn_sched_barrier(0);
-    gateup_ktile<NMT>(bA, s_a[0], m, g, acc_g, acc_u);
+    gateup_ktile<NMT>(bA, s_a[0], lane, acc_g, acc_u);
     __builtin_amdgcn_sched_barrier(0);
     load_b(bA, kt + 2);
-    A.store(s_a[1], nrows);
+    A.store(s_a[1]);
     __syncthreads();
     A.load(ws.x16, s_off, nrows, min(kt + 2, KT - 1));
     __builtin_amdgcn_sched_barrier(0);
-    gateup_ktile<NMT>(bB, s_a[1], m, g, acc_g, acc_u);
+    gateup_ktile<NMT>(bB, s_a[1], lane, acc_g, acc_u);
     __builtin_amdgcn_sched_barrier(0);
     load_b(bB, kt + 3);
-    A.store(s_a[0], nrows);
+    A.store(s_a[0]);
     __syncthreads();
   }
-  if (KT & 1) gateup_ktile<NMT>(bA, s_a[0], m, g, acc_g, acc_u);
+  if (KT & 1) gateup_ktile<NMT>(bA, s_a[0], lane, acc_g, acc_u);
 
   const int col = rt * 16 + m;
 #pragma unroll
@@ -296,7 +304,7 @@ __device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs&
 }
 
 __global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, PrefillWs ws) {
-  __shared__ __align__(16) _Float16 s_a[2][kGroupRows * kLdsStride];
+  __shared__ __align__(16) _Float16 s_a[2][kATileHalves];
   __shared__ int64_t s_off[kGroupRows];
   __shared__ float s_w[kGroupRows];
   __shared__ float s_u[kGroupRows];
@@ -325,14 +333,13 @@ __global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, P
 
 // --------------------------------------------------------------------- down --
 template <int NMT>
-__device__ __forceinline__ void down_ktile(const u32x4 (&b)[4], const _Float16* abuf, int m, int g,
+__device__ __forceinline__ void down_ktile(const u32x4 (&b)[4], const _Float16* abuf, int lane,
                                            f32x4 (&acc)[2][4]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     f16x8 a[NMT];
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-      a[mt] = *reinterpret_cast<const f16x8*>(abuf + (mt * 16 + m) * kLdsStride + 32 * j + 8 * g);
+    for (int mt = 0; mt < NMT; ++mt) a[mt] = a_frag(abuf, j, mt, lane);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const f16x8 bq = tile_block_weights(b[2 * q], b[2 * q + 1], j);
@@ -344,7 +351,7 @@ __device__ __forceinline__ void down_ktile(const u32x4 (&b)[4], const _Float16* 
 
 template <int NMT>
 __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& ws, int e, int row0,
-                                          int nrows, int rt0, _Float16 (*s_a)[kGroupRows * kLdsStride],
+                                          int nrows, int rt0, _Float16 (*s_a)[kATileHalves],
                                           const int64_t* s_off) {
   const int H = L.H, I = L.I;
   const int lane = threadIdx.x & 63;
@@ -364,9 +371,9 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
   u32x4 bA[4], bB[4];
   load_b(bA, 0);
   load_b(bB, 1);
-  ATile A;
+  ATile<NMT> A;
   A.load(ws.h, s_off, nrows, 0);
-  A.store(s_a[0], nrows);
+  A.store(s_a[0]);
   __syncthreads();
 
   f32x4 acc[2][4];
@@ -380,20 +387,20 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
     const int kt = 2 * p;
     A.load(ws.h, s_off, nrows, kt + 1);
     __builtin_amdgcn_sched_barrier(0);
-    down_ktile<NMT>(bA, s_a[0], m, g, acc);
+    down_ktile<NMT>(bA, s_a[0], lane, acc);
     __builtin_amdgcn_sched_barrier(0);
     load_b(bA, kt + 2);
-    A.store(s_a[1], nrows);
+    A.store(s_a[1]);
     __syncthreads();
     A.load(ws.h, s_off, nrows, min(kt + 2, KT - 1));
     __builtin_amdgcn_sched_barrier(0);
-    down_ktile<NMT>(bB, s_a[1], m, g, acc);
+    down_ktile<NMT>(bB, s_a[1], lane, acc);
     __builtin_amdgcn_sched_barrier(0);
     load_b(bB, kt + 3);
-    A.store(s_a[0], nrows);
+    A.store(s_a[0]);
     __syncthreads();
   }
-  if (KT & 1) down_ktile<NMT>(bA, s_a[0], m, g, acc);
+  if (KT & 1) down_ktile<NMT>(bA, s_a[0], lane, acc);
 
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -410,7 +417,7 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
 }
 
 __global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, PrefillWs ws) {
-  __shared__ __align__(16) _Float16 s_a[2][kGroupRows * kLdsStride];
+  __shared__ __align__(16) _Float16 s_a[2][kATileHalves];
   __shared__ int64_t s_off[kGroupRows];
   const int RB = L.H / kDownRowsPerBlock;
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
