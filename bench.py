@@ -16,6 +16,7 @@ an error: this build runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,6 +24,7 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 MFMA, TFLOP/s
 
@@ -167,7 +169,7 @@ def main():
         dn = kern.get("decode_down_kernel", (1, float("nan")))
         rt = kern.get("route_topk_kernel", (1, float("nan")))
         gu_ms = gu[1] / gu[0]
-        gu_bytes = slots * 2 * MAT_BYTES + T * H * 2
+        gu_bytes = slots * 2 * MAT_BYTES + T * H * 2 + (T * K + T) * I * 2   # weights, x, h
         return {
             "T": T, "routing": kind, "launch": "hip_graph", "ms_per_layer": ms,
             "ms_per_layer_eager": ms_eager, "tokens_per_s": T * 1000.0 / ms,
@@ -222,7 +224,7 @@ def main():
         gemm_ms = kms.get("prefill_gateup", 0) + kms.get("prefill_down", 0)
         gu_ms = kms.get("prefill_gateup", float("nan"))
         gu_flops = (T * K + T) * 2 * 2 * H * I
-        gu_bytes = (ne + 1) * 2 * MAT_BYTES + T * H * 2
+        gu_bytes = (ne + 1) * 2 * MAT_BYTES + T * H * 2 + (T * K + T) * I * 2   # weights, x, h
         return {
             "T": T, "routing": "router+bias N(0,0.5)", "launch": "hip_graph", "ms_per_layer": ms,
             "ms_per_layer_eager": ms_eager, "tokens_per_s": T * 1000.0 / ms,
@@ -232,6 +234,15 @@ def main():
             "TFLOPs": flops / ms / 1e9, "mfma_frac": flops / ms / 1e9 / MFMA_F16_PEAK_TFLOPS,
             "kernel_ms": kms, "grouped_gemm_ms": gemm_ms,
             "gateup_TFLOPs": gu_flops / gu_ms / 1e9, "gateup_GBps": gu_bytes / gu_ms / 1e6,
+            "roofline": {
+                "bound": "hbm", "kernel": "prefill_gateup_kernel",
+                "achieved": round(gu_bytes / gu_ms / 1e6, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gu_bytes / gu_ms / 1e6 / HBM_PEAK_GBS, 4),
+                "traffic": pmc_traffic("prefill_gateup_T1024_pmc_traffic.txt", "prefill_gateup_kernel"),
+                "algorithmic_bytes_per_launch": float(gu_bytes), "kernel_us": round(gu_ms * 1e3, 2),
+                "mfma_TFLOPs": round(gu_flops / gu_ms / 1e9, 1),
+                "mfma_frac": round(gu_flops / gu_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+            },
         }
 
     only = args.only
@@ -276,7 +287,10 @@ def main():
         line["roofline"] = {
             "bound": "hbm", "kernel": "decode_gateup_kernel",
             "achieved": round(d["gateup_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(d["gateup_GBps"] / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(d["gateup_GBps"] / HBM_PEAK_GBS, 4),
+            "traffic": pmc_traffic("decode_gateup_T1_pmc_traffic.txt", "decode_gateup_kernel"),
+            "algorithmic_bytes_per_launch": d["gateup_bytes_per_launch"],
+            "kernel_us": round(d["kernel_ms"]["decode_gateup"] * 1e3, 3),
             "layer_GBps": round(d["GBps"], 1), "layer_frac": round(d["hbm_frac"], 4),
         }
     line["results"] = results
@@ -284,6 +298,31 @@ def main():
         line["cpu_baseline"] = cpu
     line["weights_generated_s"] = round(gen_s, 1)
     print(json.dumps(line))
+
+
+def pmc_traffic(name: str, kernel: str):
+    """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, each scaled
+    by its copy-kernel calibration) from the committed counter summary
+    profiles/<name>; None when the file is absent or when the kernel's
+    sources no longer hash to what they were when the counters were taken."""
+    path = os.path.join(ROOT, "profiles", name)
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return None
+    kv = dict(l.split(": ", 1) for l in lines if ": " in l and not l.startswith("#"))
+    srcs = kv.get("sources", "").split()
+    if kv.get("kernel") != kernel or not srcs:
+        return None
+    h = hashlib.sha256()
+    for f in srcs:
+        try:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        except OSError:
+            return None
+    if h.hexdigest() != kv.get("source_sha256"):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(seconds: float):

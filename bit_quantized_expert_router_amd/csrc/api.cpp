@@ -117,21 +117,28 @@ size_t route_workspace(int T, int E, int k) {
 
 }  // namespace
 
-ProfileScope::ProfileScope(int kernel_id, hipStream_t s) : id(kernel_id), stream(s), ev0(nullptr) {
+ProfileScope::ProfileScope(int kernel_id)
+    : id(kernel_id), ev0(nullptr), ev1(nullptr), committed(false) {
   Profiler& p = prof();
   if (!p.on) return;
   std::lock_guard<std::mutex> g(p.mu);
-  hipEvent_t e = p.get();
-  if (e && hipEventRecord(e, s) == hipSuccess) ev0 = e;
+  ev0 = p.get();
+  ev1 = ev0 ? p.get() : nullptr;
+  if (!ev1 && ev0) { p.pool.push_back(ev0); ev0 = nullptr; }
 }
+
+void ProfileScope::commit() { committed = ev0 != nullptr; }
 
 ProfileScope::~ProfileScope() {
   if (!ev0) return;
   Profiler& p = prof();
   std::lock_guard<std::mutex> g(p.mu);
-  hipEvent_t e1 = p.get();
-  if (e1 && hipEventRecord(e1, stream) == hipSuccess)
-    p.pending[id].emplace_back(static_cast<hipEvent_t>(ev0), e1);
+  if (committed) {
+    p.pending[id].emplace_back(ev0, ev1);
+  } else {
+    p.pool.push_back(ev0);
+    p.pool.push_back(ev1);
+  }
 }
 
 }  // namespace moeq2

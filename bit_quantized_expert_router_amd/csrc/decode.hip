@@ -314,13 +314,12 @@ template <int KTW>
 hipError_t launch_gateup(const LayerArgs& L, int grid, size_t lds, hipStream_t s, const void* x,
                          int x_bf16, int T, const int32_t* ids, const float* w, int k, int prenorm,
                          uint8_t* ws) {
+  const uint32_t l = static_cast<uint32_t>(lds);
   if (x_bf16)
-    hipLaunchKernelGGL((decode_gateup_kernel<KTW, true>), dim3(grid), dim3(kThreads), lds, s, L, x,
-                       T, ids, w, k, prenorm, ws);
-  else
-    hipLaunchKernelGGL((decode_gateup_kernel<KTW, false>), dim3(grid), dim3(kThreads), lds, s, L, x,
-                       T, ids, w, k, prenorm, ws);
-  return hipGetLastError();
+    return launch_kernel(K_DECODE_GATEUP, decode_gateup_kernel<KTW, true>, dim3(grid),
+                         dim3(kThreads), l, s, L, x, T, ids, w, k, prenorm, ws);
+  return launch_kernel(K_DECODE_GATEUP, decode_gateup_kernel<KTW, false>, dim3(grid),
+                       dim3(kThreads), l, s, L, x, T, ids, w, k, prenorm, ws);
 }
 
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(
@@ -462,7 +461,6 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
   const int ktw = (L.H / kTileCols + 3) / 4;
   hipError_t e;
   {
-    ProfileScope prof(K_DECODE_GATEUP, s);
     uint8_t* w8 = static_cast<uint8_t*>(ws);
     const int grid = slots_max * RP;
     switch (ktw) {
@@ -480,12 +478,9 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
   const size_t pairs_max = static_cast<size_t>(T) * k + T;
   const size_t lds2 = pairs_max * L.I * sizeof(_Float16);
   const int stage = lds2 <= kDownLdsLimit ? 1 : 0;
-  {
-    ProfileScope prof(K_DECODE_DOWN, s);
-    hipLaunchKernelGGL(decode_down_kernel, dim3(L.H / kTileRows), dim3(kThreads), stage ? lds2 : 0,
-                       s, L, T, k, residual, out, out_bf16, static_cast<const uint8_t*>(ws), stage);
-  }
-  return hipGetLastError();
+  return launch_kernel(K_DECODE_DOWN, decode_down_kernel, dim3(L.H / kTileRows), dim3(kThreads),
+                       static_cast<uint32_t>(stage ? lds2 : 0), s, L, T, k, residual, out,
+                       out_bf16, static_cast<const uint8_t*>(ws), stage);
 }
 
 }  // namespace moeq2

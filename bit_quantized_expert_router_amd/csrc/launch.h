@@ -2,6 +2,7 @@
 // kernel translation units.  Internal to the library.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -21,15 +22,29 @@ enum KernelId {
   K_NUM_KERNELS
 };
 
-// Records a start event before and a stop event after `launch` when the
-// measurement hooks are on.  Defined in api.cpp.
+// Start and stop events of one launch while the measurement hooks are on
+// (both null otherwise).  hipExtLaunchKernel stamps them with the begin and
+// end of the dispatch itself, so their difference is the kernel's execution
+// time without the gap between launches.  Defined in api.cpp.
 struct ProfileScope {
-  ProfileScope(int kernel_id, hipStream_t s);
+  explicit ProfileScope(int kernel_id);
   ~ProfileScope();
+  void commit();  // the launch was enqueued: keep the pair for moe_profile_query
   int id;
-  hipStream_t stream;
-  void* ev0;
+  hipEvent_t ev0, ev1;
+  bool committed;
 };
+
+// Every kernel of the library is enqueued through here.
+template <typename F, typename... Args>
+hipError_t launch_kernel(int kernel_id, F kernel, dim3 grid, dim3 block, uint32_t lds,
+                         hipStream_t s, Args... args) {
+  ProfileScope prof(kernel_id);
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, s, prof.ev0, prof.ev1, 0u, args...);
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) prof.commit();
+  return e;
+}
 
 // ---------------------------------------------------------------- routing --
 constexpr int kRouteMaxChunkTokens = 256;

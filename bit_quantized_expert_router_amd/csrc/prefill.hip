@@ -17,8 +17,9 @@
 //            gate and of up each): A = the item's gathered x rows (fp16,
 //            staged in LDS, double buffered per 256-column K tile), B = the
 //            expert's gate and up tiles dequantized in registers (each weight
-//            is dequantized once per item and used by every M tile; a 3-deep
-//            register ring keeps two K tiles of weights in flight),
+//            is dequantized once per item and used by every M tile; two
+//            register sets alternate, so the next K tile's weights are in
+//            flight while one is multiplied),
 //            v_mfma_f32_16x16x32_f16, SwiGLU epilogue:
 //            h~[row] = w * silu(g) * u * s_t^2  (fp16, sorted-row order).
 //   down     work item x 256-row block of H, 8 waves x 2 row tiles: A = h~
@@ -495,31 +496,26 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
   hipError_t e;
   {
     const int grid = T + 1 + static_cast<int>((rows + 255) / 256);
-    ProfileScope prof(K_PREFILL_PREP, s);
-    hipLaunchKernelGGL(prefill_prep_kernel, dim3(grid), dim3(256), 0, s, L, x, x_bf16, T, k,
-                       prenorm, counts, offsets, sorted_pairs, w, nitems, ws);
+    e = launch_kernel(K_PREFILL_PREP, prefill_prep_kernel, dim3(grid), dim3(256), 0, s, L, x,
+                      x_bf16, T, k, prenorm, counts, offsets, sorted_pairs, w, nitems, ws);
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (e != hipSuccess) return e;
   {
     const long long nb = static_cast<long long>(nitems) * (L.I / kGateupRowsPerBlock);
     const int grid = static_cast<int>((nb + 7) / 8 * 8);
-    ProfileScope prof(K_PREFILL_GATEUP, s);
-    hipLaunchKernelGGL(prefill_gateup_kernel, dim3(grid), dim3(kThreads), 0, s, L, ws);
+    e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel, dim3(grid), dim3(kThreads), 0, s,
+                      L, ws);
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (e != hipSuccess) return e;
   {
     const long long nb = static_cast<long long>(nitems) * (L.H / kDownRowsPerBlock);
     const int grid = static_cast<int>((nb + 7) / 8 * 8);
-    ProfileScope prof(K_PREFILL_DOWN, s);
-    hipLaunchKernelGGL(prefill_down_kernel, dim3(grid), dim3(kThreads), 0, s, L, ws);
+    e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel, dim3(grid), dim3(kThreads), 0, s, L,
+                      ws);
   }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  {
-    ProfileScope prof(K_PREFILL_COMBINE, s);
-    hipLaunchKernelGGL(prefill_combine_kernel, dim3(T), dim3(256), 0, s, T, L.H, k,
-                       L.shared ? 1 : 0, pair_pos, residual, out, out_bf16, ws);
-  }
-  return hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_kernel(K_PREFILL_COMBINE, prefill_combine_kernel, dim3(T), dim3(256), 0, s, T,
+                       L.H, k, L.shared ? 1 : 0, pair_pos, residual, out, out_bf16, ws);
 }
 
 }  // namespace moeq2

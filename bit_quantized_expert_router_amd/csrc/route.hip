@@ -218,35 +218,30 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
   const int n_chunks = (T + ct - 1) / ct;
   const int threads = T <= 4 ? 64 * T : 1024;
   const int per = (E + kWave - 1) / kWave;
-  ProfileScope prof(K_ROUTE_TOPK, s);
-#define MOE_ROUTE_LAUNCH(P)                                                                  \
-  hipLaunchKernelGGL(route_topk_kernel<P>, dim3(n_chunks), dim3(threads), 0, s, logits, T, E, k, \
-                     ct, ids, w, rank, local_counts, n_chunks)
-  if (per <= 1) MOE_ROUTE_LAUNCH(1);
-  else if (per <= 2) MOE_ROUTE_LAUNCH(2);
-  else if (per <= 4) MOE_ROUTE_LAUNCH(4);
-  else if (per <= 8) MOE_ROUTE_LAUNCH(8);
-  else MOE_ROUTE_LAUNCH(16);
+#define MOE_ROUTE_LAUNCH(P)                                                                 \
+  launch_kernel(K_ROUTE_TOPK, route_topk_kernel<P>, dim3(n_chunks), dim3(threads), 0, s, logits, \
+                T, E, k, ct, ids, w, rank, local_counts, n_chunks)
+  if (per <= 1) return MOE_ROUTE_LAUNCH(1);
+  if (per <= 2) return MOE_ROUTE_LAUNCH(2);
+  if (per <= 4) return MOE_ROUTE_LAUNCH(4);
+  if (per <= 8) return MOE_ROUTE_LAUNCH(8);
+  return MOE_ROUTE_LAUNCH(16);
 #undef MOE_ROUTE_LAUNCH
-  return hipGetLastError();
 }
 
 hipError_t launch_route_scan(const int32_t* local_counts, int32_t* base, int E, int n_chunks,
                              int total_pairs, int32_t* counts, int32_t* offsets, hipStream_t s) {
-  ProfileScope prof(K_ROUTE_SCAN, s);
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, local_counts, base, E,
-                     n_chunks, total_pairs, counts, offsets);
-  return hipGetLastError();
+  return launch_kernel(K_ROUTE_SCAN, route_scan_kernel, dim3(1), dim3(1024), 0, s, local_counts,
+                       base, E, n_chunks, total_pairs, counts, offsets);
 }
 
 hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const int32_t* base,
                                 int T, int k, int n_chunks, int32_t* sorted_pairs,
                                 int32_t* pair_pos, hipStream_t s) {
   const int P = T * k;
-  ProfileScope prof(K_ROUTE_SCATTER, s);
-  hipLaunchKernelGGL(route_scatter_kernel, dim3((P + 255) / 256), dim3(256), 0, s, ids, rank,
-                     base, P, k, n_chunks, route_chunk_tokens(T), sorted_pairs, pair_pos);
-  return hipGetLastError();
+  return launch_kernel(K_ROUTE_SCATTER, route_scatter_kernel, dim3((P + 255) / 256), dim3(256), 0,
+                       s, ids, rank, base, P, k, n_chunks, route_chunk_tokens(T), sorted_pairs,
+                       pair_pos);
 }
 
 }  // namespace moeq2

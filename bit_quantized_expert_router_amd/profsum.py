@@ -1,0 +1,131 @@
+"""Summaries of rocprofv3 CSV output for this library's kernels.
+
+  python -m bit_quantized_expert_router_amd.profsum stats DIR
+      per-kernel dispatch count and average / min / max duration from the
+      `*kernel_stats.csv` that `rocprofv3 --kernel-trace --stats
+      --output-format csv -d DIR` writes.
+
+  python -m bit_quantized_expert_router_amd.profsum traffic FETCH_DIR WRITE_DIR
+          --kernel NAME --calib-bytes N [--sources FILE ...]
+      HBM bytes per dispatch of kernel NAME from two `rocprofv3 --pmc`
+      passes (FETCH_SIZE, then WRITE_SIZE; both counters are in KiB per
+      dispatch).  Each counter is scaled by the factor that makes it read N
+      bytes on the largest device-to-device copy kernel of the same run (a
+      plain copy of N bytes reads N and writes N).  With --sources, the
+      sha256 of those files is printed so that a reader can tell whether the
+      kernel has changed since the counters were taken.
+
+Reads CSV only; runs nothing.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import statistics
+import sys
+
+COPY_KERNEL = "copyBuffer"
+
+
+def _short(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "").replace("moeq2::", "")
+    return n.split("(")[0].replace("void ", "").strip()
+
+
+def _one(pattern: str, root: str) -> str:
+    found = sorted(glob.glob(os.path.join(root, "**", pattern), recursive=True))
+    if not found:
+        sys.exit(f"profsum: no {pattern} under {root}")
+    return found[0]
+
+
+def stats(root: str, match: str = "moeq2") -> list[dict]:
+    rows = list(csv.DictReader(open(_one("*kernel_stats.csv", root))))
+    out = []
+    for r in rows:
+        if match not in r["Name"] and COPY_KERNEL not in r["Name"]:
+            continue
+        out.append({"kernel": _short(r["Name"]), "calls": int(r["Calls"]),
+                    "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
+                    "max_us": float(r["MaxNs"]) / 1e3,
+                    "total_ms": float(r["TotalDurationNs"]) / 1e6})
+    return out
+
+
+def counter_per_dispatch(root: str, counter: str) -> dict[str, list[float]]:
+    """kernel -> [counter value of each dispatch] (values summed over the
+    per-XCD / per-instance rows of one dispatch)."""
+    per = {}
+    for f in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            did = next((r[c] for c in ("Dispatch_Id", "Dispatch-Id", "Correlation_Id") if c in r), "")
+            key = (_short(r.get("Kernel_Name", r.get("Kernel-Name", ""))), did)
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out: dict[str, list[float]] = {}
+    for (k, _), v in per.items():
+        out.setdefault(k, []).append(v)
+    return out
+
+
+def sha256_of(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(prog="profsum")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--calib-bytes", type=int, required=True)
+    t.add_argument("--sources", nargs="*", default=[])
+    a = ap.parse_args(argv)
+
+    if a.cmd == "stats":
+        print(f"{'kernel':<40} {'calls':>7} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'total_ms':>10}")
+        for r in stats(a.dir):
+            print(f"{r['kernel'][:40]:<40} {r['calls']:>7} {r['avg_us']:>9.2f} {r['min_us']:>9.2f} "
+                  f"{r['max_us']:>9.2f} {r['total_ms']:>10.3f}")
+        return
+
+    res = {}
+    for label, root, counter in (("fetch", a.fetch_dir, "FETCH_SIZE"),
+                                 ("write", a.write_dir, "WRITE_SIZE")):
+        per = counter_per_dispatch(root, counter)
+        copies = [v for k, vs in per.items() if COPY_KERNEL in k for v in vs]
+        if not copies:
+            sys.exit(f"profsum: no {COPY_KERNEL} dispatch with {counter} in {root}")
+        calib_kib = max(copies)
+        factor = a.calib_bytes / (calib_kib * 1024.0)
+        vals = [v for k, vs in per.items() if k.split("<")[0] == a.kernel for v in vs]
+        if not vals:
+            sys.exit(f"profsum: kernel {a.kernel} has no {counter} rows in {root}")
+        kib = statistics.mean(vals)
+        res[label] = (counter, calib_kib, factor, len(vals), kib, kib * 1024.0 * factor)
+    print(f"kernel: {a.kernel}")
+    for label, (counter, calib_kib, factor, n, kib, b) in res.items():
+        print(f"{label}_counter: {counter}")
+        print(f"{label}_copy_KiB: {calib_kib:.1f}")
+        print(f"{label}_scale: {factor:.5f}")
+        print(f"{label}_dispatches: {n}")
+        print(f"{label}_KiB_per_dispatch: {kib:.1f}")
+        print(f"{label}_bytes_per_launch: {b:.0f}")
+    print(f"traffic_bytes_per_launch: {res['fetch'][5] + res['write'][5]:.0f}")
+    if a.sources:
+        print(f"sources: {' '.join(a.sources)}")
+        print(f"source_sha256: {sha256_of(a.sources)}")
+
+
+if __name__ == "__main__":
+    main()

@@ -169,10 +169,12 @@ const char* moe_last_error(void);
 
 /*
  * Measurement hooks (host-side only; no device memory).  When enabled, every
- * kernel launch is bracketed by a pair of hipEvents on its stream;
- * moe_profile_query returns, per kernel id, the number of launches and the
- * summed event time (it waits for the recorded events).  Ids run
- * 0..moe_profile_num_kernels()-1; moe_profile_kernel_name names them.
+ * kernel is launched with a pair of hipEvents that the runtime stamps with the
+ * begin and end of that dispatch (hipExtLaunchKernel), so the pair measures
+ * the kernel's execution alone; moe_profile_query returns, per kernel id, the
+ * number of launches and the summed time (it waits for the events).  Ids run
+ * 0..moe_profile_num_kernels()-1; moe_profile_kernel_name names them.  Leave
+ * the hooks off while a stream is being captured into a graph.
  */
 int moe_profile_enable(int on);
 int moe_profile_reset(void);
