@@ -2,12 +2,14 @@
 """Benchmark of the routed-MoE expert layer on 2-bit weights (one MI355X).
 
 A step is one MoE layer for one batch of synthetic input through the HIP
-library: router top-k (moe_route_topk) then the expert layer.  The headline
-workload is the decode step of one token on a 512-expert layer (top-10 + 1
-shared, hidden 3072, intermediate 768, 2,211,840 bytes per expert); the same
-run also measures verify windows of 2 and 3 tokens and a 1024-token prefill
-chunk (router histogram + grouped expert GEMMs + combine) and reports them in
-the same JSON line.  Weights rotate over 16 distinct layers (about 18 GB) so
+library: router top-k and the expert layer.  The headline workload is the
+decode step of one token on a 512-expert layer (top-10 + 1 shared, hidden
+3072, intermediate 768, 2,211,840 bytes per expert) through
+moe_expert_forward_decode_routed (top-k inside the expert kernels); the same
+run also measures that step as two calls (moe_route_topk, then
+moe_expert_forward_decode), verify windows of 2 and 3 tokens and a
+1024-token prefill chunk (router histogram + grouped expert GEMMs + combine)
+and reports them in the same JSON line.  Weights rotate over 16 distinct layers (about 18 GB) so
 that no step finds its experts in the 256 MB last-level cache.
 
 Prints one JSON line (see the keys below).  `--gpus N` with N > 1 exits with
@@ -42,7 +44,8 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", default="", help="decode1|decode2|decode3|prefill (profiling runs)")
+    ap.add_argument("--only", default="",
+                    help="decode1|decode1_two_calls|decode2|decode3|prefill (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -133,7 +136,7 @@ def main():
         return {k: v for k, v in B.profile_results().items() if v[0] > 0}
 
     # ---------------------------------------------------------------- decode
-    def decode_case(T, kind, n_steps, warmup):
+    def decode_case(T, kind, n_steps, warmup, routed=True):
         total = n_steps * 2 + warmup
         rng = synth.rng_for(1, 100 + T, 0)
         xd, xv = synth.activations(rng, min(total, 64) * T, H, "bf16")
@@ -152,8 +155,12 @@ def main():
 
         def step(i):
             L = layers[i % len(layers)]
-            B.moe_route_topk(logits[i], K, ids[i], wts[i])
-            B.moe_expert_forward_decode(L, xs[i % nx], ids[i], wts[i], out, None, 0, ws)
+            if routed:   # one call: top-k inside the expert kernels
+                B.moe_expert_forward_decode_routed(L, xs[i % nx], logits[i], K, out, ids[i], wts[i],
+                                                   None, 0, ws)
+            else:        # moe_route_topk, then the expert layer
+                B.moe_route_topk(logits[i], K, ids[i], wts[i])
+                B.moe_expert_forward_decode(L, xs[i % nx], ids[i], wts[i], out, None, 0, ws)
 
         ms_eager = timed(step, n_steps, warmup)
         ncap = 2 * len(layers)
@@ -167,18 +174,21 @@ def main():
         step_bytes = wbytes + io
         gu = kern.get("decode_gateup_kernel", (1, float("nan")))
         dn = kern.get("decode_down_kernel", (1, float("nan")))
-        rt = kern.get("route_topk_kernel", (1, float("nan")))
         gu_ms = gu[1] / gu[0]
+        kms = {"decode_gateup": gu_ms, "decode_down": dn[1] / dn[0]}
+        if "route_topk_kernel" in kern:
+            rt = kern["route_topk_kernel"]
+            kms = {"route_topk": rt[1] / rt[0], **kms}
         gu_bytes = slots * 2 * MAT_BYTES + T * H * 2 + (T * K + T) * I * 2   # weights, x, h
         return {
-            "T": T, "routing": kind, "launch": "hip_graph", "ms_per_layer": ms,
+            "T": T, "routing": kind, "calls": "decode_routed" if routed else "route_topk+decode",
+            "launch": "hip_graph", "ms_per_layer": ms,
             "ms_per_layer_eager": ms_eager, "tokens_per_s": T * 1000.0 / ms,
             "tokens_per_s_eager": T * 1000.0 / ms_eager,
             "distinct_experts_per_step": float(slots - 1),
             "algorithmic_bytes_per_step": float(step_bytes),
             "GBps": step_bytes / ms / 1e6, "hbm_frac": step_bytes / ms / 1e6 / HBM_PEAK_GBS,
-            "kernel_ms": {"route_topk": rt[1] / rt[0], "decode_gateup": gu_ms,
-                          "decode_down": dn[1] / dn[0]},
+            "kernel_ms": kms,
             "gateup_bytes_per_launch": float(gu_bytes),
             "gateup_GBps": gu_bytes / gu_ms / 1e6,
         }
@@ -248,6 +258,9 @@ def main():
     only = args.only
     if only in ("", "decode1"):
         results["decode_T1"] = decode_case(1, "router", args.steps, args.warmup)
+    if only in ("", "decode1_two_calls"):
+        results["decode_T1_two_calls"] = decode_case(1, "router", args.steps // 2, args.warmup,
+                                                     routed=False)
     if only in ("", "decode2"):
         results["decode_T2"] = decode_case(2, "zipf", args.steps // 2, args.warmup)
     if only in ("", "decode3"):
@@ -275,7 +288,8 @@ def main():
         "dtype": "fp16",
         "data": "synthetic",
         "config": {
-            "workload": "moe_layer_decode_T1: route + expert layer, 1 token, 512 experts top-10 + 1 shared, "
+            "workload": "moe_layer_decode_T1: router top-k + expert layer (moe_expert_forward_decode_routed), "
+                        "1 token, 512 experts top-10 + 1 shared, "
                         "hidden 3072, inter 768, Q2 2-bit weights (2,211,840 B/expert), "
                         f"{args.layers} rotating layers",
             "tokens_per_step": 1, "experts": E, "top_k": K, "hidden": H, "inter": I,

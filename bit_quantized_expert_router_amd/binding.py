@@ -24,7 +24,7 @@ MOE_FLAG_PRENORM_RMS = 1
 MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL = 0, 1, 2
 
 EXPORTS = ["moe_workspace_bytes", "moe_route_topk", "moe_expert_forward_decode",
-           "moe_expert_forward_prefill", "moe_status_string", "moe_last_error",
+           "moe_expert_forward_decode_routed", "moe_expert_forward_prefill", "moe_status_string", "moe_last_error",
            "moe_profile_enable", "moe_profile_reset", "moe_profile_num_kernels",
            "moe_profile_kernel_name", "moe_profile_query"]
 
@@ -53,6 +53,9 @@ def _load():
     lib.moe_expert_forward_decode.argtypes = [C.POINTER(_Layer), vp, i32, i32, vp, vp, i32, vp, vp,
                                               i32, C.c_uint32, vp, sz, vp]
     lib.moe_expert_forward_decode.restype = C.c_int
+    lib.moe_expert_forward_decode_routed.argtypes = [C.POINTER(_Layer), vp, i32, i32, vp, i32, vp, vp,
+                                                     vp, vp, i32, C.c_uint32, vp, sz, vp]
+    lib.moe_expert_forward_decode_routed.restype = C.c_int
     lib.moe_expert_forward_prefill.argtypes = [C.POINTER(_Layer), vp, i32, i32, vp, vp, i32, vp, vp,
                                                vp, vp, vp, vp, i32, C.c_uint32, vp, sz, vp]
     lib.moe_expert_forward_prefill.restype = C.c_int
@@ -144,6 +147,16 @@ def moe_expert_forward_decode(layer: Layer, x, topk_ids, topk_w, out, residual=N
                                          _ptr(topk_w), k, _ptr(residual), _ptr(out), _dtype_code(out),
                                          flags, _ptr(ws), 0 if ws is None else ws.numel(),
                                          _stream(stream)))
+
+
+def moe_expert_forward_decode_routed(layer: Layer, x, logits, k, out, topk_ids=None, topk_w=None,
+                                     residual=None, flags=0, ws=None, stream=None):
+    T = logits.shape[0]
+    c = layer._c()
+    _check(lib.moe_expert_forward_decode_routed(C.byref(c), _ptr(x), _dtype_code(x), T, _ptr(logits), k,
+                                                _ptr(topk_ids), _ptr(topk_w), _ptr(residual), _ptr(out),
+                                                _dtype_code(out), flags, _ptr(ws),
+                                                0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def moe_expert_forward_prefill(layer: Layer, x, topk_ids, topk_w, counts, offsets, sorted_pairs,

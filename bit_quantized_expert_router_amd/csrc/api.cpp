@@ -211,9 +211,10 @@ int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t
   int32_t* base = reinterpret_cast<int32_t*>(ws + rank_b + cnt_b);
   if ((e = launch_route_topk(logits, T, E, k, topk_ids, topk_w, rank, local, s)) != hipSuccess)
     return hip_fail(e, "route_topk launch");
-  if ((e = launch_route_scan(local, base, E, chunks, T * k, counts, offsets, s)) != hipSuccess)
+  if ((e = launch_route_expert_scan(local, base, E, chunks, counts, s)) != hipSuccess)
     return hip_fail(e, "route_scan launch");
-  if ((e = launch_route_scatter(topk_ids, rank, base, T, k, chunks, sorted_pairs, pair_pos, s)) != hipSuccess)
+  if ((e = launch_route_scatter(topk_ids, rank, base, counts, E, T, k, chunks, offsets, sorted_pairs,
+                                pair_pos, s)) != hipSuccess)
     return hip_fail(e, "route_scatter launch");
   return MOE_OK;
 }
@@ -244,10 +245,34 @@ int moe_expert_forward_decode(const moe_q2_layer* layer, const void* x, int32_t 
   if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "decode takes at most 4 tokens");
   const size_t need = decode_workspace_bytes(T, k, layer->hidden, layer->inter);
   if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
-  const hipError_t e = launch_decode(layer_args(layer), x, x_dtype == MOE_BF16, T, topk_ids, topk_w, k,
-                                     residual, out, out_dtype == MOE_BF16,
-                                     (flags & MOE_FLAG_PRENORM_RMS) ? 1 : 0, workspace,
-                                     static_cast<hipStream_t>(stream));
+  const hipError_t e = launch_decode(layer_args(layer), x, x_dtype == MOE_BF16, T, topk_ids, topk_w,
+                                     nullptr, nullptr, nullptr, k, residual, out,
+                                     out_dtype == MOE_BF16, (flags & MOE_FLAG_PRENORM_RMS) ? 1 : 0,
+                                     workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "decode launch");
+}
+
+int moe_expert_forward_decode_routed(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
+                                     int32_t T, const float* logits, int32_t k, int32_t* topk_ids,
+                                     float* topk_w, const void* residual, void* out,
+                                     int32_t out_dtype, uint32_t flags, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (!logits) return fail(MOE_ERR_INVALID_ARG, "logits is required");
+  if ((topk_ids == nullptr) != (topk_w == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "topk_ids and topk_w: both or neither");
+  if (!aligned(logits, 4) || (topk_ids && (!aligned(topk_ids, 4) || !aligned(topk_w, 4))))
+    return fail(MOE_ERR_INVALID_ARG, "logits, topk_ids and topk_w must be 4-byte aligned");
+  // the routing outputs are optional here, so check the rest with stand-ins
+  int st = check_forward(layer, x, x_dtype, T, reinterpret_cast<const int32_t*>(logits), logits, k,
+                         out, out_dtype, flags, workspace);
+  if (st) return st;
+  if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "decode takes at most 4 tokens");
+  const size_t need = decode_workspace_bytes(T, k, layer->hidden, layer->inter);
+  if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
+  const hipError_t e = launch_decode(layer_args(layer), x, x_dtype == MOE_BF16, T, nullptr, nullptr,
+                                     logits, topk_ids, topk_w, k, residual, out,
+                                     out_dtype == MOE_BF16, (flags & MOE_FLAG_PRENORM_RMS) ? 1 : 0,
+                                     workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, "decode launch");
 }
 

@@ -29,6 +29,7 @@
 //   out = acc / s_t^2 (+ residual).
 #include "launch.h"
 #include "q2_device.h"
+#include "topk_device.h"
 #include "../../include/moe_q2.h"
 
 namespace moeq2 {
@@ -122,13 +123,20 @@ __device__ __forceinline__ void x_raw_to_float(const u32x4 (&r)[2], float (&v)[8
   }
 }
 
-template <int KTW, bool BF16>   // K tiles per wave: ceil(H / 256 / 4); x dtype
+// K tiles per wave: ceil(H / 256 / 4); x dtype; RPER = 0 when topk_ids and
+// topk_w are given, else the per-lane expert bound of the in-kernel top-k of
+// `logits` (every workgroup routes the T tokens itself, waves 0..T-1 one
+// token each; block 0 also writes the routing out when asked).
+template <int KTW, bool BF16, int RPER>
 __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
     LayerArgs L, const void* __restrict__ x, int T, const int32_t* __restrict__ ids,
-    const float* __restrict__ w, int k, int prenorm, uint8_t* __restrict__ ws) {
+    const float* __restrict__ w, const float* __restrict__ logits, int32_t* __restrict__ ids_out,
+    float* __restrict__ w_out, int k, int prenorm, uint8_t* __restrict__ ws) {
   extern __shared__ __align__(16) uint8_t dyn[];
   _Float16* xs = reinterpret_cast<_Float16*>(dyn);              // [T][H]
   __shared__ DecodeSlots S;
+  __shared__ int32_t s_rid[RPER > 0 ? MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK : 1];
+  __shared__ float s_rw[RPER > 0 ? MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK : 1];
   __shared__ float s_stat[kWaves][MOE_MAX_DECODE_TOKENS][2];
   __shared__ float s_mul[MOE_MAX_DECODE_TOKENS];
   __shared__ float s_uns[MOE_MAX_DECODE_TOKENS];
@@ -152,17 +160,40 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
       load_x_raw<BF16>(x, min(static_cast<int>(threadIdx.x) + kThreads * q, nch - 1), xr[q]);
   }
 
-  if (wid == 0) build_slots(ids, w, T, k, L.E, L.shared != nullptr, S);
+  if constexpr (RPER > 0) {
+    if (wid < T) {
+      int my_e;
+      float l;
+      topk_one_token<RPER>(logits + static_cast<size_t>(wid) * L.E, L.E, k, lane, my_e, l);
+      const float wt = topk_weight(l, k, lane);
+      if (lane < k) {
+        s_rid[wid * k + lane] = my_e;
+        s_rw[wid * k + lane] = wt;
+        if (blockIdx.x == 0 && ids_out) {
+          ids_out[wid * k + lane] = my_e;
+          w_out[wid * k + lane] = wt;
+        }
+      }
+    }
+    __syncthreads();
+    if (wid == 0) build_slots(s_rid, s_rw, T, k, L.E, L.shared != nullptr, S);
+  } else {
+    if (wid == 0) build_slots(ids, w, T, k, L.E, L.shared != nullptr, S);
+  }
   __syncthreads();
   const bool active = slot < S.n;
   if (!active && blockIdx.x != 0) return;    // block 0 always writes the header
 
-  // ---- weight loads of this row tile (gate and up), K split over 4 waves
+  // ---- weight loads of this row tile (gate and up), K split over 4 waves.
+  // Issued on every path (an inactive block 0 reads expert 0's tiles and
+  // drops them): the waits on x below then count these loads as still
+  // outstanding instead of draining them first.
   const int KT = H / kTileCols;
   const int64_t mat = static_cast<int64_t>(I) * H * 5 / 16;
   u32x4 cg[KTW], sg[KTW], cu[KTW], su[KTW];
-  if (active) {
-    const uint8_t* gate = expert_base(L, S.expert[slot]) + static_cast<int64_t>(rt) * KT * kTileBytes;
+  {
+    const uint8_t* gate = expert_base(L, active ? S.expert[slot] : 0) +
+                          static_cast<int64_t>(rt) * KT * kTileBytes;
     const uint8_t* up = gate + mat;
 #pragma unroll
     for (int i = 0; i < KTW; ++i) {
@@ -310,16 +341,39 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
   }
 }
 
+struct GateupArgs {
+  const void* x;
+  int T;
+  const int32_t* ids;
+  const float* w;
+  const float* logits;
+  int32_t* ids_out;
+  float* w_out;
+  int k, prenorm;
+  uint8_t* ws;
+};
+
+template <int KTW, bool BF16, int RPER>
+hipError_t launch_gateup3(const LayerArgs& L, int grid, uint32_t lds, hipStream_t s,
+                          const GateupArgs& a) {
+  return launch_kernel(K_DECODE_GATEUP, decode_gateup_kernel<KTW, BF16, RPER>, dim3(grid),
+                       dim3(kThreads), lds, s, L, a.x, a.T, a.ids, a.w, a.logits, a.ids_out,
+                       a.w_out, a.k, a.prenorm, a.ws);
+}
+
 template <int KTW>
-hipError_t launch_gateup(const LayerArgs& L, int grid, size_t lds, hipStream_t s, const void* x,
-                         int x_bf16, int T, const int32_t* ids, const float* w, int k, int prenorm,
-                         uint8_t* ws) {
+hipError_t launch_gateup(const LayerArgs& L, int grid, size_t lds, hipStream_t s, int x_bf16,
+                         const GateupArgs& a) {
   const uint32_t l = static_cast<uint32_t>(lds);
-  if (x_bf16)
-    return launch_kernel(K_DECODE_GATEUP, decode_gateup_kernel<KTW, true>, dim3(grid),
-                         dim3(kThreads), l, s, L, x, T, ids, w, k, prenorm, ws);
-  return launch_kernel(K_DECODE_GATEUP, decode_gateup_kernel<KTW, false>, dim3(grid),
-                       dim3(kThreads), l, s, L, x, T, ids, w, k, prenorm, ws);
+  const int rper = a.logits == nullptr ? 0 : (L.E <= 8 * kWave ? 8 : 16);
+  if (x_bf16) {
+    if (rper == 0) return launch_gateup3<KTW, true, 0>(L, grid, l, s, a);
+    if (rper == 8) return launch_gateup3<KTW, true, 8>(L, grid, l, s, a);
+    return launch_gateup3<KTW, true, 16>(L, grid, l, s, a);
+  }
+  if (rper == 0) return launch_gateup3<KTW, false, 0>(L, grid, l, s, a);
+  if (rper == 8) return launch_gateup3<KTW, false, 8>(L, grid, l, s, a);
+  return launch_gateup3<KTW, false, 16>(L, grid, l, s, a);
 }
 
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(
@@ -340,39 +394,45 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   const int wid = threadIdx.x / kWave;
   const int m = lane & 15, g = lane >> 4;
 
-  if (threadIdx.x < kMaxSlots) s_expert[threadIdx.x] = hdr->expert[threadIdx.x];
-  if (threadIdx.x < kMaxSlots * MOE_MAX_DECODE_TOKENS)
-    (&s_pidx[0][0])[threadIdx.x] = (&hdr->pidx[0][0])[threadIdx.x];
-  if (threadIdx.x == 0) s_n = hdr->n_slots;
+  // h~ of all pairs: its layout does not depend on the header, so these
+  // loads go first (always issued, so that later waits count them exactly)
+  const int hch = (T * k + T) * I / 8;
+  u32x4 hreg[kDownStage];
+#pragma unroll
+  for (int q = 0; q < kDownStage; ++q)
+    hreg[q] = *reinterpret_cast<const u32x4*>(hin + 8 * min(static_cast<int>(threadIdx.x) + kThreads * q, hch - 1));
+
+  {
+    // the three header loads are issued together (clamped, unconditional)
+    const int i = threadIdx.x;
+    const int ev = hdr->expert[min(i, kMaxSlots - 1)];
+    const int pv = (&hdr->pidx[0][0])[min(i, kMaxSlots * MOE_MAX_DECODE_TOKENS - 1)];
+    const int nv = hdr->n_slots;
+    if (i < kMaxSlots) s_expert[i] = ev;
+    if (i < kMaxSlots * MOE_MAX_DECODE_TOKENS) (&s_pidx[0][0])[i] = pv;
+    if (i == 0) s_n = nv;
+  }
   __syncthreads();
   const int n_slots = s_n;
   const int64_t mat = static_cast<int64_t>(I) * H * 5 / 16;
 
-  // h~ of all pairs: loads issued now (L2), stored to LDS below
-  const int hch = (T * k + T) * I / 8;
-  u32x4 hreg[kDownStage];
-  if (stage_lds) {
-#pragma unroll
-    for (int q = 0; q < kDownStage; ++q)
-      hreg[q] = *reinterpret_cast<const u32x4*>(hin + 8 * min(static_cast<int>(threadIdx.x) + kThreads * q, hch - 1));
-  }
-
   // records of this wave: (slot, kt) for slots wid, wid+8, ...
   const int nwork = ((n_slots - wid + kWaves - 1) / kWaves) * KT;
+  // (a wave without work reads expert 0's first record and drops it, so the
+  // first batch is issued on every path)
   auto rec_of = [&](int wi) {
-    wi = min(wi, nwork - 1);
+    wi = max(min(wi, nwork - 1), 0);
     const int slot = wid + kWaves * (wi / KT);
     const int kt = wi % KT;
-    return expert_base(L, s_expert[slot]) + 2 * mat + (static_cast<int64_t>(rt) * KT + kt) * kTileBytes;
+    const int e = slot < n_slots ? s_expert[slot] : 0;
+    return expert_base(L, e) + 2 * mat + (static_cast<int64_t>(rt) * KT + kt) * kTileBytes;
   };
   u32x4 c[kDownBatch], sc[kDownBatch];
-  if (nwork > 0) {
 #pragma unroll
-    for (int b = 0; b < kDownBatch; ++b) {
-      const uint8_t* rec = rec_of(b);
-      c[b] = load_codes(rec, lane);
-      sc[b] = load_scales(rec, lane);
-    }
+  for (int b = 0; b < kDownBatch; ++b) {
+    const uint8_t* rec = rec_of(b);
+    c[b] = load_codes(rec, lane);
+    sc[b] = load_scales(rec, lane);
   }
   if (stage_lds) {
 #pragma unroll
@@ -453,7 +513,8 @@ size_t decode_workspace_bytes(int T, int k, int H, int I) {
 }
 
 hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
-                         const int32_t* ids, const float* w, int k, const void* residual,
+                         const int32_t* ids, const float* w, const float* logits,
+                         int32_t* ids_out, float* w_out, int k, const void* residual,
                          void* out, int out_bf16, int prenorm, void* ws, hipStream_t s) {
   const int slots_max = T * k + (L.shared ? 1 : 0);
   const int RP = L.I / (2 * kTileRows);
@@ -461,17 +522,17 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
   const int ktw = (L.H / kTileCols + 3) / 4;
   hipError_t e;
   {
-    uint8_t* w8 = static_cast<uint8_t*>(ws);
+    const GateupArgs a{x, T, ids, w, logits, ids_out, w_out, k, prenorm, static_cast<uint8_t*>(ws)};
     const int grid = slots_max * RP;
     switch (ktw) {
-      case 1: e = launch_gateup<1>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
-      case 2: e = launch_gateup<2>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
-      case 3: e = launch_gateup<3>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
-      case 4: e = launch_gateup<4>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
-      case 5: e = launch_gateup<5>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
-      case 6: e = launch_gateup<6>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
-      case 7: e = launch_gateup<7>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
-      default: e = launch_gateup<8>(L, grid, lds1, s, x, x_bf16, T, ids, w, k, prenorm, w8); break;
+      case 1: e = launch_gateup<1>(L, grid, lds1, s, x_bf16, a); break;
+      case 2: e = launch_gateup<2>(L, grid, lds1, s, x_bf16, a); break;
+      case 3: e = launch_gateup<3>(L, grid, lds1, s, x_bf16, a); break;
+      case 4: e = launch_gateup<4>(L, grid, lds1, s, x_bf16, a); break;
+      case 5: e = launch_gateup<5>(L, grid, lds1, s, x_bf16, a); break;
+      case 6: e = launch_gateup<6>(L, grid, lds1, s, x_bf16, a); break;
+      case 7: e = launch_gateup<7>(L, grid, lds1, s, x_bf16, a); break;
+      default: e = launch_gateup<8>(L, grid, lds1, s, x_bf16, a); break;
     }
   }
   if (e != hipSuccess) return e;

@@ -48,17 +48,19 @@ hipError_t launch_kernel(int kernel_id, F kernel, dim3 grid, dim3 block, uint32_
 
 // ---------------------------------------------------------------- routing --
 constexpr int kRouteMaxChunkTokens = 256;
-// Tokens per routing workgroup: 64 up to 4096 tokens, 256 above (fewer
-// chunk counts to scan).
-inline __host__ __device__ int route_chunk_tokens(int T) { return T <= 4096 ? 64 : 256; }
-
+// Tokens per routing workgroup (chunk): small chunks give more workgroups
+// for the top-k, large ones fewer per-chunk counts to scan.
+inline __host__ __device__ int route_chunk_tokens(int T) {
+  return T <= 4096 ? 16 : (T <= 65536 ? 64 : 256);
+}
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              int32_t* rank, int32_t* local_counts, hipStream_t s);
-hipError_t launch_route_scan(const int32_t* local_counts, int32_t* base, int E, int n_chunks,
-                             int total_pairs, int32_t* counts, int32_t* offsets, hipStream_t s);
-hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const int32_t* base,
-                                int T, int k, int n_chunks, int32_t* sorted_pairs,
-                                int32_t* pair_pos, hipStream_t s);
+hipError_t launch_route_expert_scan(const int32_t* local_counts, int32_t* ebase, int E, int n_chunks,
+                                    int32_t* counts, hipStream_t s);
+hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const int32_t* ebase,
+                                const int32_t* counts, int E, int T, int k, int n_chunks,
+                                int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+                                hipStream_t s);
 
 // ----------------------------------------------------------------- decode --
 struct LayerArgs {
@@ -68,8 +70,12 @@ struct LayerArgs {
   int E, H, I;
 };
 
+// With `logits` non-null the routing (ids, w) is taken inside the gate/up
+// kernel (ids_out / w_out, if non-null, receive it); otherwise ids and w are
+// read.
 hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
-                         const int32_t* ids, const float* w, int k, const void* residual,
+                         const int32_t* ids, const float* w, const float* logits,
+                         int32_t* ids_out, float* w_out, int k, const void* residual,
                          void* out, int out_bf16, int prenorm, void* ws, hipStream_t s);
 size_t decode_workspace_bytes(int T, int k, int H, int I);
 

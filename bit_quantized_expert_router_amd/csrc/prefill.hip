@@ -26,9 +26,9 @@
 //            rows (LDS), B = down tiles; y~[row] = W_down h~ (fp16).
 //   combine  token t: out = (sum_j y~[pair_pos[t,j]] + y~[shared row]) / s_t^2
 //            (+ residual), j ascending: fixed order, no atomics.
-// Workgroup ids are remapped so that consecutive logical ids (the row blocks
-// of one work item, which read the same A rows) run on the same XCD and
-// share its L2.
+// Workgroup ids are remapped so that every XCD gets an equal share of the
+// real work and the row blocks of one work item (which read the same A rows)
+// run on the same XCD and share its L2.
 #include "launch.h"
 #include "q2_device.h"
 #include "../../include/moe_q2.h"
@@ -74,9 +74,17 @@ __host__ __device__ inline PrefillWs carve(void* base, int T, int E, int k, int 
   return w;
 }
 
-__device__ __forceinline__ int xcd_logical(int bid, int nblocks) {
-  const int per = nblocks / 8;
-  return (bid % 8) * per + bid / 8;
+// Work unit of a block, or -1.  Blocks are dealt to the 8 XCDs round-robin
+// (block b runs on XCD b % 8); the n real units (known only on the device)
+// are split into 8 contiguous ranges, one per XCD, so every XCD gets the
+// same share and consecutive units (the row blocks of one work item, which
+// read the same activation rows) share an XCD's L2.  The grid is sized for
+// the largest possible n; blocks beyond the work return at once.
+__device__ __forceinline__ int xcd_unit(int bid, int n) {
+  const int per = (n + 7) / 8;
+  const int i = bid / 8;
+  const int u = (bid % 8) * per + i;
+  return (i < per && u < n) ? u : -1;
 }
 
 __device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e) {
@@ -310,10 +318,10 @@ __global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, P
   __shared__ float s_w[kGroupRows];
   __shared__ float s_u[kGroupRows];
   const int RB = L.I / kGateupRowsPerBlock;
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int item = logical / RB;
-  const int rb = logical % RB;
-  if (item >= ws.hdr[0]) return;
+  const int unit = xcd_unit(blockIdx.x, ws.hdr[0] * RB);
+  if (unit < 0) return;
+  const int item = unit / RB;
+  const int rb = unit % RB;
   const int4 it = ws.items[item];
   const int e = it.x, row0 = it.y, nrows = it.z;
   if (threadIdx.x < nrows) {
@@ -421,10 +429,10 @@ __global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, Pre
   __shared__ __align__(16) _Float16 s_a[2][kATileHalves];
   __shared__ int64_t s_off[kGroupRows];
   const int RB = L.H / kDownRowsPerBlock;
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int item = logical / RB;
-  const int rb = logical % RB;
-  if (item >= ws.hdr[0]) return;
+  const int unit = xcd_unit(blockIdx.x, ws.hdr[0] * RB);
+  if (unit < 0) return;
+  const int item = unit / RB;
+  const int rb = unit % RB;
   const int4 it = ws.items[item];
   const int e = it.x, row0 = it.y, nrows = it.z;
   if (threadIdx.x < kGroupRows) s_off[threadIdx.x] = static_cast<int64_t>(row0 + threadIdx.x) * L.I;

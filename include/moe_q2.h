@@ -17,6 +17,8 @@
  *   moe_expert_forward_decode  1..4 tokens (a decode step or a verify window)
  *   moe_expert_forward_prefill any number of tokens (prompt chunks of 1024
  *                              or 32768 tokens), grouped by expert
+ * and moe_expert_forward_decode_routed does the first two for decode in one
+ * call.
  *
  * Conventions for every entry point
  *   - Pointers marked [device] are device addresses (hipMalloc'd memory or
@@ -145,6 +147,26 @@ int moe_expert_forward_decode(const moe_q2_layer* layer, const void* x, int32_t 
                               int32_t k, const void* residual, void* out, int32_t out_dtype,
                               uint32_t flags, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * Router and decode-time expert layer in one call, for T = 1..4 tokens: the
+ * top-k of `logits` is taken inside the expert kernels (every workgroup
+ * selects the experts of the T tokens itself), so no separate routing
+ * kernel runs before the weights can be fetched.  Same routing as
+ * moe_route_topk and same `out` as moe_expert_forward_decode on that routing.
+ *   logits    [device] float32 [T, E] router logits (E = layer->num_experts).
+ *   topk_ids, topk_w  [device] [T, k] outputs, or both NULL: receive the
+ *             routing (identical to moe_route_topk's).
+ *   other arguments as for moe_expert_forward_decode; the workspace size is
+ *             moe_workspace_bytes(MOE_OP_DECODE, ...).
+ * Errors: as for moe_expert_forward_decode, plus INVALID_ARG for a NULL
+ * `logits` or only one of topk_ids / topk_w.
+ */
+int moe_expert_forward_decode_routed(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
+                                     int32_t T, const float* logits, int32_t k,
+                                     int32_t* topk_ids, float* topk_w, const void* residual,
+                                     void* out, int32_t out_dtype, uint32_t flags,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Prefill-time expert layer for a chunk of T tokens, grouped by expert from

@@ -90,6 +90,13 @@ def forward(lib, which, **kw):
              ids=FAKE, w=FAKE, k=4, res=None, out=FAKE + 4096, od=0, flags=0, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     L = _Layer(a["experts"], a["shared"], a["stride"], a["E"], a["H"], a["I"])
+    if which == "routed":
+        return lib.moe_expert_forward_decode_routed(C.byref(L), C.c_void_p(a["x"]), a["xd"], a["T"],
+                                                    C.c_void_p(a.get("logits", FAKE)), a["k"],
+                                                    C.c_void_p(a["ids"]), C.c_void_p(a["w"]),
+                                                    C.c_void_p(a["res"]), C.c_void_p(a["out"]),
+                                                    a["od"], a["flags"], C.c_void_p(a["ws"]),
+                                                    a["wsb"], None)
     if which == "decode":
         return lib.moe_expert_forward_decode(C.byref(L), C.c_void_p(a["x"]), a["xd"], a["T"],
                                              C.c_void_p(a["ids"]), C.c_void_p(a["w"]), a["k"],
@@ -103,7 +110,7 @@ def forward(lib, which, **kw):
                                           a["flags"], C.c_void_p(a["ws"]), a["wsb"], None)
 
 
-@pytest.mark.parametrize("which", ["decode", "prefill"])
+@pytest.mark.parametrize("which", ["decode", "routed", "prefill"])
 def test_forward_validation(lib, which):
     assert forward(lib, which, experts=None) == -1
     assert forward(lib, which, x=None) == -1
@@ -123,9 +130,14 @@ def test_forward_validation(lib, which):
     assert forward(lib, which, ws=None) == -3
     assert forward(lib, which, wsb=100) == -3
     assert forward(lib, which, ws=FAKE + 8) == -1
-    if which == "decode":
+    if which in ("decode", "routed"):
         assert forward(lib, which, T=5) == -2
-    else:
+    if which == "routed":
+        assert forward(lib, which, logits=None) == -1
+        assert forward(lib, which, ids=None) == -1            # only one routing output
+        assert forward(lib, which, logits=FAKE + 2) == -1     # unaligned
+        assert forward(lib, which, ids=None, w=None, wsb=100) == -3   # outputs are optional
+    elif which == "prefill":
         assert forward(lib, which, counts=None) == -1
         assert forward(lib, which, T=(1 << 22) + 1) == -2
 

@@ -86,6 +86,8 @@ ROUTE_CASES = [
     (1, 64, 4, "router"), (1, 512, 10, "router"), (3, 512, 10, "zipf"), (1024, 512, 10, "biased"),
     (37, 8, 3, "ties"), (300, 1024, 16, "normal"), (5, 16, 16, "ties"), (130, 64, 1, "normal"),
     (65, 512, 10, "const"), (32768, 512, 10, "zipf"),
+    # chunk sizes 32 / 64 / 256 tokens, with and without the fused scan + scatter
+    (4096, 512, 10, "biased"), (5000, 64, 4, "normal"), (70000, 64, 4, "normal"),
 ]
 
 
@@ -199,6 +201,88 @@ def test_decode_deterministic(B, layer_full):
     a = run_decode(B, L, dev_x(xd, "bf16"), r)
     b = run_decode(B, L, dev_x(xd, "bf16"), r)
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------- routed decode call --
+ROUTED_CASES = [
+    # (layer: seed, E, H, I), T, k, logits kind, x dtype
+    ((0, 64, 1024, 256), 1, 4, "router", "f32"),
+    ((1, 512, 3072, 768), 1, 10, "router", "bf16"),
+    ((1, 512, 3072, 768), 2, 10, "zipf", "bf16"),
+    ((1, 512, 3072, 768), 3, 10, "zipf", "bf16"),
+    ((1, 512, 3072, 768), 4, 10, "ties", "bf16"),
+    ((7, 1024, 512, 256), 4, 16, "normal", "f32"),     # top-k with 16 experts per lane
+    ((8, 300, 512, 512), 2, 7, "normal", "bf16"),      # E not a multiple of 64
+]
+
+
+@pytest.fixture(scope="module")
+def routed_layers(B, layer_small, layer_full):
+    cache = {(0, 64, 1024, 256): layer_small, (1, 512, 3072, 768): layer_full}
+
+    def get(key):
+        if key not in cache:
+            cache[key] = Layer(B, *key)
+        return cache[key]
+    return get
+
+
+@pytest.mark.parametrize("lkey,T,k,kind,xdt", ROUTED_CASES)
+def test_decode_routed(B, routed_layers, lkey, T, k, kind, xdt):
+    """moe_expert_forward_decode_routed: routing bit-exact against the oracle
+    and identical to moe_route_topk's; output within tolerance of the oracle
+    and bitwise equal to the two-call path on the same routing."""
+    L = routed_layers(lkey)
+    E, H = L.E, L.H
+    print(f"routed decode E={E} H={H} T={T} k={k} {kind}", flush=True)
+    rng = synth.rng_for(40, T, E)
+    xd, xv = synth.activations(rng, T, H, xdt)
+    if kind == "router":
+        lg = synth.router_logits(rng, xv, E)
+    elif kind == "zipf":
+        lg = synth.zipf_logits(rng, T, E)
+    elif kind == "ties":
+        lg = synth.tie_logits(rng, T, E)
+    else:
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w = O.route_topk(lg, k)
+    xt = dev_x(xd, xdt)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    rid = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    rw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = B.workspace(B.MOE_OP_DECODE, T, E, k, H, L.I)
+    B.moe_expert_forward_decode_routed(L.dev, xt, dev(lg), k, out, rid, rw, None, 0, ws)
+    torch.cuda.synchronize()
+    assert_route_exact(ids, w, {"topk_ids": rid, "topk_w": rw}, E, False)
+    r = B.route(dev(lg), k)
+    assert torch.equal(r["topk_ids"], rid) and torch.equal(r["topk_w"], rw)
+    check_out(to_np(out), O.moe_layer(xv, ids, w, L.ref), f"routed decode T={T} E={E}")
+    two = run_decode(B, L, xt, r)
+    assert torch.equal(out, two)
+    # routing outputs are optional
+    out2 = torch.empty_like(out)
+    B.moe_expert_forward_decode_routed(L.dev, xt, dev(lg), k, out2, None, None, None, 0, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+def test_decode_routed_prenorm_residual_bf16(B, layer_full):
+    L = layer_full
+    rng = synth.rng_for(41, 0, 0)
+    T = 2
+    xd, xv = synth.activations(rng, T, 3072, "bf16")
+    lg = synth.zipf_logits(rng, T, 512)
+    ids, w = O.route_topk(lg, 10)
+    res = (rng.standard_normal((T, 3072)) * 0.5).astype(np.float32)
+    resd = dev(res).to(torch.bfloat16)
+    out = torch.empty((T, 3072), dtype=torch.bfloat16, device="cuda")
+    ws = B.workspace(B.MOE_OP_DECODE, T, 512, 10, 3072, 768)
+    B.moe_expert_forward_decode_routed(L.dev, dev_x(xd, "bf16"), dev(lg), 10, out, None, None, resd,
+                                       B.MOE_FLAG_PRENORM_RMS, ws)
+    torch.cuda.synchronize()
+    resb = synth.bf16_to_f32(synth.bf16_bits(res)).astype(np.float64)
+    ref = O.moe_layer(xv, ids, w, L.ref, prenorm=True, residual=resb)
+    check_out(to_np(out), ref, "routed decode prenorm+residual bf16")
 
 
 # ------------------------------------------------------------------ prefill --
