@@ -185,7 +185,7 @@ int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t
   if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E must be <= 1024");
   if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k must be <= 16");
   if (k > E) return fail(MOE_ERR_INVALID_ARG, "k must be <= E");
-  if (T > MOE_MAX_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "T must be <= 2^22");
+  if (T > MOE_MAX_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "T must be <= 2^17");
   const int nhist = (counts != nullptr) + (offsets != nullptr) + (sorted_pairs != nullptr) + (pair_pos != nullptr);
   if (nhist != 0 && nhist != 4)
     return fail(MOE_ERR_INVALID_ARG, "counts, offsets, sorted_pairs and pair_pos: all or none");
@@ -286,7 +286,7 @@ int moe_expert_forward_prefill(const moe_q2_layer* layer, const void* x, int32_t
   if (st) return st;
   if (!counts || !offsets || !sorted_pairs || !pair_pos)
     return fail(MOE_ERR_INVALID_ARG, "counts, offsets, sorted_pairs and pair_pos are required");
-  if (T > MOE_MAX_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "T must be <= 2^22");
+  if (T > MOE_MAX_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "T must be <= 2^17");
   const size_t need = prefill_workspace_bytes(T, layer->num_experts, k, layer->hidden, layer->inter);
   if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
   const hipError_t e = launch_prefill(layer_args(layer), x, x_dtype == MOE_BF16, T, topk_ids, topk_w, k,

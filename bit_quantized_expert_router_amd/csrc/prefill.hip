@@ -17,8 +17,8 @@
 //            gate and of up each): A = the item's gathered x rows (fp16,
 //            staged in LDS, double buffered per 256-column K tile), B = the
 //            expert's gate and up tiles dequantized in registers (each weight
-//            is dequantized once per item and used by every M tile; two
-//            register sets alternate, so the next K tile's weights are in
+//            is dequantized once per item and used by every M tile; a ring
+//            of four register sets keeps the next three K tiles' weights in
 //            flight while one is multiplied),
 //            v_mfma_f32_16x16x32_f16, SwiGLU epilogue:
 //            h~[row] = w * silu(g) * u * s_t^2  (fp16, sorted-row order).
@@ -29,6 +29,9 @@
 // Workgroup ids are remapped so that every XCD gets an equal share of the
 // real work and the row blocks of one work item (which read the same A rows)
 // run on the same XCD and share its L2.
+#include <type_traits>
+#include <utility>
+
 #include "launch.h"
 #include "q2_device.h"
 #include "../../include/moe_q2.h"
@@ -37,9 +40,13 @@ namespace moeq2 {
 
 namespace {
 
-constexpr int kThreads = 512;               // 8 waves
-constexpr int kGateupRowsPerBlock = 128;    // 8 waves x 16 rows of I (gate and up)
-constexpr int kDownRowsPerBlock = 256;      // 8 waves x 2 x 16 rows of H
+constexpr int kGemmWaves = 8;               // waves per GEMM workgroup
+constexpr int kThreads = 64 * kGemmWaves;
+constexpr int kDownRTW = kGemmWaves == 16 ? 1 : 2;          // 16-row tiles of H per wave
+constexpr int kGateupRowsPerBlock = 16 * kGemmWaves;        // 16 rows of I (gate and up) per wave
+constexpr int kDownRowsPerBlock = 16 * kDownRTW * kGemmWaves;
+constexpr int kGateupRing = 2;              // K tiles of weights in flight per wave
+constexpr int kDownRing = 2;
 
 struct PrefillWs {
   int32_t* hdr;        // [0] = number of work items
@@ -193,29 +200,50 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
 // slots at ((4 j + mt) * 64 + lane) * 16 bytes.  Wave w loads block j = w
 // (8 waves = 8 blocks of a 256-column K tile), one 16-byte global load per
 // M tile, and stores it to its own slot, so the stores and the fragment reads
-// are both conflict-free and need no padding.  Rows are given as element
-// offsets into one global array (loads stay global, not flat); rows at or
-// beyond nrows repeat the last row (their outputs are never written).
+// are both conflict-free and need no padding.  The rows are read through a
+// buffer resource over the activation array: each lane's byte offsets (one
+// per M tile) are fixed for the whole K loop and the K tile is a scalar
+// offset; rows at or beyond nrows repeat the last row (their outputs are
+// never written).
 constexpr int kFragHalves = 64 * 8;                 // one fragment
 constexpr int kATileHalves = 8 * 4 * kFragHalves;   // 8 blocks x 4 M tiles = 32 KB
 
+// With 16 waves, wave w loads block j = w % 8 and the M tiles w / 8,
+// w / 8 + 2, ... (clamped to the last one: a wave with nothing left repeats
+// a fragment, writing the same bytes to the same place).
 template <int NMT>
 struct ATile {
-  u32x4 r[NMT];
-  __device__ __forceinline__ void load(const _Float16* __restrict__ base, const int64_t* rowoff,
-                                       int nrows, int kt) {
-    const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
-    const int m = lane & 15, g = lane >> 4;
+  static constexpr int NR = kGemmWaves == 16 ? (NMT + 1) / 2 : NMT;   // fragments per wave
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t off[NR];
+  int slot[NR];      // fragment index 4 j + mt
+  u32x4 r[2][NR];    // two register sets: a tile is loaded two K steps before it is stored
+  // row_byte(i): byte offset of item row i in the resource
+  template <typename RowByte>
+  __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t rsrc, RowByte row_byte, int nrows) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int j = w & 7, m = lane & 15, g = lane >> 4;
+    rs = rsrc;
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-      r[mt] = *reinterpret_cast<const u32x4*>(base + rowoff[min(mt * 16 + m, nrows - 1)] +
-                                              kt * kTileCols + 32 * j + 8 * g);
+    for (int i = 0; i < NR; ++i) {
+      const int mt = kGemmWaves == 16 ? min((w >> 3) + 2 * i, NMT - 1) : i;
+      slot[i] = 4 * j + mt;
+      off[i] = row_byte(min(mt * 16 + m, nrows - 1)) + 2u * static_cast<uint32_t>(32 * j + 8 * g);
+    }
   }
-  __device__ __forceinline__ void store(_Float16* buf) const {
-    const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+  template <int SET>
+  __device__ __forceinline__ void load(int kt) {
+    const uint32_t k0 = static_cast<uint32_t>(kt) * (2 * kTileCols);
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-      *reinterpret_cast<u32x4*>(buf + ((4 * j + mt) * 64 + lane) * 8) = r[mt];
+    for (int i = 0; i < NR; ++i)
+      r[SET][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], k0, 0);
+  }
+  template <int SET>
+  __device__ __forceinline__ void store(_Float16* buf) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      *reinterpret_cast<u32x4*>(buf + (slot[i] * 64 + lane) * 8) = r[SET][i];
   }
 };
 
@@ -240,60 +268,124 @@ __device__ __forceinline__ void gateup_ktile(const u32x4 (&b)[4], const _Float16
   }
 }
 
+// The K loop shared by both GEMMs.  Tile kt's weights live in register set
+// kt % RING, so while one tile is multiplied the next RING - 1 tiles' weights
+// are in flight, without register copies (which would force early waits).
+// Activation tiles go global -> registers -> LDS (double buffered): tile
+// kt + 2 is loaded during step kt (register set kt % 2) and published into
+// LDS at the end of step kt + 1, so each load has two steps to arrive.
+// Each step: load activation tile kt + 2, multiply tile kt, refill the
+// weight set RING tiles ahead (only while such a tile exists), publish
+// activation tile kt + 1, barrier.  Full groups of RING steps run in a loop;
+// the last one or two groups are unrolled with uniform conditions, so no
+// weight load past the last tile is issued.  The caller has published tile 0
+// into s_a[0] and loaded tile 1 into activation register set 1.
+template <int RING, typename LoadB, typename ATileT, typename Mul>
+__device__ __forceinline__ void k_loop(int KT, u32x4 (&b)[RING][4], LoadB load_b, ATileT& A,
+                                       _Float16 (*s_a)[kATileHalves], Mul mul) {
+  static_assert(RING % 2 == 0, "the activation double buffer alternates every step");
+  auto step = [&](auto par, u32x4 (&bs)[4], int kt, bool refill) {
+    constexpr int P = decltype(par)::value;          // kt % 2
+    A.template load<P>(min(kt + 2, KT - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    mul(bs, s_a[P]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) load_b(bs, kt + RING);
+    A.template store<P ^ 1>(s_a[P ^ 1]);
+    __syncthreads();
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  int kt = 0;
+  for (; kt + 2 * RING <= KT; kt += RING) {
+#pragma unroll
+    for (int u = 0; u < RING; u += 2) {
+      step(P0{}, b[u], kt + u, true);
+      step(P1{}, b[u + 1], kt + u + 1, true);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < RING; u += 2) {
+    if (kt + u < KT) step(P0{}, b[u], kt + u, kt + u + RING < KT);
+    if (kt + u + 1 < KT) step(P1{}, b[u + 1], kt + u + 1, kt + u + 1 + RING < KT);
+  }
+#pragma unroll
+  for (int u = 0; u < RING - 1; u += 2) {
+    if (kt + RING + u < KT) step(P0{}, b[u], kt + RING + u, false);
+    if (u + 1 < RING - 1 && kt + RING + u + 1 < KT) step(P1{}, b[u + 1], kt + RING + u + 1, false);
+  }
+}
+
+// The same K loop for a K tile count fixed at compile time, fully unrolled:
+// every wait the compiler inserts then counts exactly the loads issued since
+// the one it waits for (a runtime loop makes it merge the loop-entry and
+// back-edge states conservatively, which drains the weight prefetch once per
+// iteration).
+template <int KTC, int RING, typename LoadB, typename ATileT, typename Mul, int... KS>
+__device__ __forceinline__ void k_loop_fixed(u32x4 (&b)[RING][4], LoadB load_b, ATileT& A,
+                                             _Float16 (*s_a)[kATileHalves], Mul mul,
+                                             std::integer_sequence<int, KS...>) {
+  static_assert(RING % 2 == 0, "the activation double buffer alternates every step");
+  auto step = [&](auto ktc) {
+    constexpr int kt = decltype(ktc)::value;
+    constexpr int P = kt & 1;
+    if constexpr (kt + 2 < KTC) A.template load<P>(kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(b[kt % RING], s_a[P]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kt + RING < KTC) load_b(b[kt % RING], kt + RING);
+    if constexpr (kt + 1 < KTC) {
+      A.template store<P ^ 1>(s_a[P ^ 1]);
+      __syncthreads();
+    }
+  };
+  (step(std::integral_constant<int, KS>{}), ...);
+}
+
 // ------------------------------------------------------------------ gate/up --
-template <int NMT>
-__device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs& ws, int e, int row0,
-                                            int nrows, int rt, _Float16 (*s_a)[kATileHalves],
-                                            const int64_t* s_off, const float* s_w, const float* s_u) {
+template <int NMT, int RING, int KTC>
+__device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs& ws, int T, int e,
+                                            int row0, int nrows, int rt,
+                                            _Float16 (*s_a)[kATileHalves], const uint32_t* s_off,
+                                            const float* s_w, const float* s_u) {
   const int H = L.H, I = L.I;
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
   const int KT = H / kTileCols;
-  const int64_t mat = static_cast<int64_t>(I) * H * 5 / 16;
-  const uint8_t* gate = expert_base(L, e) + static_cast<int64_t>(rt) * KT * kTileBytes;
-  const uint8_t* up = gate + mat;
+  const uint32_t mat = static_cast<uint32_t>(
+      __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(I) * H * 5 / 16)));
+  const __amdgpu_buffer_rsrc_t rs = expert_rsrc(expert_base(L, e), 3 * mat);
+  const uint32_t gate = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(rt)) * KT * kTileBytes;
   auto load_b = [&](u32x4 (&b)[4], int kt) {
-    kt = min(kt, KT - 1);
-    b[0] = load_codes(gate + kt * kTileBytes, lane);
-    b[1] = load_scales(gate + kt * kTileBytes, lane);
-    b[2] = load_codes(up + kt * kTileBytes, lane);
-    b[3] = load_scales(up + kt * kTileBytes, lane);
+    const uint32_t o = gate + static_cast<uint32_t>(min(kt, KT - 1)) * kTileBytes;
+    b[0] = load_codes(rs, o, lane);
+    b[1] = load_scales(rs, o, lane);
+    b[2] = load_codes(rs, o + mat, lane);
+    b[3] = load_scales(rs, o + mat, lane);
   };
-  // two fixed register sets: while one K tile is multiplied, the next one's
-  // weights are in flight (no register copies, so no early waits)
-  u32x4 bA[4], bB[4];
-  load_b(bA, 0);
-  load_b(bB, 1);
+  u32x4 b[RING][4];
+#pragma unroll
+  for (int u = 0; u < RING; ++u) load_b(b[u], u);   // clamped: no tile past the last is read
   ATile<NMT> A;
-  A.load(ws.x16, s_off, nrows, 0);
-  A.store(s_a[0]);
+  A.init(expert_rsrc(reinterpret_cast<const uint8_t*>(ws.x16),
+                     static_cast<uint32_t>(T) * static_cast<uint32_t>(H) * 2u),
+         [&](int i) { return s_off[i]; }, nrows);
+  A.template load<0>(0);
+  A.template load<1>(min(1, KT - 1));
+  A.template store<0>(s_a[0]);
   __syncthreads();
 
   f32x4 acc_g[4], acc_u[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) { acc_g[i] = f32x4{0.f, 0.f, 0.f, 0.f}; acc_u[i] = acc_g[i]; }
 
-  // K tiles in pairs, branch-free: loads past the last tile are clamped to
-  // it (cache hits) so every iteration has the same shape.
-  const int npairs = KT / 2;
-  for (int p = 0; p < npairs; ++p) {
-    const int kt = 2 * p;
-    A.load(ws.x16, s_off, nrows, kt + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    gateup_ktile<NMT>(bA, s_a[0], lane, acc_g, acc_u);
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(bA, kt + 2);
-    A.store(s_a[1]);
-    __syncthreads();
-    A.load(ws.x16, s_off, nrows, min(kt + 2, KT - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    gateup_ktile<NMT>(bB, s_a[1], lane, acc_g, acc_u);
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(bB, kt + 3);
-    A.store(s_a[0]);
-    __syncthreads();
-  }
-  if (KT & 1) gateup_ktile<NMT>(bA, s_a[0], lane, acc_g, acc_u);
+  auto mul = [&](const u32x4 (&bs)[4], const _Float16* abuf) {
+    gateup_ktile<NMT>(bs, abuf, lane, acc_g, acc_u);
+  };
+  if constexpr (KTC > 0)
+    k_loop_fixed<KTC, RING>(b, load_b, A, s_a, mul, std::make_integer_sequence<int, KTC>{});
+  else
+    k_loop<RING>(KT, b, load_b, A, s_a, mul);
 
   const int col = rt * 16 + m;
 #pragma unroll
@@ -312,9 +404,12 @@ __device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs&
   }
 }
 
-__global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, PrefillWs ws) {
+// KTC: the number of 256-column K tiles (H / 256) when fixed at compile
+// time, 0 for the runtime loop.
+template <int KTC>
+__global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, PrefillWs ws, int T) {
   __shared__ __align__(16) _Float16 s_a[2][kATileHalves];
-  __shared__ int64_t s_off[kGroupRows];
+  __shared__ uint32_t s_off[kGroupRows];
   __shared__ float s_w[kGroupRows];
   __shared__ float s_u[kGroupRows];
   const int RB = L.I / kGateupRowsPerBlock;
@@ -326,17 +421,17 @@ __global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, P
   const int e = it.x, row0 = it.y, nrows = it.z;
   if (threadIdx.x < nrows) {
     const int t = ws.row_tok[row0 + threadIdx.x];
-    s_off[threadIdx.x] = static_cast<int64_t>(t) * L.H;
+    s_off[threadIdx.x] = static_cast<uint32_t>(t) * static_cast<uint32_t>(L.H) * 2u;   // bytes
     s_w[threadIdx.x] = ws.row_w[row0 + threadIdx.x];
     s_u[threadIdx.x] = ws.unscale[t];
   }
   __syncthreads();
-  const int rt = rb * 8 + static_cast<int>(threadIdx.x >> 6);
+  const int rt = rb * kGemmWaves + static_cast<int>(threadIdx.x >> 6);
   switch ((nrows + 15) / 16) {
-    case 1: gateup_body<1>(L, ws, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
-    case 2: gateup_body<2>(L, ws, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
-    case 3: gateup_body<3>(L, ws, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
-    default: gateup_body<4>(L, ws, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+    case 1: gateup_body<1, kGateupRing, KTC>(L, ws, T, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+    case 2: gateup_body<2, kGateupRing, KTC>(L, ws, T, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+    case 3: gateup_body<3, kGateupRing, KTC>(L, ws, T, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+    default: gateup_body<4, kGateupRing, KTC>(L, ws, T, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
   }
 }
 
@@ -350,7 +445,7 @@ __device__ __forceinline__ void down_ktile(const u32x4 (&b)[4], const _Float16* 
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) a[mt] = a_frag(abuf, j, mt, lane);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kDownRTW; ++q) {
       const f16x8 bq = tile_block_weights(b[2 * q], b[2 * q + 1], j);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) acc[q][mt] = mfma16(a[mt], bq, acc[q][mt]);
@@ -358,31 +453,36 @@ __device__ __forceinline__ void down_ktile(const u32x4 (&b)[4], const _Float16* 
   }
 }
 
-template <int NMT>
+template <int NMT, int RING, int KTC>
 __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& ws, int e, int row0,
-                                          int nrows, int rt0, _Float16 (*s_a)[kATileHalves],
-                                          const int64_t* s_off) {
+                                          int nrows, int rt0, _Float16 (*s_a)[kATileHalves]) {
   const int H = L.H, I = L.I;
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
   const int KT = I / kTileCols;
-  const int64_t mat = static_cast<int64_t>(I) * H * 5 / 16;
-  const uint8_t* down = expert_base(L, e) + 2 * mat + static_cast<int64_t>(rt0) * KT * kTileBytes;
+  const uint32_t mat = static_cast<uint32_t>(
+      __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(I) * H * 5 / 16)));
+  const __amdgpu_buffer_rsrc_t rs = expert_rsrc(expert_base(L, e), 3 * mat);
+  const uint32_t down = 2 * mat + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(rt0)) * KT * kTileBytes;
   auto load_b = [&](u32x4 (&b)[4], int kt) {
-    kt = min(kt, KT - 1);
+    const uint32_t o = down + static_cast<uint32_t>(min(kt, KT - 1)) * kTileBytes;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint8_t* rec = down + (static_cast<int64_t>(q) * KT + kt) * kTileBytes;
-      b[2 * q] = load_codes(rec, lane);
-      b[2 * q + 1] = load_scales(rec, lane);
+    for (int q = 0; q < kDownRTW; ++q) {
+      b[2 * q] = load_codes(rs, o + q * KT * kTileBytes, lane);
+      b[2 * q + 1] = load_scales(rs, o + q * KT * kTileBytes, lane);
     }
   };
-  u32x4 bA[4], bB[4];
-  load_b(bA, 0);
-  load_b(bB, 1);
-  ATile<NMT> A;
-  A.load(ws.h, s_off, nrows, 0);
-  A.store(s_a[0]);
+  u32x4 b[RING][4];
+#pragma unroll
+  for (int u = 0; u < RING; ++u) load_b(b[u], u);
+  ATile<NMT> A;   // the item's h rows are consecutive: a resource over just them
+  const uint32_t row_bytes = static_cast<uint32_t>(I) * 2u;
+  A.init(expert_rsrc(reinterpret_cast<const uint8_t*>(ws.h + static_cast<size_t>(row0) * I),
+                     static_cast<uint32_t>(nrows) * row_bytes),
+         [&](int i) { return static_cast<uint32_t>(i) * row_bytes; }, nrows);
+  A.template load<0>(0);
+  A.template load<1>(min(1, KT - 1));
+  A.template store<0>(s_a[0]);
   __syncthreads();
 
   f32x4 acc[2][4];
@@ -391,28 +491,16 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int npairs = KT / 2;
-  for (int p = 0; p < npairs; ++p) {
-    const int kt = 2 * p;
-    A.load(ws.h, s_off, nrows, kt + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    down_ktile<NMT>(bA, s_a[0], lane, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(bA, kt + 2);
-    A.store(s_a[1]);
-    __syncthreads();
-    A.load(ws.h, s_off, nrows, min(kt + 2, KT - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    down_ktile<NMT>(bB, s_a[1], lane, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(bB, kt + 3);
-    A.store(s_a[0]);
-    __syncthreads();
-  }
-  if (KT & 1) down_ktile<NMT>(bA, s_a[0], lane, acc);
+  auto mul = [&](const u32x4 (&bs)[4], const _Float16* abuf) {
+    down_ktile<NMT>(bs, abuf, lane, acc);
+  };
+  if constexpr (KTC > 0)
+    k_loop_fixed<KTC, RING>(b, load_b, A, s_a, mul, std::make_integer_sequence<int, KTC>{});
+  else
+    k_loop<RING>(KT, b, load_b, A, s_a, mul);
 
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < kDownRTW; ++q) {
     const int col = (rt0 + q) * 16 + m;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
@@ -425,9 +513,9 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
   }
 }
 
+template <int KTC>   // I / 256 when fixed at compile time, else 0
 __global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, PrefillWs ws) {
   __shared__ __align__(16) _Float16 s_a[2][kATileHalves];
-  __shared__ int64_t s_off[kGroupRows];
   const int RB = L.H / kDownRowsPerBlock;
   const int unit = xcd_unit(blockIdx.x, ws.hdr[0] * RB);
   if (unit < 0) return;
@@ -435,14 +523,12 @@ __global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, Pre
   const int rb = unit % RB;
   const int4 it = ws.items[item];
   const int e = it.x, row0 = it.y, nrows = it.z;
-  if (threadIdx.x < kGroupRows) s_off[threadIdx.x] = static_cast<int64_t>(row0 + threadIdx.x) * L.I;
-  __syncthreads();
-  const int rt0 = rb * 16 + static_cast<int>(threadIdx.x >> 6) * 2;
+  const int rt0 = (rb * kGemmWaves + static_cast<int>(threadIdx.x >> 6)) * kDownRTW;
   switch ((nrows + 15) / 16) {
-    case 1: down_body<1>(L, ws, e, row0, nrows, rt0, s_a, s_off); break;
-    case 2: down_body<2>(L, ws, e, row0, nrows, rt0, s_a, s_off); break;
-    case 3: down_body<3>(L, ws, e, row0, nrows, rt0, s_a, s_off); break;
-    default: down_body<4>(L, ws, e, row0, nrows, rt0, s_a, s_off); break;
+    case 1: down_body<1, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a); break;
+    case 2: down_body<2, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a); break;
+    case 3: down_body<3, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a); break;
+    default: down_body<4, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a); break;
   }
 }
 
@@ -511,15 +597,27 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
   {
     const long long nb = static_cast<long long>(nitems) * (L.I / kGateupRowsPerBlock);
     const int grid = static_cast<int>((nb + 7) / 8 * 8);
-    e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel, dim3(grid), dim3(kThreads), 0, s,
-                      L, ws);
+    const dim3 g(grid), b(kThreads);
+    switch (L.H / kTileCols) {   // fully unrolled K loops for the common widths
+      case 4: e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel<4>, g, b, 0, s, L, ws, T); break;
+      case 8: e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel<8>, g, b, 0, s, L, ws, T); break;
+      case 12: e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel<12>, g, b, 0, s, L, ws, T); break;
+      case 16: e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel<16>, g, b, 0, s, L, ws, T); break;
+      default: e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel<0>, g, b, 0, s, L, ws, T); break;
+    }
   }
   if (e != hipSuccess) return e;
   {
     const long long nb = static_cast<long long>(nitems) * (L.H / kDownRowsPerBlock);
     const int grid = static_cast<int>((nb + 7) / 8 * 8);
-    e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel, dim3(grid), dim3(kThreads), 0, s, L,
-                      ws);
+    const dim3 g(grid), b(kThreads);
+    switch (L.I / kTileCols) {
+      case 1: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<1>, g, b, 0, s, L, ws); break;
+      case 2: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<2>, g, b, 0, s, L, ws); break;
+      case 3: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<3>, g, b, 0, s, L, ws); break;
+      case 4: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<4>, g, b, 0, s, L, ws); break;
+      default: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<0>, g, b, 0, s, L, ws); break;
+    }
   }
   if (e != hipSuccess) return e;
   return launch_kernel(K_PREFILL_COMBINE, prefill_combine_kernel, dim3(T), dim3(256), 0, s, T,

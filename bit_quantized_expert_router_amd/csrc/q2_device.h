@@ -55,7 +55,10 @@ __device__ __forceinline__ f16x8 nibbles_to_weights(uint32_t nib, f16x2 dd) {
   return r;
 }
 
-// Scale of block j (0..7) of the lane's row, from the row's 16 scale bytes.
+// Scale of block j (0..7) of the lane's row, from the row's 16 scale bytes,
+// duplicated into both halves with integer operations.  (Letting the packed
+// fma broadcast one half through its operand-select bits instead gave wrong
+// products on gfx950 in a direct comparison, so that form is not used.)
 __device__ __forceinline__ f16x2 scale_pair(const u32x4& s, int j) {
   uint32_t w = s[j >> 1];
   uint32_t h = (j & 1) ? (w >> 16) : (w & 0xFFFFu);
@@ -76,6 +79,29 @@ __device__ __forceinline__ u32x4 load_codes(const uint8_t* rec, int lane) {
 }
 __device__ __forceinline__ u32x4 load_scales(const uint8_t* rec, int lane) {
   return *reinterpret_cast<const u32x4*>(rec + kCodeBytes + 16 * (lane & 15));
+}
+
+// The same loads through a buffer resource: `base` (wave-uniform) is one
+// expert, `rec_off` (wave-uniform) the byte offset of the record in it, so
+// the address is a scalar base + scalar offset + a per-lane constant (no
+// 64-bit vector address arithmetic).  `bytes` bounds the resource: a load
+// past it returns zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t expert_rsrc(const uint8_t* base, uint32_t bytes) {
+  // the caller guarantees uniformity; readfirstlane lets the compiler keep
+  // the resource in scalar registers
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  uint8_t* p = reinterpret_cast<uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, static_cast<short>(0),
+                                           __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)),
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 load_codes(__amdgpu_buffer_rsrc_t r, uint32_t rec_off, int lane) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane, rec_off, 0);
+}
+__device__ __forceinline__ u32x4 load_scales(__amdgpu_buffer_rsrc_t r, uint32_t rec_off, int lane) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, kCodeBytes + 16 * (lane & 15), rec_off, 0);
 }
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }

@@ -80,7 +80,7 @@ enum { MOE_OP_ROUTE = 0, MOE_OP_DECODE = 1, MOE_OP_PREFILL = 2 };
 #define MOE_MAX_TOPK 16          /* k                                        */
 #define MOE_MAX_DECODE_TOKENS 4  /* T of moe_expert_forward_decode           */
 #define MOE_MAX_DIM 8192         /* H and I (each a multiple of 256)         */
-#define MOE_MAX_TOKENS (1 << 22) /* T of routing and prefill                 */
+#define MOE_MAX_TOKENS (1 << 17) /* T of routing and prefill (131072)        */
 
 typedef struct {
   const void* experts;    /* [device] E experts; expert e at experts + e*expert_stride;
@@ -114,7 +114,7 @@ size_t moe_workspace_bytes(int32_t op, int32_t T, int32_t E, int32_t k, int32_t 
  *            histogram is requested (else may be NULL), 256-byte aligned.
  * Errors: INVALID_ARG for null required pointers, T < 1, k < 1, k > E, a
  * partial set of histogram outputs; UNSUPPORTED for E > 1024, k > 16,
- * T > 2^22; WORKSPACE when too small.
+ * T > 2^17; WORKSPACE when too small.
  */
 int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
                    int32_t* topk_ids, float* topk_w,
@@ -175,7 +175,8 @@ int moe_expert_forward_decode_routed(const moe_q2_layer* layer, const void* x, i
  * 1024 and 32768: "Strata 实测 ...", section 四, change 4).
  * Arguments as for the decode call, plus the four histogram arrays from
  * moe_route_topk for the same topk_ids.  Computes the same `out`.
- * Errors: as for decode, with T limited to 1..2^22 instead of 1..4.
+ * Errors: as for decode, with T limited to 1..2^17 instead of 1..4 (so that
+ * every activation offset fits in 32 bits).
  */
 int moe_expert_forward_prefill(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
                                int32_t T, const int32_t* topk_ids, const float* topk_w,

@@ -139,7 +139,7 @@ def test_forward_validation(lib, which):
         assert forward(lib, which, ids=None, w=None, wsb=100) == -3   # outputs are optional
     elif which == "prefill":
         assert forward(lib, which, counts=None) == -1
-        assert forward(lib, which, T=(1 << 22) + 1) == -2
+        assert forward(lib, which, T=(1 << 17) + 1) == -2
 
 
 def test_profile_hooks_host_only(lib):
