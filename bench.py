@@ -45,7 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="",
-                    help="decode1|decode1_two_calls|decode2|decode3|prefill (profiling runs)")
+                    help="decode1|decode1_two_calls|decode2|decode3|prefill|stack (profiling runs)")
+    ap.add_argument("--stack-layers", type=int, default=48,
+                    help="layers of the stacked decode/prefill runs (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -267,6 +269,82 @@ def main():
         results["decode_T3"] = decode_case(3, "zipf", args.steps // 2, args.warmup)
     if only in ("", "prefill"):
         results["prefill_T1024"] = prefill_case(1024, args.prefill_steps, max(4, args.warmup // 4))
+
+    # ------------------------------------------------- 48 stacked layers
+    # 48 distinct layers (54.5 GB), x_{l+1} = x_l + MoE_l(rmsnorm(x_l)) in a
+    # float32 residual stream, Zipf(1.1) routing with a fixed seed per layer.
+    if only in ("", "stack") and args.stack_layers > 0:
+        NL = args.stack_layers
+        del layers[:]                      # free the rotating set first
+        torch.cuda.empty_cache()
+        stack = []
+        for l in range(NL):
+            ex = synth.device_expert_blob(E, H, I, synth.torch_seed(2, l, 1), dev)
+            sh = synth.device_expert_blob(1, H, I, synth.torch_seed(2, l, 2), dev)
+            stack.append(B.Layer(ex, sh, E, H, I, synth.expert_stride(H, I)))
+        torch.cuda.synchronize()
+
+        def stack_decode(T, steps):
+            lg = [synth.device_zipf_logits(T, E, synth.torch_seed(2, l, 3), dev) for l in range(NL)]
+            x0 = torch.randn((T, H), device=dev).to(torch.bfloat16).float()
+            bufs = [torch.empty_like(x0) for _ in range(2)]
+            ws = B.workspace(B.MOE_OP_DECODE, T, E, K, H, I, dev)
+
+            def step(_i):
+                x = x0
+                for l in range(NL):
+                    o = bufs[l & 1]
+                    B.moe_expert_forward_decode_routed(stack[l], x, lg[l], K, o, None, None, x,
+                                                       B.MOE_FLAG_PRENORM_RMS, ws)
+                    x = o
+            ms = graphed(step, 1, steps)
+            return {"T": T, "layers": NL, "launch": "hip_graph", "ms_per_step": ms,
+                    "us_per_layer": ms * 1e3 / NL, "tokens_per_s": T * 1000.0 / ms}
+
+        def stack_prefill(T, steps):
+            x0 = torch.randn((T, H), device=dev).to(torch.bfloat16).float()
+            bufs = [torch.empty_like(x0) for _ in range(2)]
+            ws = B.workspace(B.MOE_OP_PREFILL, T, E, K, H, I, dev)
+            wsr = B.workspace(B.MOE_OP_ROUTE, T, E, K, H, I, dev)
+            r = {n: torch.empty(sz, dtype=dt, device=dev) for n, sz, dt in [
+                ("ids", (T, K), torch.int32), ("w", (T, K), torch.float32), ("counts", (E,), torch.int32),
+                ("offsets", (E + 1,), torch.int32), ("sp", (T * K,), torch.int32),
+                ("pp", (T * K,), torch.int32)]}
+            lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+
+            def run(prof):
+                x = x0
+                for l in range(NL):
+                    lg.copy_(synth.device_zipf_logits(T, E, synth.torch_seed(2, l, 3), dev))
+                    B.moe_route_topk(lg, K, r["ids"], r["w"], r["counts"], r["offsets"], r["sp"],
+                                     r["pp"], wsr)
+                    o = bufs[l & 1]
+                    B.moe_expert_forward_prefill(stack[l], x, r["ids"], r["w"], r["counts"],
+                                                 r["offsets"], r["sp"], r["pp"], o, x,
+                                                 B.MOE_FLAG_PRENORM_RMS, ws)
+                    x = o
+            run(False)
+            torch.cuda.synchronize()
+            B.profile_reset()
+            B.profile_enable(True)
+            run(True)
+            torch.cuda.synchronize()
+            B.profile_enable(False)
+            kern = {k.replace("_kernel", ""): v[1] for k, v in B.profile_results().items() if v[0]}
+            moe_ms = sum(kern.values())
+            gemm_ms = kern.get("prefill_gateup", 0.0) + kern.get("prefill_down", 0.0)
+            return {"T": T, "layers": NL, "launch": "eager, dispatch-stamped kernel times",
+                    "moe_ms_per_step": moe_ms, "us_per_layer": moe_ms * 1e3 / NL,
+                    "grouped_gemm_us_per_layer": gemm_ms * 1e3 / NL,
+                    "tokens_per_s": T * 1000.0 / moe_ms,
+                    "kernel_ms_per_layer": {k: v / NL for k, v in kern.items()}}
+
+        for T in (1, 2, 3):
+            results[f"stack{NL}_decode_T{T}"] = stack_decode(T, 20)
+        for T in (1024, 32768):
+            results[f"stack{NL}_prefill_T{T}"] = stack_prefill(T, 1)
+        del stack
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ cpu baseline
     cpu = None

@@ -131,6 +131,23 @@ def zipf_logits(rng: np.random.Generator, T: int, E: int, s: float = 1.1) -> np.
     return (base[None, :] + gumbel).astype(np.float32)
 
 
+def device_zipf_logits(T: int, E: int, seed: int, device="cuda", s: float = 1.1):
+    """zipf_logits' recipe with torch's generator on the device (for the
+    large stacked workloads whose logits would take long to make on the
+    host).  Returns a float32 [T, E] tensor."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    ranks = torch.arange(1, E + 1, dtype=torch.float64, device=device)
+    logp = -s * torch.log(ranks)
+    logp -= torch.log(torch.exp(logp).sum())
+    perm = torch.randperm(E, device=device, generator=g)
+    base = torch.empty(E, dtype=torch.float64, device=device)
+    base[perm] = logp
+    u = torch.rand((T, E), dtype=torch.float64, device=device, generator=g).clamp_min_(1e-300)
+    return (base[None, :] - torch.log(-torch.log(u))).to(torch.float32)
+
+
 def tie_logits(rng: np.random.Generator, T: int, E: int, levels: int = 4) -> np.ndarray:
     """Logits drawn from a few values only, so equal logits are common."""
     return rng.integers(0, levels, size=(T, E)).astype(np.float32) * np.float32(0.5)
