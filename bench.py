@@ -138,7 +138,7 @@ def main():
         return {k: v for k, v in B.profile_results().items() if v[0] > 0}
 
     # ---------------------------------------------------------------- decode
-    def decode_case(T, kind, n_steps, warmup, routed=True):
+    def decode_case(T, kind, n_steps, warmup, routed=True, gemv=False):
         total = n_steps * 2 + warmup
         rng = synth.rng_for(1, 100 + T, 0)
         xd, xv = synth.activations(rng, min(total, 64) * T, H, "bf16")
@@ -154,10 +154,17 @@ def main():
         wts = torch.empty((total, T, K), dtype=torch.float32, device=dev)
         out = torch.empty((T, H), dtype=torch.float32, device=dev)
         ws = B.workspace(B.MOE_OP_DECODE, T, E, K, H, I, dev)
+        if gemv:         # router weights (bf16 [E, H]) per rotating layer
+            wr = [(torch.randn((E, H), device=dev) / np.sqrt(H)).to(torch.bfloat16)
+                  for _ in range(len(layers))]
+            wsg = B.workspace(B.MOE_OP_ROUTE_GEMV, T, E, K, H, I, dev)
 
         def step(i):
             L = layers[i % len(layers)]
-            if routed:   # one call: top-k inside the expert kernels
+            if gemv:     # router GEMV + top-k kernel, then the expert layer
+                B.moe_route_topk_gemv(xs[i % nx], wr[i % len(layers)], K, ids[i], wts[i], None, wsg)
+                B.moe_expert_forward_decode(L, xs[i % nx], ids[i], wts[i], out, None, 0, ws)
+            elif routed:   # one call: top-k inside the expert kernels
                 B.moe_expert_forward_decode_routed(L, xs[i % nx], logits[i], K, out, ids[i], wts[i],
                                                    None, 0, ws)
             else:        # moe_route_topk, then the expert layer
@@ -181,9 +188,14 @@ def main():
         if "route_topk_kernel" in kern:
             rt = kern["route_topk_kernel"]
             kms = {"route_topk": rt[1] / rt[0], **kms}
+        if "route_gemv_topk_kernel" in kern:
+            rt = kern["route_gemv_topk_kernel"]
+            kms = {"route_gemv_topk": rt[1] / rt[0], **kms}
         gu_bytes = slots * 2 * MAT_BYTES + T * H * 2 + (T * K + T) * I * 2   # weights, x, h
         return {
-            "T": T, "routing": kind, "calls": "decode_routed" if routed else "route_topk+decode",
+            "T": T, "routing": kind,
+            "calls": ("route_topk_gemv+decode (router GEMV included)" if gemv else
+                      "decode_routed" if routed else "route_topk+decode"),
             "launch": "hip_graph", "ms_per_layer": ms,
             "ms_per_layer_eager": ms_eager, "tokens_per_s": T * 1000.0 / ms,
             "tokens_per_s_eager": T * 1000.0 / ms_eager,
@@ -263,6 +275,9 @@ def main():
     if only in ("", "decode1_two_calls"):
         results["decode_T1_two_calls"] = decode_case(1, "router", args.steps // 2, args.warmup,
                                                      routed=False)
+    if only in ("", "decode1_gemv"):
+        results["decode_T1_router_gemv"] = decode_case(1, "router", args.steps // 2, args.warmup,
+                                                       routed=False, gemv=True)
     if only in ("", "decode2"):
         results["decode_T2"] = decode_case(2, "zipf", args.steps // 2, args.warmup)
     if only in ("", "decode3"):

@@ -21,9 +21,9 @@ LIB_PATH = os.environ.get("MOE_Q2_LIB", os.path.join(_HERE, "libmoe_q2.so"))
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_FLAG_PRENORM_RMS = 1
-MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL = 0, 1, 2
+MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL, MOE_OP_ROUTE_GEMV = 0, 1, 2, 3
 
-EXPORTS = ["moe_workspace_bytes", "moe_route_topk", "moe_expert_forward_decode",
+EXPORTS = ["moe_workspace_bytes", "moe_route_topk", "moe_route_topk_gemv", "moe_expert_forward_decode",
            "moe_expert_forward_decode_routed", "moe_expert_forward_prefill", "moe_status_string", "moe_last_error",
            "moe_profile_enable", "moe_profile_reset", "moe_profile_num_kernels",
            "moe_profile_kernel_name", "moe_profile_query"]
@@ -50,6 +50,8 @@ def _load():
     lib.moe_workspace_bytes.restype = sz
     lib.moe_route_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_route_topk.restype = C.c_int
+    lib.moe_route_topk_gemv.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.moe_route_topk_gemv.restype = C.c_int
     lib.moe_expert_forward_decode.argtypes = [C.POINTER(_Layer), vp, i32, i32, vp, vp, i32, vp, vp,
                                               i32, C.c_uint32, vp, sz, vp]
     lib.moe_expert_forward_decode.restype = C.c_int
@@ -127,7 +129,11 @@ def moe_workspace_bytes(op: int, T: int, E: int, k: int, H: int, I: int) -> int:
 
 
 def workspace(op: int, T: int, E: int, k: int, H: int, I: int, device="cuda") -> torch.Tensor:
+    """Workspace for one call (zeroed for MOE_OP_ROUTE_GEMV, whose counter
+    must start at zero)."""
     n = max(moe_workspace_bytes(op, T, E, k, H, I), 256)
+    if op == MOE_OP_ROUTE_GEMV:
+        return torch.zeros(n, dtype=torch.uint8, device=device)
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
@@ -137,6 +143,15 @@ def moe_route_topk(logits, k, topk_ids, topk_w, counts=None, offsets=None, sorte
     _check(lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_w), _ptr(counts),
                               _ptr(offsets), _ptr(sorted_pairs), _ptr(pair_pos), _ptr(ws),
                               0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def moe_route_topk_gemv(x, router_w, k, topk_ids, topk_w, logits=None, ws=None, stream=None):
+    """router_w: bf16 tensor [E, H] (or its int16/uint16 bits)."""
+    T, H = x.shape
+    E = router_w.shape[0]
+    _check(lib.moe_route_topk_gemv(_ptr(x), _dtype_code(x), T, _ptr(router_w), E, H, k, _ptr(logits),
+                                   _ptr(topk_ids), _ptr(topk_w), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(stream)))
 
 
 def moe_expert_forward_decode(layer: Layer, x, topk_ids, topk_w, out, residual=None, flags=0,

@@ -73,7 +73,8 @@ Profiler& prof() {
 const char* const kKernelNames[K_NUM_KERNELS] = {
     "route_topk_kernel",     "route_scan_kernel",     "route_scatter_kernel",
     "decode_gateup_kernel",  "decode_down_kernel",    "prefill_prep_kernel",
-    "prefill_gateup_kernel", "prefill_down_kernel",   "prefill_combine_kernel"};
+    "prefill_gateup_kernel", "prefill_down_kernel",   "prefill_combine_kernel",
+    "route_gemv_topk_kernel"};
 
 bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_BF16; }
 
@@ -171,6 +172,9 @@ size_t moe_workspace_bytes(int32_t op, int32_t T, int32_t E, int32_t k, int32_t 
     case MOE_OP_PREFILL:
       if (H < 256 || I < 256) return 0;
       return prefill_workspace_bytes(T, E, k, H, I);
+    case MOE_OP_ROUTE_GEMV:
+      if (T > MOE_MAX_DECODE_TOKENS) return 0;
+      return 256 + (static_cast<size_t>(T) * E * 4 + 255) / 256 * 256;
     default: return 0;
   }
 }
@@ -217,6 +221,36 @@ int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t
                                 pair_pos, s)) != hipSuccess)
     return hip_fail(e, "route_scatter launch");
   return MOE_OK;
+}
+
+int moe_route_topk_gemv(const void* x, int32_t x_dtype, int32_t T, const uint16_t* router_w,
+                        int32_t E, int32_t H, int32_t k, float* logits, int32_t* topk_ids,
+                        float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !router_w || !topk_ids || !topk_w)
+    return fail(MOE_ERR_INVALID_ARG, "x, router_w, topk_ids and topk_w are required");
+  if (!valid_dtype(x_dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1");
+  if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1");
+  if (k < 1) return fail(MOE_ERR_INVALID_ARG, "k must be >= 1");
+  if (H < 256 || H % 256) return fail(MOE_ERR_INVALID_ARG, "H must be a positive multiple of 256");
+  if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "at most 4 tokens");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E must be <= 1024");
+  if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k must be <= 16");
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "k must be <= E");
+  if (H > MOE_MAX_DIM) return fail(MOE_ERR_UNSUPPORTED, "H must be <= 8192");
+  if (!aligned(x, 16) || !aligned(router_w, 16) || (logits && !aligned(logits, 4)) ||
+      !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return fail(MOE_ERR_INVALID_ARG, "x and router_w must be 16-byte aligned, the outputs 4-byte aligned");
+  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is required");
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t need = moe_workspace_bytes(MOE_OP_ROUTE_GEMV, T, E, k, H, 0);
+  if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* lg = logits ? logits : reinterpret_cast<float*>(ws + 256);
+  const hipError_t e = launch_route_gemv_topk(x, x_dtype == MOE_BF16, T, router_w, E, H, k, lg, topk_ids,
+                                             topk_w, reinterpret_cast<uint32_t*>(ws),
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "route_gemv_topk launch");
 }
 
 static int check_forward(const moe_q2_layer* layer, const void* x, int32_t x_dtype, int32_t T,

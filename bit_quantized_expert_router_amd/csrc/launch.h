@@ -19,6 +19,7 @@ enum KernelId {
   K_PREFILL_GATEUP,
   K_PREFILL_DOWN,
   K_PREFILL_COMBINE,
+  K_ROUTE_GEMV_TOPK,
   K_NUM_KERNELS
 };
 
@@ -55,6 +56,11 @@ inline __host__ __device__ int route_chunk_tokens(int T) {
 }
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              int32_t* rank, int32_t* local_counts, hipStream_t s);
+// Router GEMV (fp64 accumulation, bf16 weight [E][H]) + top-k for T <= 4
+// tokens in one kernel; `counter` is a zeroed word the kernel leaves zeroed.
+hipError_t launch_route_gemv_topk(const void* x, int x_bf16, int T, const uint16_t* W, int E, int H,
+                                  int k, float* logits, int32_t* ids, float* w, uint32_t* counter,
+                                  hipStream_t s);
 hipError_t launch_route_expert_scan(const int32_t* local_counts, int32_t* ebase, int E, int n_chunks,
                                     int32_t* counts, hipStream_t s);
 hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const int32_t* ebase,

@@ -158,6 +158,123 @@ __global__ __launch_bounds__(1024) void route_scatter_kernel(
   }
 }
 
+
+// ------------------------------------------------- router GEMV + top-k --
+// Router logits computed on the device and the top-k taken in the same
+// kernel (decode, T <= 4): logits[t][e] = fp32(sum_h x[t][h] * W[e][h]),
+// W the bf16 router weight [E][H].  Every product of a bf16 weight and a
+// bf16 or fp32 activation is exact in fp64, and the sum is accumulated in
+// fp64 (lane partial sums over fixed columns, then a fixed-order wavefront
+// reduction) and rounded once to fp32, so the logits agree with a plain fp64
+// dot product except when that one rounding falls within the fp64 summation
+// error of an fp32 rounding boundary.  Each wave computes the logits of two
+// experts for all T tokens; the last workgroup to finish (one agent-scope
+// atomic per workgroup on a counter it then resets) selects the top-k from
+// the logits written by all of them.  No workgroup waits for another.
+constexpr int kGemvWaves = 4;
+constexpr int kGemvExpertsPerWave = 2;
+constexpr int kGemvExpertsPerBlock = kGemvWaves * kGemvExpertsPerWave;
+
+extern "C" __device__ double __ockl_wfred_add_f64(double);
+
+// NC: 512-column chunks per lane (ceil(H / 512)); the router weight rows
+// are read first (all of them in flight at once) while x is staged in LDS.
+template <bool BF16X, int PER, int NC>
+__global__ __launch_bounds__(64 * kGemvWaves) void route_gemv_topk_kernel(
+    const void* __restrict__ x, int T, const uint16_t* __restrict__ W, int E, int H, int k,
+    float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ w,
+    uint32_t* __restrict__ counter) {
+  extern __shared__ __align__(16) float s_x[];   // [T][H] as float32
+  __shared__ uint32_t s_last;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int e0 = (blockIdx.x * kGemvWaves + wid) * kGemvExpertsPerWave;
+  // weight rows: lane covers columns 8 * lane + 512 * c .. + 7 (clamped loads)
+  u32x4 wr[NC][kGemvExpertsPerWave];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int q = 0; q < kGemvExpertsPerWave; ++q)
+      wr[c][q] = *reinterpret_cast<const u32x4*>(
+          W + static_cast<size_t>(min(e0 + q, E - 1)) * H + min(8 * lane + 512 * c, H - 8));
+  // x into LDS as float32 (8 values per thread and step)
+  for (int i = 8 * static_cast<int>(threadIdx.x); i < T * H; i += 8 * 64 * kGemvWaves) {
+    f32x4 a, b;
+    if (BF16X) {
+      const u32x4 r = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + i);
+      a = f32x4{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xFFFF0000u),
+                __uint_as_float(r[1] << 16), __uint_as_float(r[1] & 0xFFFF0000u)};
+      b = f32x4{__uint_as_float(r[2] << 16), __uint_as_float(r[2] & 0xFFFF0000u),
+                __uint_as_float(r[3] << 16), __uint_as_float(r[3] & 0xFFFF0000u)};
+    } else {
+      a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + i);
+      b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + i + 4);
+    }
+    *reinterpret_cast<f32x4*>(s_x + i) = a;
+    *reinterpret_cast<f32x4*>(s_x + i + 4) = b;
+  }
+  __syncthreads();
+  double acc[kGemvExpertsPerWave][MOE_MAX_DECODE_TOKENS];
+#pragma unroll
+  for (int q = 0; q < kGemvExpertsPerWave; ++q)
+#pragma unroll
+    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) acc[q][t] = 0.0;
+#pragma unroll
+  for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
+    if (t < T) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int c0 = 8 * lane + 512 * c;
+        if (c0 < H) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(s_x + t * H + c0);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(s_x + t * H + c0 + 4);
+          const double xv[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+          for (int q = 0; q < kGemvExpertsPerWave; ++q) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const double wlo = static_cast<double>(__uint_as_float(wr[c][q][i] << 16));
+              const double whi = static_cast<double>(__uint_as_float(wr[c][q][i] & 0xFFFF0000u));
+              acc[q][t] = __builtin_fma(wlo, xv[2 * i], acc[q][t]);
+              acc[q][t] = __builtin_fma(whi, xv[2 * i + 1], acc[q][t]);
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kGemvExpertsPerWave; ++q) {
+#pragma unroll
+    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
+      if (t < T) {
+        const double sum = __ockl_wfred_add_f64(acc[q][t]);
+        if (lane == 0 && e0 + q < E) logits[static_cast<size_t>(t) * E + e0 + q] = static_cast<float>(sum);
+      }
+    }
+  }
+  // publish this workgroup's logits; the last workgroup selects
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == gridDim.x - 1 ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (wid < T) {
+    int my_e;
+    float l;
+    topk_one_token<PER>(logits + static_cast<size_t>(wid) * E, E, k, lane, my_e, l);
+    const float wt = topk_weight(l, k, lane);
+    if (lane < k) {
+      ids[static_cast<size_t>(wid) * k + lane] = my_e;
+      w[static_cast<size_t>(wid) * k + lane] = wt;
+    }
+  }
+  if (threadIdx.x == 0) counter[0] = 0u;   // ready for the next call
+}
+
 }  // namespace
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
@@ -191,6 +308,30 @@ hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const i
   return launch_kernel(K_ROUTE_SCATTER, route_scatter_kernel, dim3((P + 1023) / 1024), dim3(1024), 0,
                        s, ids, rank, ebase, counts, E, P, k, n_chunks, route_chunk_tokens(T),
                        offsets, sorted_pairs, pair_pos);
+}
+
+hipError_t launch_route_gemv_topk(const void* x, int x_bf16, int T, const uint16_t* W, int E, int H,
+                                  int k, float* logits, int32_t* ids, float* w, uint32_t* counter,
+                                  hipStream_t s) {
+  const dim3 grid((E + kGemvExpertsPerBlock - 1) / kGemvExpertsPerBlock), block(64 * kGemvWaves);
+  const uint32_t lds = static_cast<uint32_t>(T) * H * 4u;
+  const int per = (E + kWave - 1) / kWave;
+  const int nc = (H + 511) / 512;
+  // (x dtype, top-k lane bound, column chunks): the common shapes get exact
+  // chunk counts, the rest the largest
+#define MOE_GEMV_LAUNCH(XB, P, NC)                                                              \
+  launch_kernel(K_ROUTE_GEMV_TOPK, route_gemv_topk_kernel<XB, P, NC>, grid, block, lds, s, x, T, W, \
+                E, H, k, logits, ids, w, counter)
+#define MOE_GEMV_NC(XB, P)                          \
+  (nc <= 2 ? MOE_GEMV_LAUNCH(XB, P, 2)              \
+           : nc <= 6 ? MOE_GEMV_LAUNCH(XB, P, 6) : MOE_GEMV_LAUNCH(XB, P, 16))
+#define MOE_GEMV_PER(XB)                                                     \
+  (per <= 1 ? MOE_GEMV_NC(XB, 1)                                             \
+            : per <= 8 ? MOE_GEMV_NC(XB, 8) : MOE_GEMV_NC(XB, 16))
+  return x_bf16 ? MOE_GEMV_PER(true) : MOE_GEMV_PER(false);
+#undef MOE_GEMV_PER
+#undef MOE_GEMV_NC
+#undef MOE_GEMV_LAUNCH
 }
 
 }  // namespace moeq2

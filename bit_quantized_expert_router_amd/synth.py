@@ -107,6 +107,12 @@ def activations(rng: np.random.Generator, T: int, H: int, dtype: str = "bf16"):
 
 
 # -------------------------------------------------------------------- logits --
+def router_weight(rng: np.random.Generator, E: int, H: int) -> np.ndarray:
+    """bf16 router weight [E, H] (row e for expert e), N(0, 1/H), as raw
+    bf16 bits (uint16)."""
+    return bf16_bits((rng.standard_normal((E, H)) / np.sqrt(H)).astype(np.float32))
+
+
 def router_logits(rng: np.random.Generator, x_f32: np.ndarray, E: int) -> np.ndarray:
     """float32(float64(x) @ float64(W_r)), W_r = bf16(N(0, 1/H)) [H, E]."""
     H = x_f32.shape[1]

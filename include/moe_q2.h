@@ -18,7 +18,8 @@
  *   moe_expert_forward_prefill any number of tokens (prompt chunks of 1024
  *                              or 32768 tokens), grouped by expert
  * and moe_expert_forward_decode_routed does the first two for decode in one
- * call.
+ * call; moe_route_topk_gemv computes the router logits themselves and their
+ * top-k for decode.
  *
  * Conventions for every entry point
  *   - Pointers marked [device] are device addresses (hipMalloc'd memory or
@@ -73,7 +74,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * experts; the pre-norm of a residual block x + MoE(rmsnorm(x)). */
 #define MOE_FLAG_PRENORM_RMS 1u
 
-enum { MOE_OP_ROUTE = 0, MOE_OP_DECODE = 1, MOE_OP_PREFILL = 2 };
+enum { MOE_OP_ROUTE = 0, MOE_OP_DECODE = 1, MOE_OP_PREFILL = 2, MOE_OP_ROUTE_GEMV = 3 };
 
 /* Limits of this build (validated): */
 #define MOE_MAX_EXPERTS 1024     /* E                                        */
@@ -121,6 +122,30 @@ int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
                    int32_t* counts, int32_t* offsets,
                    int32_t* sorted_pairs, int32_t* pair_pos,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Router logits and top-k in one kernel, for T = 1..4 decode tokens: the
+ * router is the linear map logits = x W^T with a bf16 weight W [E, H]
+ * (the routing step that hands the selected expert ids to the expert
+ * compute, "RTX PRO 4500 ...", section 最重要机制, item 1).  Each logit is
+ * the dot product of exact fp64 products accumulated in fp64 and rounded
+ * once to float32; the selection and weights are then exactly those of
+ * moe_route_topk on these logits.
+ *   x         [device] [T, H] activations, x_dtype MOE_F32 or MOE_BF16, 16-byte aligned.
+ *   router_w  [device] bf16 [E, H] (row e belongs to expert e), 16-byte aligned.
+ *   logits    [device] float32 [T, E] output, or NULL (then only in the workspace).
+ *   topk_ids, topk_w  [device] [T, k] outputs.
+ *   workspace [device] >= moe_workspace_bytes(MOE_OP_ROUTE_GEMV, T, E, k, H, 0),
+ *             256-byte aligned.  Its first 4 bytes are a counter that must be
+ *             zero before the first call on this workspace; every call leaves
+ *             it zero.  Concurrent calls need separate workspaces.
+ * Errors: INVALID_ARG (null pointers, T, E or k < 1, k > E, H not a multiple
+ * of 256, unknown dtype, misalignment), UNSUPPORTED (T > 4, E > 1024, k > 16,
+ * H > 8192), WORKSPACE.
+ */
+int moe_route_topk_gemv(const void* x, int32_t x_dtype, int32_t T, const uint16_t* router_w,
+                        int32_t E, int32_t H, int32_t k, float* logits, int32_t* topk_ids,
+                        float* topk_w, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Decode-time expert layer for T = 1..4 tokens (one decode step or a verify

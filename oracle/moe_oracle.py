@@ -40,7 +40,7 @@ __all__ = [
     "TILE_ROWS", "TILE_COLS", "TILE_BYTES", "CODE_BYTES", "BLOCK",
     "matrix_nbytes", "expert_layout", "decode_matrix", "encode_matrix",
     "dequantize", "quantize_q2", "ExpertBlob",
-    "route_topk", "route_weights", "route_histogram",
+    "router_logits", "route_topk", "route_weights", "route_histogram",
     "rms_prenorm", "silu", "expert_ffn", "moe_token", "moe_layer", "moe_stack",
     "RMS_EPS",
 ]
@@ -205,6 +205,18 @@ class ExpertBlob:
 # --------------------------------------------------------------------------
 # Router (a1) and permutation (a2)
 # --------------------------------------------------------------------------
+def router_logits(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Router logits for the GPU-side router (reading R7): the token
+    activations times the router weight, W [E, H] with row e belonging to
+    expert e, accumulated in float64 and rounded once to float32.  The
+    routing step is the one that hands the per-token expert ids to the
+    expert compute ("RTX PRO 4500 单卡跑 125B MoE", section 最重要机制,
+    item 1)."""
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    return (x @ W.T).astype(np.float32)
+
+
 def route_topk(logits: np.ndarray, k: int):
     """Per token, the k experts with the largest logit, compared as exact
     float32 values; equal logits go to the lower expert id (R2).  Returns

@@ -70,6 +70,32 @@ def route(lib, **kw):
                               a["wsb"], None)
 
 
+def gemv(lib, **kw):
+    a = dict(x=FAKE, xd=1, T=1, W=FAKE, E=64, H=1024, k=4, lg=None, ids=FAKE, w=FAKE, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return lib.moe_route_topk_gemv(C.c_void_p(a["x"]), a["xd"], a["T"], C.c_void_p(a["W"]), a["E"], a["H"],
+                                   a["k"], C.c_void_p(a["lg"]), C.c_void_p(a["ids"]), C.c_void_p(a["w"]),
+                                   C.c_void_p(a["ws"]), a["wsb"], None)
+
+
+def test_route_gemv_validation(lib):
+    assert gemv(lib, x=None) == -1
+    assert gemv(lib, W=None) == -1
+    assert gemv(lib, T=0) == -1
+    assert gemv(lib, T=5) == -2
+    assert gemv(lib, E=2048) == -2
+    assert gemv(lib, k=17) == -2
+    assert gemv(lib, E=3, k=4) == -1
+    assert gemv(lib, H=1000) == -1
+    assert gemv(lib, H=16384) == -2
+    assert gemv(lib, xd=9) == -1
+    assert gemv(lib, W=FAKE + 8) == -1
+    assert gemv(lib, ws=None) == -3
+    assert gemv(lib, wsb=16) == -3
+    assert lib.moe_workspace_bytes(3, 4, 512, 10, 3072, 0) >= 256 + 4 * 512 * 4
+    assert lib.moe_workspace_bytes(3, 5, 512, 10, 3072, 0) == 0
+
+
 def test_route_validation(lib):
     assert route(lib, logits=None) == -1
     assert route(lib, T=0) == -1

@@ -114,6 +114,56 @@ def test_route_bit_exact(B, T, E, k, kind):
         assert_route_exact(ids, w, r, E, hist)
 
 
+# -------------------------------------------------------- router GEMV + top-k --
+GEMV_CASES = [  # T, E, H, k, x dtype
+    (1, 64, 1024, 4, "f32"), (1, 512, 3072, 10, "bf16"), (2, 512, 3072, 10, "bf16"),
+    (3, 512, 3072, 10, "bf16"), (4, 512, 3072, 10, "f32"), (4, 1024, 512, 16, "bf16"),
+    (2, 300, 768, 7, "f32"),
+]
+
+
+@pytest.mark.parametrize("T,E,H,k,xdt", GEMV_CASES)
+def test_route_gemv_topk(B, T, E, H, k, xdt):
+    """Logits bit-exact with the oracle's fp64 dot products rounded to
+    float32, ids bit-exact, weights within 1e-6; two calls in a row on one
+    workspace (its counter must come back to zero)."""
+    print(f"router gemv T={T} E={E} H={H} k={k} {xdt}", flush=True)
+    rng = synth.rng_for(60, T, E)
+    xd, xv = synth.activations(rng, T, H, xdt)
+    Wb = synth.router_weight(rng, E, H)
+    ref_lg = O.router_logits(xv, synth.bf16_to_f32(Wb))
+    ids, w = O.route_topk(ref_lg, k)
+    Wt = torch.from_numpy(Wb.view(np.int16)).cuda()
+    ws = B.workspace(B.MOE_OP_ROUTE_GEMV, T, E, k, H, 0)
+    for rep in range(2):
+        lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        rid = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        rw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        B.moe_route_topk_gemv(dev_x(xd, xdt), Wt, k, rid, rw, lg, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(lg.cpu().numpy(), ref_lg), "logits differ"
+        assert_route_exact(ids, w, {"topk_ids": rid, "topk_w": rw}, E, False)
+    assert int(ws[:4].view(torch.int32)[0]) == 0
+
+
+def test_route_gemv_then_decode_matches_oracle(B, layer_full):
+    """Router GEMV + top-k, then the decode layer: the whole decode path from
+    activations and the router weight."""
+    L = layer_full
+    T = 2
+    rng = synth.rng_for(61, 0, 0)
+    xd, xv = synth.activations(rng, T, 3072, "bf16")
+    Wb = synth.router_weight(rng, 512, 3072)
+    ids, w = O.route_topk(O.router_logits(xv, synth.bf16_to_f32(Wb)), 10)
+    rid = torch.empty((T, 10), dtype=torch.int32, device="cuda")
+    rw = torch.empty((T, 10), dtype=torch.float32, device="cuda")
+    B.moe_route_topk_gemv(dev_x(xd, "bf16"), torch.from_numpy(Wb.view(np.int16)).cuda(), 10, rid, rw,
+                          None, B.workspace(B.MOE_OP_ROUTE_GEMV, T, 512, 10, 3072, 0))
+    out = run_decode(B, L, dev_x(xd, "bf16"), {"topk_ids": rid, "topk_w": rw})
+    assert np.array_equal(rid.cpu().numpy(), ids)
+    check_out(to_np(out), O.moe_layer(xv, ids, w, L.ref), "router gemv + decode")
+
+
 # ------------------------------------------------------------------- decode --
 @pytest.fixture(scope="module")
 def layer_small(B):

@@ -143,3 +143,34 @@ def test_histogram_tiny_by_hand():
     assert list(offsets) == [0, 2, 4, 6, 6]
     assert list(sp) == [1, 2, 3, 5, 0, 4]
     assert list(pp) == [4, 0, 1, 2, 5, 3]
+
+
+# ----------------------------------------------------------- router logits --
+def test_router_logits_exact_dot_products():
+    """Each logit is the exactly rounded dot product: compare with math.fsum
+    (an exactly rounded sum of the exact fp64 products of bf16 values) on
+    small random cases."""
+    import math
+    rng = synth.rng_for(70, 0, 0)
+    T, E, H = 3, 5, 256
+    xb = synth.bf16_to_f32(synth.bf16_bits(rng.standard_normal((T, H)).astype(np.float32)))
+    Wb = synth.router_weight(rng, E, H)
+    W = synth.bf16_to_f32(Wb)
+    got = O.router_logits(xb, W)
+    assert got.dtype == np.float32 and got.shape == (T, E)
+    for t in range(T):
+        for e in range(E):
+            exact = math.fsum(float(a) * float(b) for a, b in zip(xb[t], W[e]))
+            assert got[t, e] == np.float32(exact)
+
+
+def test_router_logits_orientation():
+    """One nonzero weight at (e, h) puts x[:, h] * w into column e only."""
+    T, E, H = 2, 4, 8
+    x = np.arange(T * H, dtype=np.float32).reshape(T, H) + 1
+    W = np.zeros((E, H), dtype=np.float32)
+    W[2, 5] = 0.5
+    got = O.router_logits(x, W)
+    want = np.zeros((T, E), dtype=np.float32)
+    want[:, 2] = x[:, 5] * 0.5
+    assert np.array_equal(got, want)
