@@ -4,13 +4,13 @@
 // Reading the selected experts' weights is what decode time goes to ("Strata
 // 实测 ...", kefong.net, section 四: a higher expert-cache hit rate gave +39 %
 // decode; "RTX PRO 4500 ...", section 最重要机制, item 3: verify windows spread
-// the weight reads over several tokens).  Both kernels therefore put every
+// the weight reads over several tokens).  The kernels therefore put every
 // weight load of a wave in flight before anything waits on it, stream each
 // 16x256 tile with one 16-byte load of codes and one of scales per lane, and
 // keep all arithmetic on the MFMA (tokens are the M dimension, padded to 16)
-// so the cost per weight does not grow with T.  Each kernel is sized to run
-// in a single round of workgroups (every workgroup resident at once): on this
-// hardware a kernel's time is its slowest workgroup's dependent-latency chain.
+// so the cost per weight does not grow with T.  On this hardware a kernel's
+// time is its slowest workgroup's dependent-latency chain, so the layer is
+// built to have as few links in that chain as possible.
 //
 // Slots: the distinct selected experts in first-occurrence order of topk_ids,
 // then the shared expert.  Pairs: routed pair p = t*k + j, shared pair T*k + t;
@@ -18,15 +18,23 @@
 //
 // Kernel 1 (gate/up + SwiGLU): one workgroup of 8 waves per (slot, two 16-row
 //   tiles of I); 4 waves per row tile split the H/256 K tiles.  Each
-//   workgroup derives the slots from topk_ids with ballots (<= 64 ids), issues
-//   its weight loads, then stages x_hat * s_t as fp16 in LDS (s_t: per-token
-//   power of two, max |x_hat s_t| in [0.5, 1)).  h~[pair][I] (fp16) =
-//   w * silu(g) * u * s_t^2.
+//   workgroup derives the slots from topk_ids (or takes the top-k of the
+//   logits itself), issues its weight loads, then stages x_hat * s_t as fp16
+//   in LDS (s_t: per-token power of two, max |x_hat s_t| in [0.5, 1)).
+//   h~[pair][I] (fp16) = w * silu(g) * u * s_t^2.
 // Kernel 2 (down + weighted combine + shared + residual): one workgroup of 8
-//   waves per 16-row tile of H; the waves split the slots.  h~ is staged in
-//   LDS once per workgroup; the MFMA accumulator sums W_down(e) h~(e) over all
-//   slots, so the weighted combine is exact and in a fixed order;
-//   out = acc / s_t^2 (+ residual).
+//   waves per 16-row tile of H; work items (slot, K tile) of all slots, item i
+//   to wave i % 8.  h~ is staged in LDS once per workgroup; the MFMA
+//   accumulator sums W_down(e) h~(e) over all slots, so the weighted combine
+//   is exact and in a fixed order; out = acc / s_t^2 (+ residual).
+// The two halves meet at a kernel boundary.  A grid-wide barrier inside one
+// kernel was measured as no faster on this device: with the workgroups spread
+// over 8 XCDs every cross-XCD signal is a round trip through memory, and the
+// best barrier (per-workgroup flags, no shared polling address) took 3.5-5 us
+// from the last arrival at 264 workgroups -- more than the gap between two
+// kernels.
+#include <mutex>
+
 #include "launch.h"
 #include "q2_device.h"
 #include "topk_device.h"
@@ -38,10 +46,17 @@ namespace {
 
 constexpr int kMaxSlots = MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK + 1;                   // 65
 constexpr int kMaxPairs = MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK + MOE_MAX_DECODE_TOKENS; // 68
-constexpr int kThreads = 512;            // 8 waves
+constexpr int kThreads = 512;            // 8 waves (kernel 2)
 constexpr int kWaves = kThreads / kWave;
-constexpr int kXRegChunks = 3;           // x chunks of 8 kept in registers (T*H <= 12288)
-constexpr int kDownBatch = 8;            // weight tiles in flight per wave in kernel 2
+constexpr int kXRegValues = 12288;       // x is kept in registers when T*H <= this
+
+// x chunks of 8 values per thread kept in registers when NT threads less
+// the (up to 4) routing waves hold x
+template <int NT>
+constexpr int x_reg_chunks() {
+  return (kXRegValues / 8 + NT - kWave * MOE_MAX_DECODE_TOKENS - 1) / (NT - kWave * MOE_MAX_DECODE_TOKENS);
+}
+constexpr int kDownBatch = 8;            // down tiles in flight per wave in kernel 2
 constexpr int kDownStage = 4;            // h~ chunks per thread loaded ahead in kernel 2
 
 struct DecodeHeader {          // start of the workspace, written by block 0 of kernel 1
@@ -60,6 +75,10 @@ struct DecodeSlots {
   int pidx[kMaxSlots][MOE_MAX_DECODE_TOKENS];
   float wpair[kMaxPairs];
 };
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+}
 
 // Wave 0: slots (distinct valid ids in first-occurrence order, then the
 // shared expert), the pair of every (slot, token) and every pair's weight.
@@ -98,6 +117,13 @@ __device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e)
   return e < 0 ? L.shared : L.experts + static_cast<int64_t>(e) * L.stride;
 }
 
+// Bytes of one I x H (or H x I) matrix in tile records.
+__device__ __forceinline__ uint32_t matrix_bytes(int H, int I) {
+  return static_cast<uint32_t>(I) * static_cast<uint32_t>(H) / 16u * 5u;
+}
+
+// ------------------------------------------------------------ x and routing --
+
 // x chunk c (8 consecutive values of the row-major [T][H] input): raw load
 // (two 16-byte vectors; the second is unused for bf16) and conversion.
 template <bool BF16>
@@ -123,96 +149,57 @@ __device__ __forceinline__ void x_raw_to_float(const u32x4 (&r)[2], float (&v)[8
   }
 }
 
-// K tiles per wave: ceil(H / 256 / 4); x dtype; RPER = 0 when topk_ids and
-// topk_w are given, else the per-lane expert bound of the in-kernel top-k of
-// `logits` (every workgroup routes the T tokens itself, waves 0..T-1 one
-// token each; block 0 also writes the routing out when asked).
-template <int KTW, bool BF16, int RPER>
-__global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
-    LayerArgs L, const void* __restrict__ x, int T, const int32_t* __restrict__ ids,
-    const float* __restrict__ w, const float* __restrict__ logits, int32_t* __restrict__ ids_out,
-    float* __restrict__ w_out, int k, int prenorm, uint8_t* __restrict__ ws) {
-  extern __shared__ __align__(16) uint8_t dyn[];
-  _Float16* xs = reinterpret_cast<_Float16*>(dyn);              // [T][H]
-  __shared__ DecodeSlots S;
-  __shared__ int32_t s_rid[RPER > 0 ? MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK : 1];
-  __shared__ float s_rw[RPER > 0 ? MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK : 1];
-  __shared__ float s_stat[kWaves][MOE_MAX_DECODE_TOKENS][2];
-  __shared__ float s_mul[MOE_MAX_DECODE_TOKENS];
-  __shared__ float s_uns[MOE_MAX_DECODE_TOKENS];
-  __shared__ f32x4 s_red[kWaves][2][16];
-
-  const int H = L.H, I = L.I;
-  const int RP = I / (2 * kTileRows);        // row-tile pairs
-  const int slot = blockIdx.x / RP;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
-  const int rt = 2 * (blockIdx.x % RP) + (wid >> 2);
-  const int kq = wid & 3;
-
-  // x into registers first (independent of the routing)
-  const int nch = T * H / 8;
-  const bool xreg = nch <= kThreads * kXRegChunks;
-  u32x4 xr[kXRegChunks][2];
+// x into registers first (independent of the routing) when it fits: thread
+// xt of nxt takes chunks xt, xt + nxt, ... (at most XC).
+template <bool BF16, int XC>
+__device__ __forceinline__ void issue_x(const void* x, int nch, bool xreg, u32x4 (&xr)[XC][2],
+                                        int xt, int nxt) {
   if (xreg) {
 #pragma unroll
-    for (int q = 0; q < kXRegChunks; ++q)
-      load_x_raw<BF16>(x, min(static_cast<int>(threadIdx.x) + kThreads * q, nch - 1), xr[q]);
+    for (int q = 0; q < XC; ++q) load_x_raw<BF16>(x, min(xt + nxt * q, nch - 1), xr[q]);
   }
+}
 
-  if constexpr (RPER > 0) {
-    if (wid < T) {
-      int my_e;
-      float l;
-      topk_one_token<RPER>(logits + static_cast<size_t>(wid) * L.E, L.E, k, lane, my_e, l);
-      const float wt = topk_weight(l, k, lane);
-      if (lane < k) {
-        s_rid[wid * k + lane] = my_e;
-        s_rw[wid * k + lane] = wt;
-        if (blockIdx.x == 0 && ids_out) {
-          ids_out[wid * k + lane] = my_e;
-          w_out[wid * k + lane] = wt;
-        }
+// Top-k of the logits, waves 0..T-1 one token each, into s_rid / s_rw
+// (block 0 also writes it to ids_out / w_out when given).
+template <int RPER>
+__device__ __forceinline__ void route_topk_waves(const LayerArgs& L, int T, int k,
+                                                 const float* logits, int32_t* ids_out,
+                                                 float* w_out, int32_t* s_rid, float* s_rw) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = wave_id();
+  if (wid < T) {
+    int my_e;
+    float l;
+    topk_one_token<RPER>(logits + static_cast<size_t>(wid) * L.E, L.E, k, lane, my_e, l);
+    const float wt = topk_weight(l, k, lane);
+    if (lane < k) {
+      s_rid[wid * k + lane] = my_e;
+      s_rw[wid * k + lane] = wt;
+      if (blockIdx.x == 0 && ids_out) {
+        ids_out[wid * k + lane] = my_e;
+        w_out[wid * k + lane] = wt;
       }
     }
-    __syncthreads();
-    if (wid == 0) build_slots(s_rid, s_rw, T, k, L.E, L.shared != nullptr, S);
-  } else {
-    if (wid == 0) build_slots(ids, w, T, k, L.E, L.shared != nullptr, S);
   }
-  __syncthreads();
-  const bool active = slot < S.n;
-  if (!active && blockIdx.x != 0) return;    // block 0 always writes the header
+}
 
-  // ---- weight loads of this row tile (gate and up), K split over 4 waves.
-  // Issued on every path (an inactive block 0 reads expert 0's tiles and
-  // drops them): the waits on x below then count these loads as still
-  // outstanding instead of draining them first.
-  const int KT = H / kTileCols;
-  const int64_t mat = static_cast<int64_t>(I) * H * 5 / 16;
-  u32x4 cg[KTW], sg[KTW], cu[KTW], su[KTW];
-  {
-    const uint8_t* gate = expert_base(L, active ? S.expert[slot] : 0) +
-                          static_cast<int64_t>(rt) * KT * kTileBytes;
-    const uint8_t* up = gate + mat;
-#pragma unroll
-    for (int i = 0; i < KTW; ++i) {
-      const int kt = min(kq + 4 * i, KT - 1);
-      cg[i] = load_codes(gate + kt * kTileBytes, lane);
-      cu[i] = load_codes(up + kt * kTileBytes, lane);
-      sg[i] = load_scales(gate + kt * kTileBytes, lane);
-      su[i] = load_scales(up + kt * kTileBytes, lane);
-    }
-  }
-
-  // ---- per-token statistics and the fp16 copy of x_hat * s_t ------------
-  // (token of chunk c: c / (H/8), by comparisons; T <= 4)
+// Per-token pre-norm multiplier rmul (1 without the pre-norm) and fp16
+// normaliser smul: every wave writes its partial sums of x^2 and max |x| to
+// s_stat (token_partials), and after a barrier every thread derives the
+// multipliers from them itself (token_derive).
+// (token of chunk c: c / (H/8), by comparisons; T <= 4)
+template <bool BF16, int XC>
+__device__ void token_partials(const void* x, int T, int H, bool xreg, const u32x4 (&xr)[XC][2],
+                               float (*s_stat)[MOE_MAX_DECODE_TOKENS][2], int xt, int nxt) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = wave_id();
+  const int nch = T * H / 8;
   const int cpt = H / 8;
-  auto token_of = [&](int c) { return (c >= cpt) + (c >= 2 * cpt) + (c >= 3 * cpt); };
   float ss[MOE_MAX_DECODE_TOKENS] = {0.f, 0.f, 0.f, 0.f};
   float mx[MOE_MAX_DECODE_TOKENS] = {0.f, 0.f, 0.f, 0.f};
   auto accum = [&](int c, const float (&v)[8]) {
-    const int t = token_of(c);
+    const int t = (c >= cpt) + (c >= 2 * cpt) + (c >= 3 * cpt);
     float a = 0.0f, b = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) { a += v[i] * v[i]; b = fmaxf(b, fabsf(v[i])); }
@@ -224,8 +211,8 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
   };
   if (xreg) {
 #pragma unroll
-    for (int q = 0; q < kXRegChunks; ++q) {
-      const int c = threadIdx.x + kThreads * q;
+    for (int q = 0; q < XC; ++q) {
+      const int c = xt + nxt * q;
       if (c < nch) {
         float v[8];
         x_raw_to_float<BF16>(xr[q], v);
@@ -233,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
       }
     }
   } else {
-    for (int c = threadIdx.x; c < nch; c += kThreads) {
+    for (int c = xt; c < nch; c += nxt) {
       u32x4 r[2];
       float v[8];
       load_x_raw<BF16>(x, c, r);
@@ -246,25 +233,35 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
     const float b = wave_max(mx[t]);
     if (lane == 0) { s_stat[wid][t][0] = a; s_stat[wid][t][1] = b; }
   }
-  __syncthreads();
-  // every thread derives the per-token multipliers itself (no second barrier)
-  float rmul[MOE_MAX_DECODE_TOKENS], smul[MOE_MAX_DECODE_TOKENS];
+}
+
+template <int NW>
+__device__ __forceinline__ void token_derive(int T, int H, int prenorm,
+                                             const float (*s_stat)[MOE_MAX_DECODE_TOKENS][2],
+                                             float (&rmul)[MOE_MAX_DECODE_TOKENS],
+                                             float (&smul)[MOE_MAX_DECODE_TOKENS]) {
 #pragma unroll
   for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
     float a = 0.0f, b = 0.0f;
     if (t < T) {
 #pragma unroll
-      for (int q = 0; q < kWaves; ++q) { a += s_stat[q][t][0]; b = fmaxf(b, s_stat[q][t][1]); }
+      for (int q = 0; q < NW; ++q) { a += s_stat[q][t][0]; b = fmaxf(b, s_stat[q][t][1]); }
     }
     rmul[t] = prenorm ? 1.0f / sqrtf(a / static_cast<float>(H) + 1e-6f) : 1.0f;
     smul[t] = pow2_normaliser(b * rmul[t]);
   }
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) { s_mul[t] = rmul[t]; s_uns[t] = smul[t]; }
-  }
+}
+
+// fp16 copy of x_hat * s_t into LDS ([T][H]).
+template <bool BF16, int XC>
+__device__ void stage_x(const void* x, int T, int H, bool xreg, const u32x4 (&xr)[XC][2],
+                        const float (&rmul)[MOE_MAX_DECODE_TOKENS],
+                        const float (&smul)[MOE_MAX_DECODE_TOKENS], _Float16* xs, int xt,
+                        int nxt) {
+  const int nch = T * H / 8;
+  const int cpt = H / 8;
   auto put = [&](int c, const float (&v)[8]) {
-    const int t = token_of(c);
+    const int t = (c >= cpt) + (c >= 2 * cpt) + (c >= 3 * cpt);
     float r = rmul[0], s = smul[0];
 #pragma unroll
     for (int q = 1; q < MOE_MAX_DECODE_TOKENS; ++q) { r = (q == t) ? rmul[q] : r; s = (q == t) ? smul[q] : s; }
@@ -275,8 +272,8 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
   };
   if (xreg) {
 #pragma unroll
-    for (int q = 0; q < kXRegChunks; ++q) {
-      const int c = threadIdx.x + kThreads * q;
+    for (int q = 0; q < XC; ++q) {
+      const int c = xt + nxt * q;
       if (c < nch) {
         float v[8];
         x_raw_to_float<BF16>(xr[q], v);
@@ -284,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
       }
     }
   } else {
-    for (int c = threadIdx.x; c < nch; c += kThreads) {
+    for (int c = xt; c < nch; c += nxt) {
       u32x4 r[2];
       float v[8];
       load_x_raw<BF16>(x, c, r);
@@ -292,21 +289,47 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
       put(c, v);
     }
   }
-  if (blockIdx.x == 0) {
-    DecodeHeader* hdr = reinterpret_cast<DecodeHeader*>(ws);
-    if (threadIdx.x == 0) {
-#pragma unroll
-      for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t)
-        if (t < T) hdr->unscale[t] = 1.0f / smul[t];
-    }
-    for (int i = threadIdx.x; i < S.n * MOE_MAX_DECODE_TOKENS; i += kThreads)
-      (&hdr->pidx[0][0])[i] = (&S.pidx[0][0])[i];
-    if (threadIdx.x < S.n) hdr->expert[threadIdx.x] = S.expert[threadIdx.x];
-    if (threadIdx.x == 0) hdr->n_slots = S.n;
-  }
-  __syncthreads();
-  if (!active) return;
+}
 
+// ---------------------------------------------------------------- gate/up --
+
+template <int KTW>
+struct GateUpTiles {
+  u32x4 cg[KTW], sg[KTW], cu[KTW], su[KTW];
+};
+
+// Gate and up tiles (rt, kq + 4i) of one expert for this wave (K tiles
+// clamped).  With live == false the resource has size zero: the loads are
+// still issued (so later waits count them exactly) but touch no memory and
+// return zeros.
+template <int KTW>
+__device__ __forceinline__ void load_gateup(const uint8_t* expert, bool live, int H, int I, int rt,
+                                            int kq, int lane, GateUpTiles<KTW>& R) {
+  const int KT = H / kTileCols;
+  const uint32_t mat = __builtin_amdgcn_readfirstlane(matrix_bytes(H, I));
+  const __amdgpu_buffer_rsrc_t r = expert_rsrc(expert, live ? 2u * mat : 0u);
+  const uint32_t row0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt * KT) * kTileBytes);
+#pragma unroll
+  for (int i = 0; i < KTW; ++i) {
+    const uint32_t off = row0 + static_cast<uint32_t>(min(kq + 4 * i, KT - 1)) * kTileBytes;
+    R.cg[i] = load_codes(r, off, lane);
+    R.cu[i] = load_codes(r, off + mat, lane);
+    R.sg[i] = load_scales(r, off, lane);
+    R.su[i] = load_scales(r, off + mat, lane);
+  }
+}
+
+// Gate/up products of one row tile from LDS x (xs), K split over a group of
+// 4 waves, summed in LDS in wave order; the group's first wave writes h~ of
+// every (slot, token) pair (not for an inactive group).
+template <int KTW>
+__device__ void gateup_compute(const GateUpTiles<KTW>& R, const _Float16* xs, int T, int H, int I,
+                               int rt, int kq, int slot, bool active, const DecodeSlots& S,
+                               const float (&smul)[MOE_MAX_DECODE_TOKENS],
+                               f32x4 (*s_red)[2][16], _Float16* hout) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = wave_id();
+  const int KT = H / kTileCols;
   const int m = lane & 15, g = lane >> 4;
   f32x4 acc_g = {0.f, 0.f, 0.f, 0.f}, acc_u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -317,22 +340,22 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
       for (int j = 0; j < 8; ++j) {
         f16x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
         if (m < T) a = *reinterpret_cast<const f16x8*>(xs + m * H + kt * kTileCols + 32 * j + 8 * g);
-        acc_g = mfma16(a, tile_block_weights(cg[i], sg[i], j), acc_g);
-        acc_u = mfma16(a, tile_block_weights(cu[i], su[i], j), acc_u);
+        acc_g = mfma16(a, tile_block_weights(R.cg[i], R.sg[i], j), acc_g);
+        acc_u = mfma16(a, tile_block_weights(R.cu[i], R.su[i], j), acc_u);
       }
     }
   }
   if (lane < 16) { s_red[wid][0][lane] = acc_g; s_red[wid][1][lane] = acc_u; }
   __syncthreads();
-  if (kq == 0 && lane < 16) {
+  if (active && kq == 0 && lane < 16) {
     f32x4 G = s_red[wid][0][lane], U = s_red[wid][1][lane];
     for (int q = 1; q < 4; ++q) { G += s_red[wid + q][0][lane]; U += s_red[wid + q][1][lane]; }
-    _Float16* hout = reinterpret_cast<_Float16*>(ws + sizeof(DecodeHeader));
     const int row = rt * kTileRows + lane;
-    for (int t = 0; t < T; ++t) {
-      const int p = S.pidx[slot][t];
+#pragma unroll
+    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
+      const int p = t < T ? S.pidx[slot][t] : -1;
       if (p < 0) continue;
-      const float s = s_uns[t];
+      const float s = smul[t];
       const float u = 1.0f / s;
       const float gv = G[t] * u, uv = U[t] * u;
       const float h = S.wpair[p] * silu(gv) * uv * (s * s);
@@ -341,41 +364,177 @@ __global__ __launch_bounds__(kThreads) void decode_gateup_kernel(
   }
 }
 
-struct GateupArgs {
-  const void* x;
-  int T;
-  const int32_t* ids;
-  const float* w;
-  const float* logits;
-  int32_t* ids_out;
-  float* w_out;
-  int k, prenorm;
-  uint8_t* ws;
+// ------------------------------------------------------------------- down --
+
+template <int DB>
+struct DownTiles {
+  u32x4 c[DB], s[DB];
 };
 
-template <int KTW, bool BF16, int RPER>
-hipError_t launch_gateup3(const LayerArgs& L, int grid, uint32_t lds, hipStream_t s,
-                          const GateupArgs& a) {
-  return launch_kernel(K_DECODE_GATEUP, decode_gateup_kernel<KTW, BF16, RPER>, dim3(grid),
-                       dim3(kThreads), lds, s, L, a.x, a.T, a.ids, a.w, a.logits, a.ids_out,
-                       a.w_out, a.k, a.prenorm, a.ws);
-}
-
-template <int KTW>
-hipError_t launch_gateup(const LayerArgs& L, int grid, size_t lds, hipStream_t s, int x_bf16,
-                         const GateupArgs& a) {
-  const uint32_t l = static_cast<uint32_t>(lds);
-  const int rper = a.logits == nullptr ? 0 : (L.E <= 8 * kWave ? 8 : 16);
-  if (x_bf16) {
-    if (rper == 0) return launch_gateup3<KTW, true, 0>(L, grid, l, s, a);
-    if (rper == 8) return launch_gateup3<KTW, true, 8>(L, grid, l, s, a);
-    return launch_gateup3<KTW, true, 16>(L, grid, l, s, a);
+// Work items of down row tile rt: item i = (slot i / KTd, K tile i % KTd),
+// wave w takes items w, w + 8, ...; this loads the wave's items j0..j0+DB-1
+// (an item past nitems gets a zero-size resource: issued, no memory touched).
+template <int DB>
+__device__ __forceinline__ void load_down(const LayerArgs& L, const int* expert, int nitems, int KTd,
+                                          int rt, int j0, int lane, DownTiles<DB>& D) {
+  const int wid = wave_id();
+  const uint32_t mat = __builtin_amdgcn_readfirstlane(matrix_bytes(L.H, L.I));
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    const int wi = wid + kWaves * (j0 + b);
+    const bool live = wi < nitems;
+    const int slot = live ? wi / KTd : 0;
+    const int kt = live ? wi % KTd : 0;
+    const int e = __builtin_amdgcn_readfirstlane(live ? expert[slot] : 0);
+    const __amdgpu_buffer_rsrc_t r = expert_rsrc(expert_base(L, e), live ? 3u * mat : 0u);
+    const uint32_t off = __builtin_amdgcn_readfirstlane(
+        2u * mat + static_cast<uint32_t>(rt * KTd + kt) * kTileBytes);
+    D.c[b] = load_codes(r, off, lane);
+    D.s[b] = load_scales(r, off, lane);
   }
-  if (rper == 0) return launch_gateup3<KTW, false, 0>(L, grid, l, s, a);
-  if (rper == 8) return launch_gateup3<KTW, false, 8>(L, grid, l, s, a);
-  return launch_gateup3<KTW, false, 16>(L, grid, l, s, a);
 }
 
+template <int DB>
+__device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int KTd, int j0,
+                                         int lane, const _Float16* hsrc,
+                                         const int (*pidx)[MOE_MAX_DECODE_TOKENS], int T, int I,
+                                         f32x4& acc) {
+  const int wid = wave_id();
+  const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    const int wi = wid + kWaves * (j0 + b);
+    if (wi < nitems) {
+      const int slot = wi / KTd;
+      const int kt = wi % KTd;
+      const int p = (m < T) ? pidx[slot][m] : -1;
+      const _Float16* arow = hsrc + static_cast<size_t>(p < 0 ? 0 : p) * I + kt * kTileCols + 8 * g;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        f16x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (p >= 0) a = *reinterpret_cast<const f16x8*>(arow + 32 * j);
+        acc = mfma16(a, tile_block_weights(D.c[b], D.s[b], j), acc);
+      }
+    }
+  }
+}
+
+// Sum of the 8 waves' accumulators (wave order) and the output rows of tile
+// rt: out = acc * unscale^2 (+ residual); NaN rows when `poison`.
+__device__ void down_store(const f32x4& acc, f32x4 (*s_red)[16], int rt, int T, int H,
+                           const float (&unscale)[MOE_MAX_DECODE_TOKENS], const void* residual,
+                           void* out, int out_bf16, bool poison) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = wave_id();
+  if (lane < 16) s_red[wid][lane] = acc;
+  __syncthreads();
+  if (wid == 0 && lane < 16) {
+    f32x4 Y = s_red[0][lane];
+    for (int q = 1; q < kWaves; ++q) Y += s_red[q][lane];
+    const int row = rt * kTileRows + lane;
+#pragma unroll
+    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
+      if (t >= T) break;
+      const float u = unscale[t];
+      float v = Y[t] * (u * u);
+      if (poison) v = __builtin_nanf("");
+      const size_t o = static_cast<size_t>(t) * H + row;
+      if (out_bf16) {
+        if (residual) v += bf16_to_float(static_cast<const uint16_t*>(residual)[o]);
+        static_cast<uint16_t*>(out)[o] = float_to_bf16(v);
+      } else {
+        if (residual) v += static_cast<const float*>(residual)[o];
+        static_cast<float*>(out)[o] = v;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ the kernels --
+
+// Kernel 1: RTW groups of 4 waves; group q of block b takes row tile
+// g = b + gridDim.x * q of the flattened (slot, row tile) list, so that one
+// block per CU covers all of them (a second block on a CU would double that
+// CU's share and finish last).  Block 0 also writes the header that kernel 2
+// reads.
+template <int KTW, bool BF16, int RPER, int RTW>
+__global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
+    LayerArgs L, const void* __restrict__ x, int T, const int32_t* __restrict__ ids,
+    const float* __restrict__ w, const float* __restrict__ logits, int32_t* __restrict__ ids_out,
+    float* __restrict__ w_out, int k, int prenorm, uint8_t* __restrict__ ws) {
+  constexpr int NT = 256 * RTW, NW = 4 * RTW, XC = x_reg_chunks<NT>();
+  extern __shared__ __align__(16) uint8_t dyn[];
+  _Float16* xs = reinterpret_cast<_Float16*>(dyn);              // [T][H]
+  __shared__ DecodeSlots S;
+  __shared__ int32_t s_rid[RPER > 0 ? MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK : 1];
+  __shared__ float s_rw[RPER > 0 ? MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK : 1];
+  __shared__ float s_stat[NW][MOE_MAX_DECODE_TOKENS][2];
+  __shared__ f32x4 s_red[NW][2][16];
+
+  const int H = L.H, I = L.I;
+  const int RTI = I / kTileRows;                 // row tiles of one gate (or up) matrix
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = wave_id();
+  const int kq = wid & 3;
+  const int g = blockIdx.x + gridDim.x * (wid >> 2);
+
+  // Waves 0..T-1 route (one token each); meanwhile the other waves load x,
+  // sum its statistics and, after one barrier, stage its fp16 copy while
+  // wave 0 builds the slots.  So x is ready in LDS when the weight loads are
+  // issued, and the MFMA loop can take each tile as it arrives.
+  const int nch = T * H / 8;
+  const int xt = static_cast<int>(threadIdx.x) - kWave * T;   // x thread (waves T..)
+  const int nxt = NT - kWave * T;
+  const bool xreg = nch <= nxt * XC;
+  u32x4 xr[XC][2];
+  if (wid < T) {
+    if (lane < MOE_MAX_DECODE_TOKENS) { s_stat[wid][lane][0] = 0.0f; s_stat[wid][lane][1] = 0.0f; }
+    if constexpr (RPER > 0) {
+      route_topk_waves<RPER>(L, T, k, logits, ids_out, w_out, s_rid, s_rw);
+    } else {
+      if (wid == 0) build_slots(ids, w, T, k, L.E, L.shared != nullptr, S);
+    }
+  } else {
+    issue_x<BF16, XC>(x, nch, xreg, xr, xt, nxt);
+    token_partials<BF16, XC>(x, T, H, xreg, xr, s_stat, xt, nxt);
+  }
+  __syncthreads();
+  float rmul[MOE_MAX_DECODE_TOKENS], smul[MOE_MAX_DECODE_TOKENS];
+  token_derive<NW>(T, H, prenorm, s_stat, rmul, smul);
+  if (wid < T) {
+    if constexpr (RPER > 0) {
+      if (wid == 0) build_slots(s_rid, s_rw, T, k, L.E, L.shared != nullptr, S);
+    }
+  } else {
+    stage_x<BF16, XC>(x, T, H, xreg, xr, rmul, smul, xs, xt, nxt);
+  }
+  __syncthreads();
+  const int n_rows = S.n * RTI;
+  if (static_cast<int>(blockIdx.x) >= n_rows && blockIdx.x != 0) return;   // no active group
+  const bool active = g < n_rows;
+  const int slot = active ? g / RTI : 0;
+  const int rt = active ? g % RTI : 0;
+
+  GateUpTiles<KTW> R;
+  load_gateup<KTW>(expert_base(L, active ? S.expert[slot] : 0), active, H, I, rt, kq, lane, R);
+  if (blockIdx.x == 0) {
+    DecodeHeader* hdr = reinterpret_cast<DecodeHeader*>(ws);
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t)
+        if (t < T) hdr->unscale[t] = 1.0f / smul[t];
+    }
+    for (int i = threadIdx.x; i < S.n * MOE_MAX_DECODE_TOKENS; i += NT)
+      (&hdr->pidx[0][0])[i] = (&S.pidx[0][0])[i];
+    if (threadIdx.x < S.n) hdr->expert[threadIdx.x] = S.expert[threadIdx.x];
+    if (threadIdx.x == 0) hdr->n_slots = S.n;
+  }
+  if (static_cast<int>(blockIdx.x) >= n_rows) return;
+  gateup_compute<KTW>(R, xs, T, H, I, rt, kq, slot, active, S, smul, s_red,
+                      reinterpret_cast<_Float16*>(ws + sizeof(DecodeHeader)));
+}
+
+// Kernel 2: down row tile blockIdx.x.
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     LayerArgs L, int T, int k, const void* __restrict__ residual, void* __restrict__ out,
     int out_bf16, const uint8_t* __restrict__ ws, int stage_lds) {
@@ -384,15 +543,14 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   __shared__ int s_expert[kMaxSlots];
   __shared__ int s_pidx[kMaxSlots][MOE_MAX_DECODE_TOKENS];
   __shared__ int s_n;
+  __shared__ float s_uns[MOE_MAX_DECODE_TOKENS];
   __shared__ f32x4 s_red[kWaves][16];
   const DecodeHeader* hdr = reinterpret_cast<const DecodeHeader*>(ws);
   const _Float16* hin = reinterpret_cast<const _Float16*>(ws + sizeof(DecodeHeader));
-  const int H = L.H, I = L.I;
-  const int KT = I / kTileCols;
+  const int I = L.I;
+  const int KTd = I / kTileCols;
   const int rt = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
-  const int m = lane & 15, g = lane >> 4;
 
   // h~ of all pairs: its layout does not depend on the header, so these
   // loads go first (always issued, so that later waits count them exactly)
@@ -403,37 +561,22 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     hreg[q] = *reinterpret_cast<const u32x4*>(hin + 8 * min(static_cast<int>(threadIdx.x) + kThreads * q, hch - 1));
 
   {
-    // the three header loads are issued together (clamped, unconditional)
+    // the header loads are issued together (clamped, unconditional)
     const int i = threadIdx.x;
     const int ev = hdr->expert[min(i, kMaxSlots - 1)];
     const int pv = (&hdr->pidx[0][0])[min(i, kMaxSlots * MOE_MAX_DECODE_TOKENS - 1)];
     const int nv = hdr->n_slots;
+    const float uv = hdr->unscale[min(i, MOE_MAX_DECODE_TOKENS - 1)];
     if (i < kMaxSlots) s_expert[i] = ev;
     if (i < kMaxSlots * MOE_MAX_DECODE_TOKENS) (&s_pidx[0][0])[i] = pv;
     if (i == 0) s_n = nv;
+    if (i < MOE_MAX_DECODE_TOKENS) s_uns[i] = uv;
   }
   __syncthreads();
-  const int n_slots = s_n;
-  const int64_t mat = static_cast<int64_t>(I) * H * 5 / 16;
+  const int nitems = s_n * KTd;
 
-  // records of this wave: (slot, kt) for slots wid, wid+8, ...
-  const int nwork = ((n_slots - wid + kWaves - 1) / kWaves) * KT;
-  // (a wave without work reads expert 0's first record and drops it, so the
-  // first batch is issued on every path)
-  auto rec_of = [&](int wi) {
-    wi = max(min(wi, nwork - 1), 0);
-    const int slot = wid + kWaves * (wi / KT);
-    const int kt = wi % KT;
-    const int e = slot < n_slots ? s_expert[slot] : 0;
-    return expert_base(L, e) + 2 * mat + (static_cast<int64_t>(rt) * KT + kt) * kTileBytes;
-  };
-  u32x4 c[kDownBatch], sc[kDownBatch];
-#pragma unroll
-  for (int b = 0; b < kDownBatch; ++b) {
-    const uint8_t* rec = rec_of(b);
-    c[b] = load_codes(rec, lane);
-    sc[b] = load_scales(rec, lane);
-  }
+  DownTiles<kDownBatch> D;
+  load_down<kDownBatch>(L, s_expert, nitems, KTd, rt, 0, lane, D);
   if (stage_lds) {
 #pragma unroll
     for (int q = 0; q < kDownStage; ++q) {
@@ -452,56 +595,91 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   }
   __syncthreads();
 
+  // h~ from LDS or from global memory: two separate calls, so that each
+  // keeps its own address space (one pointer selected between them would
+  // make every h~ read a flat load, waited for before each MFMA)
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const _Float16* hsrc = stage_lds ? hs : hin;
-  for (int b0 = 0; b0 < nwork; b0 += kDownBatch) {
-    if (b0 > 0) {
-#pragma unroll
-      for (int b = 0; b < kDownBatch; ++b) {
-        const uint8_t* rec = rec_of(b0 + b);
-        c[b] = load_codes(rec, lane);
-        sc[b] = load_scales(rec, lane);
-      }
+  const int per_wave = (nitems + kWaves - 1) / kWaves;
+  auto run = [&](const _Float16* hsrc) {
+    mma_down<kDownBatch>(D, nitems, KTd, 0, lane, hsrc, s_pidx, T, I, acc);
+    for (int j0 = kDownBatch; j0 < per_wave; j0 += kDownBatch) {
+      load_down<kDownBatch>(L, s_expert, nitems, KTd, rt, j0, lane, D);
+      mma_down<kDownBatch>(D, nitems, KTd, j0, lane, hsrc, s_pidx, T, I, acc);
     }
+  };
+  if (stage_lds) run(hs);
+  else run(hin);
+  float uns[MOE_MAX_DECODE_TOKENS];
 #pragma unroll
-    for (int b = 0; b < kDownBatch; ++b) {
-      const int wi = b0 + b;
-      if (wi < nwork) {
-        const int slot = wid + kWaves * (wi / KT);
-        const int kt = wi % KT;
-        const int p = (m < T) ? s_pidx[slot][m] : -1;
-        const _Float16* arow = hsrc + static_cast<size_t>(p < 0 ? 0 : p) * I + kt * kTileCols + 8 * g;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          f16x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
-          if (p >= 0) a = *reinterpret_cast<const f16x8*>(arow + 32 * j);
-          acc = mfma16(a, tile_block_weights(c[b], sc[b], j), acc);
-        }
-      }
-    }
-  }
-  if (lane < 16) s_red[wid][lane] = acc;
-  __syncthreads();
-  if (wid == 0 && lane < 16) {
-    f32x4 Y = s_red[0][lane];
-    for (int q = 1; q < kWaves; ++q) Y += s_red[q][lane];
-    const int row = rt * kTileRows + lane;
-    for (int t = 0; t < T; ++t) {
-      const float u = hdr->unscale[t];
-      float v = Y[t] * (u * u);
-      const size_t o = static_cast<size_t>(t) * H + row;
-      if (out_bf16) {
-        if (residual) v += bf16_to_float(static_cast<const uint16_t*>(residual)[o]);
-        static_cast<uint16_t*>(out)[o] = float_to_bf16(v);
-      } else {
-        if (residual) v += static_cast<const float*>(residual)[o];
-        static_cast<float*>(out)[o] = v;
-      }
-    }
-  }
+  for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) uns[t] = s_uns[t];
+  down_store(acc, s_red, rt, T, L.H, uns, residual, out, out_bf16, false);
 }
 
-constexpr size_t kDownLdsLimit = 96 * 1024;
+// -------------------------------------------------------------- launching --
+
+struct DecodeArgs {
+  const void* x;
+  int T;
+  const int32_t* ids;
+  const float* w;
+  const float* logits;
+  int32_t* ids_out;
+  float* w_out;
+  int k, prenorm;
+  const void* residual;
+  void* out;
+  int out_bf16;
+  uint8_t* ws;
+};
+
+constexpr size_t kHStageLimit = 96 * 1024;   // largest h~ staged in LDS
+
+template <int KTW, bool BF16, int RPER, int RTW>
+hipError_t launch_gateup4(const LayerArgs& L, int grid, uint32_t lds, hipStream_t s,
+                          const DecodeArgs& a) {
+  return launch_kernel(K_DECODE_GATEUP, decode_gateup_kernel<KTW, BF16, RPER, RTW>, dim3(grid),
+                       dim3(256 * RTW), lds, s, L, a.x, a.T, a.ids, a.w, a.logits, a.ids_out,
+                       a.w_out, a.k, a.prenorm, a.ws);
+}
+
+// Row-tile groups per block: 2..4 while KTW <= 4 (the 16-wave block then
+// stays within 128 registers per lane), else 2.
+template <int KTW, bool BF16, int RPER>
+hipError_t launch_gateup3(const LayerArgs& L, int grid, int rtw, uint32_t lds, hipStream_t s,
+                          const DecodeArgs& a) {
+  if constexpr (KTW <= 4) {
+    if (rtw == 3) return launch_gateup4<KTW, BF16, RPER, 3>(L, grid, lds, s, a);
+    if (rtw == 4) return launch_gateup4<KTW, BF16, RPER, 4>(L, grid, lds, s, a);
+  }
+  return launch_gateup4<KTW, BF16, RPER, 2>(L, grid, lds, s, a);
+}
+
+template <int KTW>
+hipError_t launch_gateup(const LayerArgs& L, int grid, int rtw, uint32_t lds, int x_bf16, int rper,
+                         hipStream_t s, const DecodeArgs& a) {
+  if (x_bf16) {
+    if (rper == 0) return launch_gateup3<KTW, true, 0>(L, grid, rtw, lds, s, a);
+    if (rper == 8) return launch_gateup3<KTW, true, 8>(L, grid, rtw, lds, s, a);
+    return launch_gateup3<KTW, true, 16>(L, grid, rtw, lds, s, a);
+  }
+  if (rper == 0) return launch_gateup3<KTW, false, 0>(L, grid, rtw, lds, s, a);
+  if (rper == 8) return launch_gateup3<KTW, false, 8>(L, grid, rtw, lds, s, a);
+  return launch_gateup3<KTW, false, 16>(L, grid, rtw, lds, s, a);
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::mutex mu;
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> g(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 }  // namespace
 
@@ -517,31 +695,41 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
                          int32_t* ids_out, float* w_out, int k, const void* residual,
                          void* out, int out_bf16, int prenorm, void* ws, hipStream_t s) {
   const int slots_max = T * k + (L.shared ? 1 : 0);
-  const int RP = L.I / (2 * kTileRows);
-  const size_t lds1 = static_cast<size_t>(T) * L.H * sizeof(_Float16);
+  const size_t lds_x = static_cast<size_t>(T) * L.H * sizeof(_Float16);
+  const size_t lds_h = (static_cast<size_t>(T) * k + T) * L.I * sizeof(_Float16);
+  const int stage_h = lds_h <= kHStageLimit ? 1 : 0;
   const int ktw = (L.H / kTileCols + 3) / 4;
+  const int rper = logits == nullptr ? 0 : (L.E <= 8 * kWave ? 8 : 16);
+  const DecodeArgs a{x, T, ids, w, logits, ids_out, w_out, k, prenorm, residual, out, out_bf16,
+                     static_cast<uint8_t*>(ws)};
   hipError_t e;
   {
-    const GateupArgs a{x, T, ids, w, logits, ids_out, w_out, k, prenorm, static_cast<uint8_t*>(ws)};
-    const int grid = slots_max * RP;
+    // one block per CU with 2 or 3 row-tile groups when that covers every row
+    // tile; otherwise 2 groups per block and more blocks than CUs (four
+    // groups of 16 waves measured slower than two blocks of 8 per CU)
+    const int rows = slots_max * (L.I / kTileRows);
+    const int cus = device_cus();
+    int grid = (rows + 1) / 2, rtw = 2;
+    if (cus > 0 && ktw <= 4 && grid > cus && (rows + cus - 1) / cus <= 3) {
+      grid = cus;
+      rtw = (rows + cus - 1) / cus;
+    }
+    const uint32_t lds = static_cast<uint32_t>(lds_x);
     switch (ktw) {
-      case 1: e = launch_gateup<1>(L, grid, lds1, s, x_bf16, a); break;
-      case 2: e = launch_gateup<2>(L, grid, lds1, s, x_bf16, a); break;
-      case 3: e = launch_gateup<3>(L, grid, lds1, s, x_bf16, a); break;
-      case 4: e = launch_gateup<4>(L, grid, lds1, s, x_bf16, a); break;
-      case 5: e = launch_gateup<5>(L, grid, lds1, s, x_bf16, a); break;
-      case 6: e = launch_gateup<6>(L, grid, lds1, s, x_bf16, a); break;
-      case 7: e = launch_gateup<7>(L, grid, lds1, s, x_bf16, a); break;
-      default: e = launch_gateup<8>(L, grid, lds1, s, x_bf16, a); break;
+      case 1: e = launch_gateup<1>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
+      case 2: e = launch_gateup<2>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
+      case 3: e = launch_gateup<3>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
+      case 4: e = launch_gateup<4>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
+      case 5: e = launch_gateup<5>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
+      case 6: e = launch_gateup<6>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
+      case 7: e = launch_gateup<7>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
+      default: e = launch_gateup<8>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
     }
   }
   if (e != hipSuccess) return e;
-  const size_t pairs_max = static_cast<size_t>(T) * k + T;
-  const size_t lds2 = pairs_max * L.I * sizeof(_Float16);
-  const int stage = lds2 <= kDownLdsLimit ? 1 : 0;
   return launch_kernel(K_DECODE_DOWN, decode_down_kernel, dim3(L.H / kTileRows), dim3(kThreads),
-                       static_cast<uint32_t>(stage ? lds2 : 0), s, L, T, k, residual, out,
-                       out_bf16, static_cast<const uint8_t*>(ws), stage);
+                       static_cast<uint32_t>(stage_h ? lds_h : 0), s, L, T, k, residual, out,
+                       out_bf16, static_cast<const uint8_t*>(ws), stage_h);
 }
 
 }  // namespace moeq2

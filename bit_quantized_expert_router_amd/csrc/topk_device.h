@@ -26,16 +26,35 @@ __device__ __forceinline__ float key_float(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
+// b in the lanes whose bit is set in the (wave-uniform) mask, a elsewhere:
+// one v_cndmask on a scalar lane mask.  Written out so that the compiler
+// keeps the per-round list shift as a handful of selects instead of merging
+// the rounds' selects into a position-tracking network.
+__device__ __forceinline__ uint32_t select_lanes(uint32_t a, uint32_t b, uint64_t mask) {
+  uint32_t r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(mask));
+  return r;
+}
+
+// (key, id) order of the selection: larger key first, lower id first among
+// equal keys.
+__device__ __forceinline__ bool topk_before(uint32_t ka, int ia, uint32_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
 // One token per wave.  Lane l holds experts l*per .. l*per+per-1, so a lower
-// lane always holds lower ids: each round takes the wave maximum of the lanes'
-// best keys (a DPP wavefront reduction), the lowest lane holding it wins, and
-// inside that lane the lowest position holding it is taken -- together the
-// lowest expert id among equal logits.  PER (>= per) is a compile-time bound;
-// all loads are issued before any is used (clamped, so none is conditional).
-// Lane j < k receives the id and the logit of round j.
+// lane always holds lower ids.  Each lane first sorts its PER (key, id) pairs
+// into selection order (a bitonic network, compile-time indices only); then
+// every round takes the wave maximum of the lanes' head keys (a DPP wavefront
+// reduction), the lowest lane holding it wins -- its head is the lowest id
+// among the equal keys -- and the winner shifts its list up by one.  PER
+// (>= per, a power of two) is a compile-time bound; all loads are issued
+// before any is used (clamped, so none is conditional).  Lane j < k receives
+// the id and the logit of round j.
 template <int PER>
 __device__ __forceinline__ void topk_one_token(const float* __restrict__ row, int E, int k,
                                                int lane, int& my_e, float& my_l) {
+  static_assert((PER & (PER - 1)) == 0, "PER must be a power of two");
   const int per = (E + kWave - 1) / kWave;
   float lv[PER];
   if (PER >= 4 && E == PER * kWave && (reinterpret_cast<uintptr_t>(row) & 15) == 0) {
@@ -50,30 +69,49 @@ __device__ __forceinline__ void topk_one_token(const float* __restrict__ row, in
     for (int i = 0; i < PER; ++i) lv[i] = row[min(lane * per + i, E - 1)];
   }
   uint32_t key[PER];
+  int id[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane * per + i;
     key[i] = (i < per && e < E) ? float_key(lv[i]) : 0u;
+    id[i] = e;
+  }
+  // bitonic sort into selection order (position 0 first)
+#pragma unroll
+  for (int size = 2; size <= PER; size <<= 1) {
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          // runs of `size` alternate direction; the last merge is forward
+          const bool fwd = (i & size) == 0;
+          const bool sw = fwd ? topk_before(key[j], id[j], key[i], id[i])
+                              : topk_before(key[i], id[i], key[j], id[j]);
+          const uint32_t ki = key[i], kj = key[j];
+          const int ii = id[i], ij = id[j];
+          key[i] = sw ? kj : ki; key[j] = sw ? ki : kj;
+          id[i] = sw ? ij : ii;  id[j] = sw ? ii : ij;
+        }
+      }
+    }
   }
   my_e = 0;
   uint32_t my_key = 0;
   for (int j = 0; j < k; ++j) {
-    uint32_t best = key[0];
-    int pick = 0;
-#pragma unroll
-    for (int i = 1; i < PER; ++i) {
-      const bool gt = key[i] > best;   // strict: the first position wins ties
-      best = gt ? key[i] : best;
-      pick = gt ? i : pick;
-    }
-    const uint32_t gbest = __ockl_wfred_max_u32(best);
-    const uint64_t holders = __ballot(best == gbest);
+    const uint32_t gbest = __ockl_wfred_max_u32(key[0]);
+    const uint64_t holders = __ballot(key[0] == gbest);
     const int winner = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(holders)));
-    const int e = __builtin_amdgcn_readlane(lane * per + pick, winner);
-    if (lane == winner) {
+    const int e = __builtin_amdgcn_readlane(id[0], winner);
+    const uint64_t wm = 1ull << winner;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) key[i] = (i == pick) ? 0u : key[i];
+    for (int i = 0; i + 1 < PER; ++i) {
+      key[i] = select_lanes(key[i], key[i + 1], wm);
+      id[i] = static_cast<int>(select_lanes(static_cast<uint32_t>(id[i]),
+                                            static_cast<uint32_t>(id[i + 1]), wm));
     }
+    key[PER - 1] = select_lanes(key[PER - 1], 0u, wm);
     if (lane == j) { my_e = e; my_key = gbest; }
   }
   my_l = key_float(my_key);
