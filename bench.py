@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="",
-                    help="decode1|decode1_two_calls|decode2|decode3|prefill|stack (profiling runs)")
+                    help="decode1|decode1_two_calls|decode1_gemv|decode2|decode3|prefill|windows|stack "
+                         "(profiling runs)")
     ap.add_argument("--stack-layers", type=int, default=48,
                     help="layers of the stacked decode/prefill runs (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -269,6 +270,58 @@ def main():
             },
         }
 
+    # ------------------------------------------------ verify windows T = 4..8
+    # The same Zipf-routed windows through the decode path (one call, top-k
+    # inside) and through the grouped prefill path (routing histogram +
+    # grouped GEMMs), to find where decode should hand over.
+    def grouped_window(T, n_steps, warmup):
+        total = n_steps * 2 + warmup
+        rng = synth.rng_for(1, 100 + T, 0)
+        xd, _ = synth.activations(rng, min(total, 64) * T, H, "bf16")
+        xs = torch.from_numpy(xd.view(np.int16)).view(torch.bfloat16).to(dev).view(-1, T, H)
+        nx = xs.shape[0]
+        lg = synth.zipf_logits(rng, total * T, E).reshape(total, T, E)
+        logits = torch.from_numpy(np.ascontiguousarray(lg)).to(dev)
+        r = {n: torch.empty(s_, dtype=dt, device=dev) for n, s_, dt in [
+            ("ids", (T, K), torch.int32), ("w", (T, K), torch.float32), ("counts", (E,), torch.int32),
+            ("offsets", (E + 1,), torch.int32), ("sp", (T * K,), torch.int32),
+            ("pp", (T * K,), torch.int32)]}
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+        wsr = B.workspace(B.MOE_OP_ROUTE, T, E, K, H, I, dev)
+        ws = B.workspace(B.MOE_OP_PREFILL, T, E, K, H, I, dev)
+
+        def step(i):
+            L = layers[i % len(layers)]
+            B.moe_route_topk(logits[i], K, r["ids"], r["w"], r["counts"], r["offsets"], r["sp"],
+                             r["pp"], wsr)
+            B.moe_expert_forward_prefill(L, xs[i % nx], r["ids"], r["w"], r["counts"], r["offsets"],
+                                         r["sp"], r["pp"], out, None, 0, ws)
+
+        timed(step, n_steps, warmup)
+        ncap = 2 * len(layers)
+        return graphed(step, ncap, max(1, n_steps // ncap))
+
+    def verify_windows(Ts, n_steps, warmup):
+        rows = {}
+        handover = None
+        for T in Ts:
+            d = decode_case(T, "zipf", n_steps, warmup)
+            d2 = decode_case(T, "zipf", n_steps, warmup, routed=False)
+            g_ms = grouped_window(T, n_steps, warmup)
+            dec_ms = min(d["ms_per_layer"], d2["ms_per_layer"])
+            faster = "decode" if dec_ms <= g_ms else "grouped"
+            if faster == "grouped" and handover is None:
+                handover = T
+            rows[f"T{T}"] = {"decode_ms_per_layer": d["ms_per_layer"],
+                             "decode_two_calls_ms_per_layer": d2["ms_per_layer"],
+                             "grouped_ms_per_layer": g_ms,
+                             "decode_tokens_per_s": T * 1000.0 / dec_ms,
+                             "grouped_tokens_per_s": T * 1000.0 / g_ms,
+                             "distinct_experts": d["distinct_experts_per_step"],
+                             "decode_hbm_frac": d["hbm_frac"], "faster": faster}
+        return {"routing": "zipf(1.1)", "launch": "hip_graph", "windows": rows,
+                "grouped_first_faster_at_T": handover}
+
     only = args.only
     if only in ("", "decode1"):
         results["decode_T1"] = decode_case(1, "router", args.steps, args.warmup)
@@ -284,6 +337,9 @@ def main():
         results["decode_T3"] = decode_case(3, "zipf", args.steps // 2, args.warmup)
     if only in ("", "prefill"):
         results["prefill_T1024"] = prefill_case(1024, args.prefill_steps, max(4, args.warmup // 4))
+    if only in ("", "windows"):
+        results["verify_windows"] = verify_windows([4, 5, 6, 7, 8], max(32, args.steps // 8),
+                                                   max(4, args.warmup // 2))
 
     # ------------------------------------------------- 48 stacked layers
     # 48 distinct layers (54.5 GB), x_{l+1} = x_l + MoE_l(rmsnorm(x_l)) in a
@@ -366,7 +422,9 @@ def main():
     if not args.no_cpu_baseline and only == "":
         cpu = cpu_baseline(args.cpu_seconds)
 
-    head = results.get("decode_T1") or next(iter(results.values()))
+    head = results.get("decode_T1") or next(
+        (v for v in results.values() if "tokens_per_s" in v),
+        {"tokens_per_s": float("nan"), "ms_per_layer": float("nan")})
     line = {
         "metric": "MoE-layer tokens/s (decode B=1..3, prefill 1024 chunk); HBM GB/s % peak",
         "value": round(head["tokens_per_s"], 2),

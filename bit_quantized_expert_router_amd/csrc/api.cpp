@@ -173,7 +173,7 @@ size_t moe_workspace_bytes(int32_t op, int32_t T, int32_t E, int32_t k, int32_t 
       if (H < 256 || I < 256) return 0;
       return prefill_workspace_bytes(T, E, k, H, I);
     case MOE_OP_ROUTE_GEMV:
-      if (T > MOE_MAX_DECODE_TOKENS) return 0;
+      if (T > MOE_MAX_GEMV_TOKENS) return 0;
       return 256 + (static_cast<size_t>(T) * E * 4 + 255) / 256 * 256;
     default: return 0;
   }
@@ -233,7 +233,7 @@ int moe_route_topk_gemv(const void* x, int32_t x_dtype, int32_t T, const uint16_
   if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1");
   if (k < 1) return fail(MOE_ERR_INVALID_ARG, "k must be >= 1");
   if (H < 256 || H % 256) return fail(MOE_ERR_INVALID_ARG, "H must be a positive multiple of 256");
-  if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "at most 4 tokens");
+  if (T > MOE_MAX_GEMV_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "at most 4 tokens");
   if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E must be <= 1024");
   if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k must be <= 16");
   if (k > E) return fail(MOE_ERR_INVALID_ARG, "k must be <= E");
@@ -276,7 +276,7 @@ int moe_expert_forward_decode(const moe_q2_layer* layer, const void* x, int32_t 
                               void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_forward(layer, x, x_dtype, T, topk_ids, topk_w, k, out, out_dtype, flags, workspace);
   if (st) return st;
-  if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "decode takes at most 4 tokens");
+  if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "decode takes at most 8 tokens");
   const size_t need = decode_workspace_bytes(T, k, layer->hidden, layer->inter);
   if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
   const hipError_t e = launch_decode(layer_args(layer), x, x_dtype == MOE_BF16, T, topk_ids, topk_w,
@@ -300,7 +300,7 @@ int moe_expert_forward_decode_routed(const moe_q2_layer* layer, const void* x, i
   int st = check_forward(layer, x, x_dtype, T, reinterpret_cast<const int32_t*>(logits), logits, k,
                          out, out_dtype, flags, workspace);
   if (st) return st;
-  if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "decode takes at most 4 tokens");
+  if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "decode takes at most 8 tokens");
   const size_t need = decode_workspace_bytes(T, k, layer->hidden, layer->inter);
   if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
   const hipError_t e = launch_decode(layer_args(layer), x, x_dtype == MOE_BF16, T, nullptr, nullptr,

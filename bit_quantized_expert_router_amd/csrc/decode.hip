@@ -44,18 +44,17 @@ namespace moeq2 {
 
 namespace {
 
-constexpr int kMaxSlots = MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK + 1;                   // 65
-constexpr int kMaxPairs = MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK + MOE_MAX_DECODE_TOKENS; // 68
+constexpr int kMaxT = MOE_MAX_DECODE_TOKENS;    // 8
+constexpr int kMaxSlots = kMaxT * MOE_MAX_TOPK + 1;                 // 129
+constexpr int kMaxPairs = kMaxT * MOE_MAX_TOPK + kMaxT;             // 136
 constexpr int kThreads = 512;            // 8 waves (kernel 2)
 constexpr int kWaves = kThreads / kWave;
 constexpr int kXRegValues = 12288;       // x is kept in registers when T*H <= this
 
-// x chunks of 8 values per thread kept in registers when NT threads less
-// the (up to 4) routing waves hold x
+// x chunks of 8 values per thread kept in registers; at least half of the
+// NT threads hold x
 template <int NT>
-constexpr int x_reg_chunks() {
-  return (kXRegValues / 8 + NT - kWave * MOE_MAX_DECODE_TOKENS - 1) / (NT - kWave * MOE_MAX_DECODE_TOKENS);
-}
+constexpr int x_reg_chunks() { return (kXRegValues / 8 + NT / 2 - 1) / (NT / 2); }
 constexpr int kDownBatch = 8;            // down tiles in flight per wave in kernel 2
 constexpr int kDownStage = 4;            // h~ chunks per thread loaded ahead in kernel 2
 
@@ -63,16 +62,16 @@ struct DecodeHeader {          // start of the workspace, written by block 0 of 
   int32_t n_slots;
   int32_t pad0[3];
   int32_t expert[kMaxSlots];                       // -1 = shared expert
-  int32_t pidx[kMaxSlots][MOE_MAX_DECODE_TOKENS];  // pair of (slot, token) or -1
-  float unscale[MOE_MAX_DECODE_TOKENS];            // 1 / s_t
-  int32_t pad1[179];
+  int32_t pidx[kMaxSlots][kMaxT];                  // pair of (slot, token) or -1
+  float unscale[kMaxT];                            // 1 / s_t
 };
-static_assert(sizeof(DecodeHeader) == 2048, "header size");
+constexpr size_t kHeaderBytes = 8192;            // h~ starts here
+static_assert(sizeof(DecodeHeader) <= kHeaderBytes, "header size");
 
 struct DecodeSlots {
   int n;
   int expert[kMaxSlots];
-  int pidx[kMaxSlots][MOE_MAX_DECODE_TOKENS];
+  int pidx[kMaxSlots][kMaxT];
   float wpair[kMaxPairs];
 };
 
@@ -82,27 +81,44 @@ __device__ __forceinline__ int wave_id() {
 
 // Wave 0: slots (distinct valid ids in first-occurrence order, then the
 // shared expert), the pair of every (slot, token) and every pair's weight.
-// Ids outside [0, E) are ignored.
+// Ids outside [0, E) are ignored.  The T*k pairs are taken 64 at a time; an
+// id already given a slot by an earlier group is found in slot_of (LDS, E
+// entries, used only when there is more than one group), duplicates inside a
+// group by lane matching.
 __device__ void build_slots(const int32_t* ids, const float* w, int T, int k, int E,
-                            bool has_shared, DecodeSlots& S) {
+                            bool has_shared, DecodeSlots& S, int* slot_of) {
   const int lane = threadIdx.x & (kWave - 1);
   const int np = T * k;
-  const int e = lane < np ? ids[lane] : -1;
-  const float wl = lane < np ? w[lane] : 0.0f;
-  const bool valid = lane < np && e >= 0 && e < E;
+  const bool multi = np > kWave;
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
-  const uint64_t same = match_lanes(valid ? e : 0, valid, nbits);
-  const uint64_t below = (1ull << lane) - 1ull;
-  const bool first = valid && (same & below) == 0;
-  const uint64_t fm = __ballot(first);
-  const int nd = __popcll(fm);
-  const int slot = valid ? __popcll(fm & ((1ull << __builtin_ctzll(same)) - 1ull)) : 0;
-  for (int i = lane; i < kMaxSlots * MOE_MAX_DECODE_TOKENS; i += kWave) (&S.pidx[0][0])[i] = -1;
+  for (int i = lane; i < kMaxSlots * kMaxT; i += kWave) (&S.pidx[0][0])[i] = -1;
+  if (multi)
+    for (int i = lane; i < E; i += kWave) slot_of[i] = -1;
   __builtin_amdgcn_wave_barrier();
-  if (first) S.expert[slot] = e;
-  if (valid) S.pidx[slot][lane / k] = lane;
-  if (lane < np) S.wpair[lane] = valid ? wl : 0.0f;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int nd = 0;
+  for (int base = 0; base < np; base += kWave) {
+    const int p = base + lane;
+    const int e = p < np ? ids[p] : -1;
+    const float wl = p < np ? w[p] : 0.0f;
+    const bool valid = p < np && e >= 0 && e < E;
+    const int prev = (multi && valid) ? slot_of[e] : -1;   // slot from an earlier group
+    const bool fresh = valid && prev < 0;
+    const uint64_t same = match_lanes(fresh ? e : 0, fresh, nbits);
+    const bool first = fresh && (same & below) == 0;
+    const uint64_t fm = __ballot(first);
+    const int slot = !valid ? 0
+                            : (prev >= 0 ? prev : nd + __popcll(fm & ((1ull << __builtin_ctzll(same)) - 1ull)));
+    if (first) {
+      S.expert[slot] = e;
+      if (multi) slot_of[e] = slot;
+    }
+    if (valid) S.pidx[slot][p / k] = p;
+    if (p < np) S.wpair[p] = valid ? wl : 0.0f;
+    nd += __popcll(fm);
+    __builtin_amdgcn_wave_barrier();
+  }
   if (has_shared && lane < T) {
     S.pidx[nd][lane] = np + lane;
     S.wpair[np + lane] = 1.0f;
@@ -111,6 +127,14 @@ __device__ void build_slots(const int32_t* ids, const float* w, int T, int k, in
     if (has_shared) S.expert[nd] = -1;
     S.n = nd + (has_shared ? 1 : 0);
   }
+}
+
+// Token of x chunk c (chunks of 8 values, cpt chunks per token).
+__device__ __forceinline__ int token_of_chunk(int c, int cpt) {
+  int t = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxT; ++q) t += c >= q * cpt;
+  return t;
 }
 
 __device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e) {
@@ -188,23 +212,24 @@ __device__ __forceinline__ void route_topk_waves(const LayerArgs& L, int T, int 
 // normaliser smul: every wave writes its partial sums of x^2 and max |x| to
 // s_stat (token_partials), and after a barrier every thread derives the
 // multipliers from them itself (token_derive).
-// (token of chunk c: c / (H/8), by comparisons; T <= 4)
+// (token of chunk c: c / (H/8), by comparisons)
 template <bool BF16, int XC>
 __device__ void token_partials(const void* x, int T, int H, bool xreg, const u32x4 (&xr)[XC][2],
-                               float (*s_stat)[MOE_MAX_DECODE_TOKENS][2], int xt, int nxt) {
+                               float (*s_stat)[kMaxT][2], int xt, int nxt) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = wave_id();
   const int nch = T * H / 8;
   const int cpt = H / 8;
-  float ss[MOE_MAX_DECODE_TOKENS] = {0.f, 0.f, 0.f, 0.f};
-  float mx[MOE_MAX_DECODE_TOKENS] = {0.f, 0.f, 0.f, 0.f};
+  float ss[kMaxT], mx[kMaxT];
+#pragma unroll
+  for (int q = 0; q < kMaxT; ++q) { ss[q] = 0.0f; mx[q] = 0.0f; }
   auto accum = [&](int c, const float (&v)[8]) {
-    const int t = (c >= cpt) + (c >= 2 * cpt) + (c >= 3 * cpt);
+    const int t = token_of_chunk(c, cpt);
     float a = 0.0f, b = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) { a += v[i] * v[i]; b = fmaxf(b, fabsf(v[i])); }
 #pragma unroll
-    for (int q = 0; q < MOE_MAX_DECODE_TOKENS; ++q) {
+    for (int q = 0; q < kMaxT; ++q) {
       ss[q] += (q == t) ? a : 0.0f;
       mx[q] = (q == t) ? fmaxf(mx[q], b) : mx[q];
     }
@@ -237,11 +262,11 @@ __device__ void token_partials(const void* x, int T, int H, bool xreg, const u32
 
 template <int NW>
 __device__ __forceinline__ void token_derive(int T, int H, int prenorm,
-                                             const float (*s_stat)[MOE_MAX_DECODE_TOKENS][2],
-                                             float (&rmul)[MOE_MAX_DECODE_TOKENS],
-                                             float (&smul)[MOE_MAX_DECODE_TOKENS]) {
+                                             const float (*s_stat)[kMaxT][2],
+                                             float (&rmul)[kMaxT],
+                                             float (&smul)[kMaxT]) {
 #pragma unroll
-  for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
+  for (int t = 0; t < kMaxT; ++t) {
     float a = 0.0f, b = 0.0f;
     if (t < T) {
 #pragma unroll
@@ -255,16 +280,16 @@ __device__ __forceinline__ void token_derive(int T, int H, int prenorm,
 // fp16 copy of x_hat * s_t into LDS ([T][H]).
 template <bool BF16, int XC>
 __device__ void stage_x(const void* x, int T, int H, bool xreg, const u32x4 (&xr)[XC][2],
-                        const float (&rmul)[MOE_MAX_DECODE_TOKENS],
-                        const float (&smul)[MOE_MAX_DECODE_TOKENS], _Float16* xs, int xt,
+                        const float (&rmul)[kMaxT],
+                        const float (&smul)[kMaxT], _Float16* xs, int xt,
                         int nxt) {
   const int nch = T * H / 8;
   const int cpt = H / 8;
   auto put = [&](int c, const float (&v)[8]) {
-    const int t = (c >= cpt) + (c >= 2 * cpt) + (c >= 3 * cpt);
+    const int t = token_of_chunk(c, cpt);
     float r = rmul[0], s = smul[0];
 #pragma unroll
-    for (int q = 1; q < MOE_MAX_DECODE_TOKENS; ++q) { r = (q == t) ? rmul[q] : r; s = (q == t) ? smul[q] : s; }
+    for (int q = 1; q < kMaxT; ++q) { r = (q == t) ? rmul[q] : r; s = (q == t) ? smul[q] : s; }
     f16x8 h;
 #pragma unroll
     for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>((v[i] * r) * s);
@@ -325,8 +350,8 @@ __device__ __forceinline__ void load_gateup(const uint8_t* expert, bool live, in
 template <int KTW>
 __device__ void gateup_compute(const GateUpTiles<KTW>& R, const _Float16* xs, int T, int H, int I,
                                int rt, int kq, int slot, bool active, const DecodeSlots& S,
-                               const float (&smul)[MOE_MAX_DECODE_TOKENS],
-                               f32x4 (*s_red)[2][16], _Float16* hout) {
+                               const float* s_smul,
+                               f32x4 (*s_red)[2][32], _Float16* hout) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = wave_id();
   const int KT = H / kTileCols;
@@ -345,19 +370,23 @@ __device__ void gateup_compute(const GateUpTiles<KTW>& R, const _Float16* xs, in
       }
     }
   }
-  if (lane < 16) { s_red[wid][0][lane] = acc_g; s_red[wid][1][lane] = acc_u; }
+  // accumulator element r of lane l: token 4 (l / 16) + r, row l % 16; the
+  // first two lane groups hold tokens 0..7
+  if (lane < 32) { s_red[wid][0][lane] = acc_g; s_red[wid][1][lane] = acc_u; }
   __syncthreads();
-  if (active && kq == 0 && lane < 16) {
+  if (active && kq == 0 && lane < 32) {
     f32x4 G = s_red[wid][0][lane], U = s_red[wid][1][lane];
     for (int q = 1; q < 4; ++q) { G += s_red[wid + q][0][lane]; U += s_red[wid + q][1][lane]; }
-    const int row = rt * kTileRows + lane;
+    const int row = rt * kTileRows + (lane & 15);
+    const bool hi = lane >= 16;
 #pragma unroll
-    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
+    for (int r = 0; r < 4; ++r) {
+      const int t = (hi ? 4 : 0) + r;
       const int p = t < T ? S.pidx[slot][t] : -1;
       if (p < 0) continue;
-      const float s = smul[t];
+      const float s = s_smul[t];
       const float u = 1.0f / s;
-      const float gv = G[t] * u, uv = U[t] * u;
+      const float gv = G[r] * u, uv = U[r] * u;
       const float h = S.wpair[p] * silu(gv) * uv * (s * s);
       hout[static_cast<size_t>(p) * I + row] = static_cast<_Float16>(h);
     }
@@ -397,7 +426,7 @@ __device__ __forceinline__ void load_down(const LayerArgs& L, const int* expert,
 template <int DB>
 __device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int KTd, int j0,
                                          int lane, const _Float16* hsrc,
-                                         const int (*pidx)[MOE_MAX_DECODE_TOKENS], int T, int I,
+                                         const int (*pidx)[kMaxT], int T, int I,
                                          f32x4& acc) {
   const int wid = wave_id();
   const int m = lane & 15, g = lane >> 4;
@@ -421,22 +450,24 @@ __device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int
 
 // Sum of the 8 waves' accumulators (wave order) and the output rows of tile
 // rt: out = acc * unscale^2 (+ residual); NaN rows when `poison`.
-__device__ void down_store(const f32x4& acc, f32x4 (*s_red)[16], int rt, int T, int H,
-                           const float (&unscale)[MOE_MAX_DECODE_TOKENS], const void* residual,
+__device__ void down_store(const f32x4& acc, f32x4 (*s_red)[32], int rt, int T, int H,
+                           const float (&unscale)[kMaxT], const void* residual,
                            void* out, int out_bf16, bool poison) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = wave_id();
-  if (lane < 16) s_red[wid][lane] = acc;
+  if (lane < 32) s_red[wid][lane] = acc;
   __syncthreads();
-  if (wid == 0 && lane < 16) {
+  if (wid == 0 && lane < 32) {
     f32x4 Y = s_red[0][lane];
     for (int q = 1; q < kWaves; ++q) Y += s_red[q][lane];
-    const int row = rt * kTileRows + lane;
+    const int row = rt * kTileRows + (lane & 15);
+    const bool hi = lane >= 16;
 #pragma unroll
-    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
+    for (int r = 0; r < 4; ++r) {
+      const int t = (hi ? 4 : 0) + r;
       if (t >= T) break;
-      const float u = unscale[t];
-      float v = Y[t] * (u * u);
+      const float u = hi ? unscale[4 + r] : unscale[r];
+      float v = Y[r] * (u * u);
       if (poison) v = __builtin_nanf("");
       const size_t o = static_cast<size_t>(t) * H + row;
       if (out_bf16) {
@@ -466,10 +497,12 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
   extern __shared__ __align__(16) uint8_t dyn[];
   _Float16* xs = reinterpret_cast<_Float16*>(dyn);              // [T][H]
   __shared__ DecodeSlots S;
-  __shared__ int32_t s_rid[RPER > 0 ? MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK : 1];
-  __shared__ float s_rw[RPER > 0 ? MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK : 1];
-  __shared__ float s_stat[NW][MOE_MAX_DECODE_TOKENS][2];
-  __shared__ f32x4 s_red[NW][2][16];
+  __shared__ int32_t s_rid[RPER > 0 ? kMaxT * MOE_MAX_TOPK : 1];
+  __shared__ float s_rw[RPER > 0 ? kMaxT * MOE_MAX_TOPK : 1];
+  __shared__ float s_stat[NW][kMaxT][2];
+  __shared__ f32x4 s_red[NW][2][32];
+  __shared__ int s_slot_of[MOE_MAX_EXPERTS];
+  __shared__ float s_smul[kMaxT];
 
   const int H = L.H, I = L.I;
   const int RTI = I / kTileRows;                 // row tiles of one gate (or up) matrix
@@ -481,32 +514,43 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
   // Waves 0..T-1 route (one token each); meanwhile the other waves load x,
   // sum its statistics and, after one barrier, stage its fp16 copy while
   // wave 0 builds the slots.  So x is ready in LDS when the weight loads are
-  // issued, and the MFMA loop can take each tile as it arrives.
+  // issued, and the MFMA loop can take each tile as it arrives.  With more
+  // than half of the waves routing, all waves take x after routing.
   const int nch = T * H / 8;
-  const int xt = static_cast<int>(threadIdx.x) - kWave * T;   // x thread (waves T..)
-  const int nxt = NT - kWave * T;
+  const int xw0 = T <= NW / 2 ? T : 0;                         // first x wave
+  const int xt = static_cast<int>(threadIdx.x) - kWave * xw0;  // x thread
+  const int nxt = NT - kWave * xw0;
   const bool xreg = nch <= nxt * XC;
   u32x4 xr[XC][2];
+  if (wid >= xw0) issue_x<BF16, XC>(x, nch, xreg, xr, xt, nxt);
   if (wid < T) {
-    if (lane < MOE_MAX_DECODE_TOKENS) { s_stat[wid][lane][0] = 0.0f; s_stat[wid][lane][1] = 0.0f; }
     if constexpr (RPER > 0) {
       route_topk_waves<RPER>(L, T, k, logits, ids_out, w_out, s_rid, s_rw);
     } else {
-      if (wid == 0) build_slots(ids, w, T, k, L.E, L.shared != nullptr, S);
+      if (wid == 0) build_slots(ids, w, T, k, L.E, L.shared != nullptr, S, s_slot_of);
     }
-  } else {
-    issue_x<BF16, XC>(x, nch, xreg, xr, xt, nxt);
+  }
+  if (wid >= xw0) {
     token_partials<BF16, XC>(x, T, H, xreg, xr, s_stat, xt, nxt);
+  } else if (lane < kMaxT) {
+    s_stat[wid][lane][0] = 0.0f;
+    s_stat[wid][lane][1] = 0.0f;
   }
   __syncthreads();
-  float rmul[MOE_MAX_DECODE_TOKENS], smul[MOE_MAX_DECODE_TOKENS];
-  token_derive<NW>(T, H, prenorm, s_stat, rmul, smul);
-  if (wid < T) {
-    if constexpr (RPER > 0) {
-      if (wid == 0) build_slots(s_rid, s_rw, T, k, L.E, L.shared != nullptr, S);
+  {
+    // the multipliers live in registers only while x is staged; the epilogue
+    // and the header read the fp16 normalisers from LDS
+    float rmul[kMaxT], smul[kMaxT];
+    token_derive<NW>(T, H, prenorm, s_stat, rmul, smul);
+    if (threadIdx.x < kMaxT) {
+#pragma unroll
+      for (int t = 0; t < kMaxT; ++t)
+        if (t == static_cast<int>(threadIdx.x)) s_smul[t] = smul[t];
     }
-  } else {
-    stage_x<BF16, XC>(x, T, H, xreg, xr, rmul, smul, xs, xt, nxt);
+    if constexpr (RPER > 0) {
+      if (wid == 0) build_slots(s_rid, s_rw, T, k, L.E, L.shared != nullptr, S, s_slot_of);
+    }
+    if (wid >= xw0) stage_x<BF16, XC>(x, T, H, xreg, xr, rmul, smul, xs, xt, nxt);
   }
   __syncthreads();
   const int n_rows = S.n * RTI;
@@ -519,19 +563,15 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
   load_gateup<KTW>(expert_base(L, active ? S.expert[slot] : 0), active, H, I, rt, kq, lane, R);
   if (blockIdx.x == 0) {
     DecodeHeader* hdr = reinterpret_cast<DecodeHeader*>(ws);
-    if (threadIdx.x == 0) {
-#pragma unroll
-      for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t)
-        if (t < T) hdr->unscale[t] = 1.0f / smul[t];
-    }
-    for (int i = threadIdx.x; i < S.n * MOE_MAX_DECODE_TOKENS; i += NT)
+    if (threadIdx.x < T) hdr->unscale[threadIdx.x] = 1.0f / s_smul[threadIdx.x];
+    for (int i = threadIdx.x; i < S.n * kMaxT; i += NT)
       (&hdr->pidx[0][0])[i] = (&S.pidx[0][0])[i];
     if (threadIdx.x < S.n) hdr->expert[threadIdx.x] = S.expert[threadIdx.x];
     if (threadIdx.x == 0) hdr->n_slots = S.n;
   }
   if (static_cast<int>(blockIdx.x) >= n_rows) return;
-  gateup_compute<KTW>(R, xs, T, H, I, rt, kq, slot, active, S, smul, s_red,
-                      reinterpret_cast<_Float16*>(ws + sizeof(DecodeHeader)));
+  gateup_compute<KTW>(R, xs, T, H, I, rt, kq, slot, active, S, s_smul, s_red,
+                      reinterpret_cast<_Float16*>(ws + kHeaderBytes));
 }
 
 // Kernel 2: down row tile blockIdx.x.
@@ -541,12 +581,12 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   extern __shared__ __align__(16) uint8_t dyn[];
   _Float16* hs = reinterpret_cast<_Float16*>(dyn);     // [T*k + T][I] when staged
   __shared__ int s_expert[kMaxSlots];
-  __shared__ int s_pidx[kMaxSlots][MOE_MAX_DECODE_TOKENS];
+  __shared__ int s_pidx[kMaxSlots][kMaxT];
   __shared__ int s_n;
-  __shared__ float s_uns[MOE_MAX_DECODE_TOKENS];
-  __shared__ f32x4 s_red[kWaves][16];
+  __shared__ float s_uns[kMaxT];
+  __shared__ f32x4 s_red[kWaves][32];
   const DecodeHeader* hdr = reinterpret_cast<const DecodeHeader*>(ws);
-  const _Float16* hin = reinterpret_cast<const _Float16*>(ws + sizeof(DecodeHeader));
+  const _Float16* hin = reinterpret_cast<const _Float16*>(ws + kHeaderBytes);
   const int I = L.I;
   const int KTd = I / kTileCols;
   const int rt = blockIdx.x;
@@ -562,15 +602,21 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
 
   {
     // the header loads are issued together (clamped, unconditional)
+    constexpr int kPidxLoads = (kMaxSlots * kMaxT + kThreads - 1) / kThreads;
     const int i = threadIdx.x;
     const int ev = hdr->expert[min(i, kMaxSlots - 1)];
-    const int pv = (&hdr->pidx[0][0])[min(i, kMaxSlots * MOE_MAX_DECODE_TOKENS - 1)];
+    int pv[kPidxLoads];
+#pragma unroll
+    for (int q = 0; q < kPidxLoads; ++q)
+      pv[q] = (&hdr->pidx[0][0])[min(i + kThreads * q, kMaxSlots * kMaxT - 1)];
     const int nv = hdr->n_slots;
-    const float uv = hdr->unscale[min(i, MOE_MAX_DECODE_TOKENS - 1)];
+    const float uv = hdr->unscale[min(i, kMaxT - 1)];
     if (i < kMaxSlots) s_expert[i] = ev;
-    if (i < kMaxSlots * MOE_MAX_DECODE_TOKENS) (&s_pidx[0][0])[i] = pv;
+#pragma unroll
+    for (int q = 0; q < kPidxLoads; ++q)
+      if (i + kThreads * q < kMaxSlots * kMaxT) (&s_pidx[0][0])[i + kThreads * q] = pv[q];
     if (i == 0) s_n = nv;
-    if (i < MOE_MAX_DECODE_TOKENS) s_uns[i] = uv;
+    if (i < kMaxT) s_uns[i] = uv;
   }
   __syncthreads();
   const int nitems = s_n * KTd;
@@ -609,9 +655,9 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   };
   if (stage_lds) run(hs);
   else run(hin);
-  float uns[MOE_MAX_DECODE_TOKENS];
+  float uns[kMaxT];
 #pragma unroll
-  for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) uns[t] = s_uns[t];
+  for (int t = 0; t < kMaxT; ++t) uns[t] = s_uns[t];
   down_store(acc, s_red, rt, T, L.H, uns, residual, out, out_bf16, false);
 }
 
@@ -632,7 +678,7 @@ struct DecodeArgs {
   uint8_t* ws;
 };
 
-constexpr size_t kHStageLimit = 96 * 1024;   // largest h~ staged in LDS
+constexpr size_t kHStageLimit = 144 * 1024;  // largest h~ staged in LDS (one block per CU)
 
 template <int KTW, bool BF16, int RPER, int RTW>
 hipError_t launch_gateup4(const LayerArgs& L, int grid, uint32_t lds, hipStream_t s,
@@ -687,7 +733,7 @@ size_t decode_workspace_bytes(int T, int k, int H, int I) {
   (void)H;
   const size_t pairs = static_cast<size_t>(T) * k + T;
   const size_t h = pairs * I * sizeof(_Float16);
-  return sizeof(DecodeHeader) + (h + 255) / 256 * 256;
+  return kHeaderBytes + (h + 255) / 256 * 256;
 }
 
 hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,

@@ -213,13 +213,13 @@ __global__ __launch_bounds__(64 * kGemvWaves) void route_gemv_topk_kernel(
     *reinterpret_cast<f32x4*>(s_x + i + 4) = b;
   }
   __syncthreads();
-  double acc[kGemvExpertsPerWave][MOE_MAX_DECODE_TOKENS];
+  double acc[kGemvExpertsPerWave][MOE_MAX_GEMV_TOKENS];
 #pragma unroll
   for (int q = 0; q < kGemvExpertsPerWave; ++q)
 #pragma unroll
-    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) acc[q][t] = 0.0;
+    for (int t = 0; t < MOE_MAX_GEMV_TOKENS; ++t) acc[q][t] = 0.0;
 #pragma unroll
-  for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
+  for (int t = 0; t < MOE_MAX_GEMV_TOKENS; ++t) {
     if (t < T) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void route_gemv_topk_kernel(
 #pragma unroll
   for (int q = 0; q < kGemvExpertsPerWave; ++q) {
 #pragma unroll
-    for (int t = 0; t < MOE_MAX_DECODE_TOKENS; ++t) {
+    for (int t = 0; t < MOE_MAX_GEMV_TOKENS; ++t) {
       if (t < T) {
         const double sum = __ockl_wfred_add_f64(acc[q][t]);
         if (lane == 0 && e0 + q < E) logits[static_cast<size_t>(t) * E + e0 + q] = static_cast<float>(sum);

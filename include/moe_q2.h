@@ -14,7 +14,7 @@
  * Three calls make up one layer:
  *   moe_route_topk             router top-k + weights (+ token->expert
  *                              histogram and stable permutation for prefill)
- *   moe_expert_forward_decode  1..4 tokens (a decode step or a verify window)
+ *   moe_expert_forward_decode  1..8 tokens (a decode step or a verify window)
  *   moe_expert_forward_prefill any number of tokens (prompt chunks of 1024
  *                              or 32768 tokens), grouped by expert
  * and moe_expert_forward_decode_routed does the first two for decode in one
@@ -79,7 +79,8 @@ enum { MOE_OP_ROUTE = 0, MOE_OP_DECODE = 1, MOE_OP_PREFILL = 2, MOE_OP_ROUTE_GEM
 /* Limits of this build (validated): */
 #define MOE_MAX_EXPERTS 1024     /* E                                        */
 #define MOE_MAX_TOPK 16          /* k                                        */
-#define MOE_MAX_DECODE_TOKENS 4  /* T of moe_expert_forward_decode           */
+#define MOE_MAX_DECODE_TOKENS 8  /* T of moe_expert_forward_decode           */
+#define MOE_MAX_GEMV_TOKENS 4    /* T of moe_route_topk_gemv                  */
 #define MOE_MAX_DIM 8192         /* H and I (each a multiple of 256)         */
 #define MOE_MAX_TOKENS (1 << 17) /* T of routing and prefill (131072)        */
 
@@ -148,7 +149,7 @@ int moe_route_topk_gemv(const void* x, int32_t x_dtype, int32_t T, const uint16_
                         float* topk_w, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Decode-time expert layer for T = 1..4 tokens (one decode step or a verify
+ * Decode-time expert layer for T = 1..8 tokens (one decode step or a verify
  * window that checks a few drafted tokens at once: "32GB Mac mini ...",
  * section 一, and "RTX PRO 4500 ...", section 最重要机制, item 3).  Only the
  * selected experts' weights are read.
@@ -165,7 +166,7 @@ int moe_route_topk_gemv(const void* x, int32_t x_dtype, int32_t T, const uint16_
  *   workspace [device] >= moe_workspace_bytes(MOE_OP_DECODE, ...), 256-B aligned.
  * Errors: INVALID_ARG (null pointers, T < 1, k < 1 or > E, stride too small or
  * unaligned, H or I not multiples of 256, unknown dtype or flag),
- * UNSUPPORTED (T > 4, E > 1024, k > 16, H or I > 8192), WORKSPACE.
+ * UNSUPPORTED (T > 8, E > 1024, k > 16, H or I > 8192), WORKSPACE.
  */
 int moe_expert_forward_decode(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
                               int32_t T, const int32_t* topk_ids, const float* topk_w,
@@ -174,7 +175,7 @@ int moe_expert_forward_decode(const moe_q2_layer* layer, const void* x, int32_t 
                               void* stream);
 
 /*
- * Router and decode-time expert layer in one call, for T = 1..4 tokens: the
+ * Router and decode-time expert layer in one call, for T = 1..8 tokens: the
  * top-k of `logits` is taken inside the expert kernels (every workgroup
  * selects the experts of the T tokens itself), so no separate routing
  * kernel runs before the weights can be fetched.  Same routing as
@@ -200,7 +201,7 @@ int moe_expert_forward_decode_routed(const moe_q2_layer* layer, const void* x, i
  * 1024 and 32768: "Strata 实测 ...", section 四, change 4).
  * Arguments as for the decode call, plus the four histogram arrays from
  * moe_route_topk for the same topk_ids.  Computes the same `out`.
- * Errors: as for decode, with T limited to 1..2^17 instead of 1..4 (so that
+ * Errors: as for decode, with T limited to 1..2^17 instead of 1..8 (so that
  * every activation offset fits in 32 bits).
  */
 int moe_expert_forward_prefill(const moe_q2_layer* layer, const void* x, int32_t x_dtype,

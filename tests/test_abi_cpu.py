@@ -50,7 +50,10 @@ def test_status_strings(lib):
 def test_workspace_sizes(lib):
     from bit_quantized_expert_router_amd import binding as B
     assert B.moe_workspace_bytes(B.MOE_OP_DECODE, 1, 512, 10, 3072, 768) > 0
-    assert B.moe_workspace_bytes(B.MOE_OP_DECODE, 5, 512, 10, 3072, 768) == 0
+    # header + h~ rows of T*k + T pairs
+    assert B.moe_workspace_bytes(B.MOE_OP_DECODE, 8, 512, 10, 3072, 768) >= 88 * 768 * 2
+    assert B.moe_workspace_bytes(B.MOE_OP_DECODE, 9, 512, 10, 3072, 768) == 0
+    assert B.moe_workspace_bytes(B.MOE_OP_ROUTE_GEMV, 5, 512, 10, 3072, 0) == 0
     p = B.moe_workspace_bytes(B.MOE_OP_PREFILL, 1024, 512, 10, 3072, 768)
     # x16 + h + y at least
     assert p >= 1024 * 3072 * 2 + 11264 * 768 * 2 + 11264 * 3072 * 2
@@ -157,7 +160,7 @@ def test_forward_validation(lib, which):
     assert forward(lib, which, wsb=100) == -3
     assert forward(lib, which, ws=FAKE + 8) == -1
     if which in ("decode", "routed"):
-        assert forward(lib, which, T=5) == -2
+        assert forward(lib, which, T=9) == -2
     if which == "routed":
         assert forward(lib, which, logits=None) == -1
         assert forward(lib, which, ids=None) == -1            # only one routing output

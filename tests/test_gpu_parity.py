@@ -198,7 +198,7 @@ def test_decode_small_config(B, layer_small):
     check_out(to_np(out), ref, "decode cfg0")
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_decode_full_size(B, layer_full, T):
     L = layer_full
     rng = synth.rng_for(1, 0, 10 + T)
@@ -231,11 +231,13 @@ def test_decode_prenorm_residual_bf16(B, layer_full):
     check_out(to_np(outb), refb, "decode bf16 out")
 
 
-def test_decode_duplicates_and_no_shared(B):
-    """Tokens sharing experts (slot dedup) and a layer without shared expert."""
+@pytest.mark.parametrize("T", [4, 8])
+def test_decode_duplicates_and_no_shared(B, T):
+    """Tokens sharing experts (slot dedup) and a layer without shared expert;
+    at T = 8 the 128 pairs are deduplicated in two groups of 64."""
     L = Layer(B, 5, 16, 512, 256, shared=False)
-    T, k = 4, 16
-    rng = synth.rng_for(5, 0, 3)
+    k = 16
+    rng = synth.rng_for(5, 0, T - 1)
     xd, xv = synth.activations(rng, T, 512, "f32")
     lg = synth.tie_logits(rng, T, 16)
     ids, w, r = route_both(B, lg, k, False)
@@ -261,7 +263,10 @@ ROUTED_CASES = [
     ((1, 512, 3072, 768), 2, 10, "zipf", "bf16"),
     ((1, 512, 3072, 768), 3, 10, "zipf", "bf16"),
     ((1, 512, 3072, 768), 4, 10, "ties", "bf16"),
+    ((1, 512, 3072, 768), 6, 10, "zipf", "f32"),
+    ((1, 512, 3072, 768), 8, 10, "zipf", "bf16"),      # 8 routing waves, 80 pairs
     ((7, 1024, 512, 256), 4, 16, "normal", "f32"),     # top-k with 16 experts per lane
+    ((7, 1024, 512, 256), 8, 16, "normal", "bf16"),    # 128 pairs, up to 129 slots
     ((8, 300, 512, 512), 2, 7, "normal", "bf16"),      # E not a multiple of 64
 ]
 
