@@ -423,7 +423,7 @@ def main():
         cpu = cpu_baseline(args.cpu_seconds)
 
     head = results.get("decode_T1") or next(
-        (v for v in results.values() if "tokens_per_s" in v),
+        (v for v in results.values() if "tokens_per_s" in v and "ms_per_layer" in v),
         {"tokens_per_s": float("nan"), "ms_per_layer": float("nan")})
     line = {
         "metric": "MoE-layer tokens/s (decode B=1..3, prefill 1024 chunk); HBM GB/s % peak",
