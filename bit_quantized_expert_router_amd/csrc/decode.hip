@@ -750,15 +750,16 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
                      static_cast<uint8_t*>(ws)};
   hipError_t e;
   {
-    // one block per CU with 2 or 3 row-tile groups when that covers every row
-    // tile; otherwise 2 groups per block and more blocks than CUs (four
-    // groups of 16 waves measured slower than two blocks of 8 per CU)
+    // at most one block per CU, each with 2 or 3 fully used row-tile groups,
+    // when that covers every row tile; otherwise 2 groups per block and more
+    // blocks than CUs (four groups of 16 waves measured slower than two
+    // blocks of 8 per CU)
     const int rows = slots_max * (L.I / kTileRows);
     const int cus = device_cus();
     int grid = (rows + 1) / 2, rtw = 2;
     if (cus > 0 && ktw <= 4 && grid > cus && (rows + cus - 1) / cus <= 3) {
-      grid = cus;
       rtw = (rows + cus - 1) / cus;
+      grid = (rows + rtw - 1) / rtw;
     }
     const uint32_t lds = static_cast<uint32_t>(lds_x);
     switch (ktw) {
