@@ -158,13 +158,14 @@ def main():
         if gemv:         # router weights (bf16 [E, H]) per rotating layer
             wr = [(torch.randn((E, H), device=dev) / np.sqrt(H)).to(torch.bfloat16)
                   for _ in range(len(layers))]
-            wsg = B.workspace(B.MOE_OP_ROUTE_GEMV, T, E, K, H, I, dev)
+            lgg = [torch.empty((T, E), dtype=torch.float32, device=dev) for _ in range(2)]
 
         def step(i):
             L = layers[i % len(layers)]
-            if gemv:     # router GEMV + top-k kernel, then the expert layer
-                B.moe_route_topk_gemv(xs[i % nx], wr[i % len(layers)], K, ids[i], wts[i], None, wsg)
-                B.moe_expert_forward_decode(L, xs[i % nx], ids[i], wts[i], out, None, 0, ws)
+            if gemv:     # router logits GEMV, then the one-call expert layer (top-k inside)
+                B.moe_route_topk_gemv(xs[i % nx], wr[i % len(layers)], K, None, None, lgg[i % 2], None)
+                B.moe_expert_forward_decode_routed(L, xs[i % nx], lgg[i % 2], K, out, ids[i], wts[i],
+                                                   None, 0, ws)
             elif routed:   # one call: top-k inside the expert kernels
                 B.moe_expert_forward_decode_routed(L, xs[i % nx], logits[i], K, out, ids[i], wts[i],
                                                    None, 0, ws)
@@ -195,7 +196,7 @@ def main():
         gu_bytes = slots * 2 * MAT_BYTES + T * H * 2 + (T * K + T) * I * 2   # weights, x, h
         return {
             "T": T, "routing": kind,
-            "calls": ("route_topk_gemv+decode (router GEMV included)" if gemv else
+            "calls": ("route_topk_gemv (logits) + decode_routed (router GEMV included)" if gemv else
                       "decode_routed" if routed else "route_topk+decode"),
             "launch": "hip_graph", "ms_per_layer": ms,
             "ms_per_layer_eager": ms_eager, "tokens_per_s": T * 1000.0 / ms,

@@ -146,7 +146,8 @@ def moe_route_topk(logits, k, topk_ids, topk_w, counts=None, offsets=None, sorte
 
 
 def moe_route_topk_gemv(x, router_w, k, topk_ids, topk_w, logits=None, ws=None, stream=None):
-    """router_w: bf16 tensor [E, H] (or its int16/uint16 bits)."""
+    """router_w: bf16 tensor [E, H] (or its int16/uint16 bits).  topk_ids and
+    topk_w may both be None (logits only; ws may then be None too)."""
     T, H = x.shape
     E = router_w.shape[0]
     _check(lib.moe_route_topk_gemv(_ptr(x), _dtype_code(x), T, _ptr(router_w), E, H, k, _ptr(logits),

@@ -226,8 +226,11 @@ int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t
 int moe_route_topk_gemv(const void* x, int32_t x_dtype, int32_t T, const uint16_t* router_w,
                         int32_t E, int32_t H, int32_t k, float* logits, int32_t* topk_ids,
                         float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!x || !router_w || !topk_ids || !topk_w)
-    return fail(MOE_ERR_INVALID_ARG, "x, router_w, topk_ids and topk_w are required");
+  if (!x || !router_w) return fail(MOE_ERR_INVALID_ARG, "x and router_w are required");
+  if ((topk_ids == nullptr) != (topk_w == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "topk_ids and topk_w: both or neither");
+  const bool select = topk_ids != nullptr;
+  if (!select && !logits) return fail(MOE_ERR_INVALID_ARG, "logits is required without topk_ids");
   if (!valid_dtype(x_dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
   if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1");
   if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1");
@@ -239,16 +242,18 @@ int moe_route_topk_gemv(const void* x, int32_t x_dtype, int32_t T, const uint16_
   if (k > E) return fail(MOE_ERR_INVALID_ARG, "k must be <= E");
   if (H > MOE_MAX_DIM) return fail(MOE_ERR_UNSUPPORTED, "H must be <= 8192");
   if (!aligned(x, 16) || !aligned(router_w, 16) || (logits && !aligned(logits, 4)) ||
-      !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+      (select && (!aligned(topk_ids, 4) || !aligned(topk_w, 4))))
     return fail(MOE_ERR_INVALID_ARG, "x and router_w must be 16-byte aligned, the outputs 4-byte aligned");
-  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is required");
-  if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const size_t need = moe_workspace_bytes(MOE_OP_ROUTE_GEMV, T, E, k, H, 0);
-  if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (select) {   // the counter (and the logits when not requested) live in the workspace
+    if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is required");
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const size_t need = moe_workspace_bytes(MOE_OP_ROUTE_GEMV, T, E, k, H, 0);
+    if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
+  }
   float* lg = logits ? logits : reinterpret_cast<float*>(ws + 256);
   const hipError_t e = launch_route_gemv_topk(x, x_dtype == MOE_BF16, T, router_w, E, H, k, lg, topk_ids,
-                                             topk_w, reinterpret_cast<uint32_t*>(ws),
+                                             topk_w, select ? reinterpret_cast<uint32_t*>(ws) : nullptr,
                                              static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, "route_gemv_topk launch");
 }

@@ -167,12 +167,13 @@ __global__ __launch_bounds__(1024) void route_scatter_kernel(
 // fp64 (lane partial sums over fixed columns, then a fixed-order wavefront
 // reduction) and rounded once to fp32, so the logits agree with a plain fp64
 // dot product except when that one rounding falls within the fp64 summation
-// error of an fp32 rounding boundary.  Each wave computes the logits of two
-// experts for all T tokens; the last workgroup to finish (one agent-scope
-// atomic per workgroup on a counter it then resets) selects the top-k from
-// the logits written by all of them.  No workgroup waits for another.
+// error of an fp32 rounding boundary.  Each wave computes the logits of one
+// expert for all T tokens.  With `ids` given, the last workgroup to finish
+// (one agent-scope atomic per workgroup on a counter it then resets) selects
+// the top-k from the logits written by all of them; no workgroup waits for
+// another.  Without `ids` the kernel only writes the logits.
 constexpr int kGemvWaves = 4;
-constexpr int kGemvExpertsPerWave = 2;
+constexpr int kGemvExpertsPerWave = 1;
 constexpr int kGemvExpertsPerBlock = kGemvWaves * kGemvExpertsPerWave;
 
 extern "C" __device__ double __ockl_wfred_add_f64(double);
@@ -252,8 +253,12 @@ __global__ __launch_bounds__(64 * kGemvWaves) void route_gemv_topk_kernel(
       }
     }
   }
-  // publish this workgroup's logits; the last workgroup selects
-  __threadfence();
+  if (ids == nullptr) return;
+  // Publish this workgroup's logits; the last workgroup selects.  The block
+  // barrier completes every wave's stores (they are in this XCD's L2); thread
+  // 0's arrival is a device-scope release (one L2 write-back per workgroup)
+  // and, for the last workgroup, an acquire that invalidates this CU's and
+  // XCD's stale lines before any wave reads the logits.
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -261,7 +266,6 @@ __global__ __launch_bounds__(64 * kGemvWaves) void route_gemv_topk_kernel(
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   if (wid < T) {
     int my_e;
     float l;

@@ -135,13 +135,17 @@ int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
  *   x         [device] [T, H] activations, x_dtype MOE_F32 or MOE_BF16, 16-byte aligned.
  *   router_w  [device] bf16 [E, H] (row e belongs to expert e), 16-byte aligned.
  *   logits    [device] float32 [T, E] output, or NULL (then only in the workspace).
- *   topk_ids, topk_w  [device] [T, k] outputs.
+ *   topk_ids, topk_w  [device] [T, k] outputs, or both NULL: then only the
+ *             logits are computed (they must then be requested), e.g. to feed
+ *             moe_expert_forward_decode_routed, which takes the top-k itself.
  *   workspace [device] >= moe_workspace_bytes(MOE_OP_ROUTE_GEMV, T, E, k, H, 0),
- *             256-byte aligned.  Its first 4 bytes are a counter that must be
- *             zero before the first call on this workspace; every call leaves
- *             it zero.  Concurrent calls need separate workspaces.
- * Errors: INVALID_ARG (null pointers, T, E or k < 1, k > E, H not a multiple
- * of 256, unknown dtype, misalignment), UNSUPPORTED (T > 4, E > 1024, k > 16,
+ *             256-byte aligned; may be NULL when topk_ids is NULL.  Its first
+ *             4 bytes are a counter that must be zero before the first call
+ *             on this workspace; every call leaves it zero.  Concurrent calls
+ *             need separate workspaces.
+ * Errors: INVALID_ARG (null x or router_w, only one of topk_ids / topk_w,
+ * neither logits nor topk_ids, T, E or k < 1, k > E, H not a multiple of 256,
+ * unknown dtype, misalignment), UNSUPPORTED (T > 4, E > 1024, k > 16,
  * H > 8192), WORKSPACE.
  */
 int moe_route_topk_gemv(const void* x, int32_t x_dtype, int32_t T, const uint16_t* router_w,

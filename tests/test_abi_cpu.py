@@ -95,6 +95,9 @@ def test_route_gemv_validation(lib):
     assert gemv(lib, W=FAKE + 8) == -1
     assert gemv(lib, ws=None) == -3
     assert gemv(lib, wsb=16) == -3
+    assert gemv(lib, ids=None) == -1                      # only one routing output
+    assert gemv(lib, ids=None, w=None) == -1              # nothing requested
+    assert gemv(lib, ids=None, w=None, lg=FAKE + 2) == -1  # unaligned logits
     assert lib.moe_workspace_bytes(3, 4, 512, 10, 3072, 0) >= 256 + 4 * 512 * 4
     assert lib.moe_workspace_bytes(3, 5, 512, 10, 3072, 0) == 0
 

@@ -144,6 +144,11 @@ def test_route_gemv_topk(B, T, E, H, k, xdt):
         assert np.array_equal(lg.cpu().numpy(), ref_lg), "logits differ"
         assert_route_exact(ids, w, {"topk_ids": rid, "topk_w": rw}, E, False)
     assert int(ws[:4].view(torch.int32)[0]) == 0
+    # logits only (no top-k, no workspace)
+    lg2 = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    B.moe_route_topk_gemv(dev_x(xd, xdt), Wt, k, None, None, lg2, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(lg2.cpu().numpy(), ref_lg), "logits-only call differs"
 
 
 def test_route_gemv_then_decode_matches_oracle(B, layer_full):
@@ -162,6 +167,18 @@ def test_route_gemv_then_decode_matches_oracle(B, layer_full):
     out = run_decode(B, L, dev_x(xd, "bf16"), {"topk_ids": rid, "topk_w": rw})
     assert np.array_equal(rid.cpu().numpy(), ids)
     check_out(to_np(out), O.moe_layer(xv, ids, w, L.ref), "router gemv + decode")
+    # logits only, then the one-call decode that takes the top-k itself
+    lg = torch.empty((T, 512), dtype=torch.float32, device="cuda")
+    B.moe_route_topk_gemv(dev_x(xd, "bf16"), torch.from_numpy(Wb.view(np.int16)).cuda(), 10, None, None,
+                          lg, None)
+    out2 = torch.empty((T, 3072), dtype=torch.float32, device="cuda")
+    rid2 = torch.empty_like(rid)
+    rw2 = torch.empty_like(rw)
+    B.moe_expert_forward_decode_routed(L.dev, dev_x(xd, "bf16"), lg, 10, out2, rid2, rw2, None, 0,
+                                       B.workspace(B.MOE_OP_DECODE, T, 512, 10, 3072, 768))
+    torch.cuda.synchronize()
+    assert np.array_equal(rid2.cpu().numpy(), ids)
+    assert torch.equal(out2, out)
 
 
 # ------------------------------------------------------------------- decode --
