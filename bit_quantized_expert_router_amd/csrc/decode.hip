@@ -84,15 +84,17 @@ __device__ __forceinline__ int wave_id() {
 // Ids outside [0, E) are ignored.  The T*k pairs are taken 64 at a time; an
 // id already given a slot by an earlier group is found in slot_of (LDS, E
 // entries, used only when there is more than one group), duplicates inside a
-// group by lane matching.
+// group by lane matching -- skipped when the caller knows the ids are
+// distinct (one token's own top-k).
 __device__ void build_slots(const int32_t* ids, const float* w, int T, int k, int E,
-                            bool has_shared, DecodeSlots& S, int* slot_of) {
+                            bool has_shared, DecodeSlots& S, int* slot_of, bool distinct) {
   const int lane = threadIdx.x & (kWave - 1);
   const int np = T * k;
   const bool multi = np > kWave;
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
-  for (int i = lane; i < kMaxSlots * kMaxT; i += kWave) (&S.pidx[0][0])[i] = -1;
+  // only the rows of slots that can exist (at most T*k + 1) are read later
+  for (int i = lane; i < (np + 1) * kMaxT; i += kWave) (&S.pidx[0][0])[i] = -1;
   if (multi)
     for (int i = lane; i < E; i += kWave) slot_of[i] = -1;
   __builtin_amdgcn_wave_barrier();
@@ -105,7 +107,7 @@ __device__ void build_slots(const int32_t* ids, const float* w, int T, int k, in
     const bool valid = p < np && e >= 0 && e < E;
     const int prev = (multi && valid) ? slot_of[e] : -1;   // slot from an earlier group
     const bool fresh = valid && prev < 0;
-    const uint64_t same = match_lanes(fresh ? e : 0, fresh, nbits);
+    const uint64_t same = distinct ? (1ull << lane) : match_lanes(fresh ? e : 0, fresh, nbits);
     const bool first = fresh && (same & below) == 0;
     const uint64_t fm = __ballot(first);
     const int slot = !valid ? 0
@@ -267,13 +269,15 @@ __device__ __forceinline__ void token_derive(int T, int H, int prenorm,
                                              float (&smul)[kMaxT]) {
 #pragma unroll
   for (int t = 0; t < kMaxT; ++t) {
-    float a = 0.0f, b = 0.0f;
-    if (t < T) {
+    rmul[t] = 1.0f;
+    smul[t] = 1.0f;
+    if (t < T) {   // uniform: only the window's tokens pay for the divisions
+      float a = 0.0f, b = 0.0f;
 #pragma unroll
       for (int q = 0; q < NW; ++q) { a += s_stat[q][t][0]; b = fmaxf(b, s_stat[q][t][1]); }
+      rmul[t] = prenorm ? 1.0f / sqrtf(a / static_cast<float>(H) + 1e-6f) : 1.0f;
+      smul[t] = pow2_normaliser(b * rmul[t]);
     }
-    rmul[t] = prenorm ? 1.0f / sqrtf(a / static_cast<float>(H) + 1e-6f) : 1.0f;
-    smul[t] = pow2_normaliser(b * rmul[t]);
   }
 }
 
@@ -527,7 +531,7 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
     if constexpr (RPER > 0) {
       route_topk_waves<RPER>(L, T, k, logits, ids_out, w_out, s_rid, s_rw);
     } else {
-      if (wid == 0) build_slots(ids, w, T, k, L.E, L.shared != nullptr, S, s_slot_of);
+      if (wid == 0) build_slots(ids, w, T, k, L.E, L.shared != nullptr, S, s_slot_of, false);
     }
   }
   if (wid >= xw0) {
@@ -542,13 +546,12 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
     // and the header read the fp16 normalisers from LDS
     float rmul[kMaxT], smul[kMaxT];
     token_derive<NW>(T, H, prenorm, s_stat, rmul, smul);
-    if (threadIdx.x < kMaxT) {
+    if (threadIdx.x == 0) {
 #pragma unroll
-      for (int t = 0; t < kMaxT; ++t)
-        if (t == static_cast<int>(threadIdx.x)) s_smul[t] = smul[t];
+      for (int t = 0; t < kMaxT; ++t) s_smul[t] = smul[t];
     }
     if constexpr (RPER > 0) {
-      if (wid == 0) build_slots(s_rid, s_rw, T, k, L.E, L.shared != nullptr, S, s_slot_of);
+      if (wid == 0) build_slots(s_rid, s_rw, T, k, L.E, L.shared != nullptr, S, s_slot_of, T == 1);
     }
     if (wid >= xw0) stage_x<BF16, XC>(x, T, H, xreg, xr, rmul, smul, xs, xt, nxt);
   }
