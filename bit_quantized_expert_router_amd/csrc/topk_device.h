@@ -42,40 +42,18 @@ __device__ __forceinline__ bool topk_before(uint32_t ka, int ia, uint32_t kb, in
   return ka > kb || (ka == kb && ia < ib);
 }
 
-// One token per wave.  Lane l holds experts l*per .. l*per+per-1, so a lower
-// lane always holds lower ids.  Each lane first sorts its PER (key, id) pairs
-// into selection order (a bitonic network, compile-time indices only); then
-// every round takes the wave maximum of the lanes' head keys (a DPP wavefront
-// reduction), the lowest lane holding it wins -- its head is the lowest id
-// among the equal keys -- and the winner shifts its list up by one.  PER
-// (>= per, a power of two) is a compile-time bound; all loads are issued
-// before any is used (clamped, so none is conditional).  Lane j < k receives
-// the id and the logit of round j.
+// Top-k of the (key, id) pairs a wave holds, PER per lane (a power of two;
+// key 0 marks an empty entry; every id of a lower lane is lower).  Each lane
+// first sorts its pairs into selection order (a bitonic network,
+// compile-time indices only); then every round takes the wave maximum of the
+// lanes' head keys (a DPP wavefront reduction), the lowest lane holding it
+// wins -- its head is the lowest id among the equal keys -- and the winner
+// shifts its list up by one.  Lane j < k receives the id and the key of
+// round j.
 template <int PER>
-__device__ __forceinline__ void topk_one_token(const float* __restrict__ row, int E, int k,
-                                               int lane, int& my_e, float& my_l) {
+__device__ __forceinline__ void topk_select(uint32_t (&key)[PER], int (&id)[PER], int k, int lane,
+                                            int& my_e, uint32_t& my_key) {
   static_assert((PER & (PER - 1)) == 0, "PER must be a power of two");
-  const int per = (E + kWave - 1) / kWave;
-  float lv[PER];
-  if (PER >= 4 && E == PER * kWave && (reinterpret_cast<uintptr_t>(row) & 15) == 0) {
-    // whole 16-byte vectors per lane (E = 64 * PER)
-#pragma unroll
-    for (int i = 0; i < PER; i += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(row + lane * PER + i);
-      lv[i] = v[0]; lv[i + 1] = v[1]; lv[i + 2] = v[2]; lv[i + 3] = v[3];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) lv[i] = row[min(lane * per + i, E - 1)];
-  }
-  uint32_t key[PER];
-  int id[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane * per + i;
-    key[i] = (i < per && e < E) ? float_key(lv[i]) : 0u;
-    id[i] = e;
-  }
   // bitonic sort into selection order (position 0 first)
 #pragma unroll
   for (int size = 2; size <= PER; size <<= 1) {
@@ -98,7 +76,7 @@ __device__ __forceinline__ void topk_one_token(const float* __restrict__ row, in
     }
   }
   my_e = 0;
-  uint32_t my_key = 0;
+  my_key = 0;
   for (int j = 0; j < k; ++j) {
     const uint32_t gbest = __ockl_wfred_max_u32(key[0]);
     const uint64_t holders = __ballot(key[0] == gbest);
@@ -114,6 +92,38 @@ __device__ __forceinline__ void topk_one_token(const float* __restrict__ row, in
     key[PER - 1] = select_lanes(key[PER - 1], 0u, wm);
     if (lane == j) { my_e = e; my_key = gbest; }
   }
+}
+
+// One token per wave.  Lane l holds experts l*per .. l*per+per-1, so a lower
+// lane always holds lower ids.  PER (>= per) is a compile-time bound; all
+// loads are issued before any is used (clamped, so none is conditional).
+// Lane j < k receives the id and the logit of round j.
+template <int PER>
+__device__ __forceinline__ void topk_one_token(const float* __restrict__ row, int E, int k,
+                                               int lane, int& my_e, float& my_l) {
+  const int per = (E + kWave - 1) / kWave;
+  float lv[PER];
+  if (PER >= 4 && E == PER * kWave && (reinterpret_cast<uintptr_t>(row) & 15) == 0) {
+    // whole 16-byte vectors per lane (E = 64 * PER)
+#pragma unroll
+    for (int i = 0; i < PER; i += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(row + lane * PER + i);
+      lv[i] = v[0]; lv[i + 1] = v[1]; lv[i + 2] = v[2]; lv[i + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) lv[i] = row[min(lane * per + i, E - 1)];
+  }
+  uint32_t key[PER];
+  int id[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane * per + i;
+    key[i] = (i < per && e < E) ? float_key(lv[i]) : 0u;
+    id[i] = e;
+  }
+  uint32_t my_key;
+  topk_select<PER>(key, id, k, lane, my_e, my_key);
   my_l = key_float(my_key);
 }
 

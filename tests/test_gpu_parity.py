@@ -277,6 +277,9 @@ ROUTED_CASES = [
     # (layer: seed, E, H, I), T, k, logits kind, x dtype
     ((0, 64, 1024, 256), 1, 4, "router", "f32"),
     ((1, 512, 3072, 768), 1, 10, "router", "bf16"),
+    ((1, 512, 3072, 768), 1, 10, "ties", "bf16"),      # block-wide top-k, ties across slices
+    ((7, 1024, 512, 256), 1, 16, "ties", "f32"),
+    ((8, 300, 512, 512), 1, 7, "normal", "f32"),       # slices not a multiple of 64
     ((1, 512, 3072, 768), 2, 10, "zipf", "bf16"),
     ((1, 512, 3072, 768), 3, 10, "zipf", "bf16"),
     ((1, 512, 3072, 768), 4, 10, "ties", "bf16"),
