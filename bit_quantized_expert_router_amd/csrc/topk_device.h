@@ -36,14 +36,9 @@ __device__ __forceinline__ uint32_t select_lanes(uint32_t a, uint32_t b, uint64_
   return r;
 }
 
-// (key, id) order of the selection: larger key first, lower id first among
-// equal keys.
-__device__ __forceinline__ bool topk_before(uint32_t ka, int ia, uint32_t kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);
-}
-
 // Top-k of the (key, id) pairs a wave holds, PER per lane (a power of two;
-// key 0 marks an empty entry; every id of a lower lane is lower).  Each lane
+// key 0 marks an empty entry; a lane's ids are id[0], id[0] + 1, ... and
+// every id of a lower lane is lower).  Each lane
 // first sorts its pairs into selection order (a bitonic network,
 // compile-time indices only); then every round takes the wave maximum of the
 // lanes' head keys (a DPP wavefront reduction), the lowest lane holding it
@@ -54,7 +49,14 @@ template <int PER>
 __device__ __forceinline__ void topk_select(uint32_t (&key)[PER], int (&id)[PER], int k, int lane,
                                             int& my_e, uint32_t& my_key) {
   static_assert((PER & (PER - 1)) == 0, "PER must be a power of two");
-  // bitonic sort into selection order (position 0 first)
+  // bitonic sort into selection order (position 0 first) on 64-bit words
+  // (key, PER - 1 - position): one 64-bit compare per exchange, and since ids
+  // ascend with the position inside a lane, the lower id first among equal
+  // keys
+  uint64_t kp[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) kp[i] = (static_cast<uint64_t>(key[i]) << 32) | (PER - 1 - i);
+  const int id0 = id[0];
 #pragma unroll
   for (int size = 2; size <= PER; size <<= 1) {
 #pragma unroll
@@ -65,15 +67,18 @@ __device__ __forceinline__ void topk_select(uint32_t (&key)[PER], int (&id)[PER]
         if (j > i) {
           // runs of `size` alternate direction; the last merge is forward
           const bool fwd = (i & size) == 0;
-          const bool sw = fwd ? topk_before(key[j], id[j], key[i], id[i])
-                              : topk_before(key[i], id[i], key[j], id[j]);
-          const uint32_t ki = key[i], kj = key[j];
-          const int ii = id[i], ij = id[j];
-          key[i] = sw ? kj : ki; key[j] = sw ? ki : kj;
-          id[i] = sw ? ij : ii;  id[j] = sw ? ii : ij;
+          const bool sw = fwd ? kp[j] > kp[i] : kp[i] > kp[j];
+          const uint64_t a = kp[i], b = kp[j];
+          kp[i] = sw ? b : a;
+          kp[j] = sw ? a : b;
         }
       }
     }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    key[i] = static_cast<uint32_t>(kp[i] >> 32);
+    id[i] = id0 + (PER - 1 - static_cast<int>(kp[i] & 0xFFFFFFFFu));
   }
   my_e = 0;
   my_key = 0;
