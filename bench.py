@@ -18,7 +18,6 @@ an error: this build runs on one GPU.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -470,7 +469,8 @@ def pmc_traffic(name: str, kernel: str):
     """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, each scaled
     by its copy-kernel calibration) from the committed counter summary
     profiles/<name>; None when the file is absent or when the kernel's
-    sources no longer hash to what they were when the counters were taken."""
+    sources (comments aside) no longer hash to what they were when the
+    counters were taken."""
     path = os.path.join(ROOT, "profiles", name)
     try:
         lines = open(path).read().splitlines()
@@ -480,13 +480,12 @@ def pmc_traffic(name: str, kernel: str):
     srcs = kv.get("sources", "").split()
     if kv.get("kernel") != kernel or not srcs:
         return None
-    h = hashlib.sha256()
-    for f in srcs:
-        try:
-            h.update(open(os.path.join(ROOT, f), "rb").read())
-        except OSError:
-            return None
-    if h.hexdigest() != kv.get("source_sha256"):
+    from bit_quantized_expert_router_amd.profsum import code_sha256
+    try:
+        sha = code_sha256([os.path.join(ROOT, f) for f in srcs])
+    except OSError:
+        return None
+    if sha != kv.get("source_sha256"):
         return None
     return float(kv["traffic_bytes_per_launch"])
 

@@ -17,9 +17,9 @@
 //            gate and of up each): A = the item's gathered x rows (fp16,
 //            staged in LDS, double buffered per 256-column K tile), B = the
 //            expert's gate and up tiles dequantized in registers (each weight
-//            is dequantized once per item and used by every M tile; a ring
-//            of four register sets keeps the next three K tiles' weights in
-//            flight while one is multiplied),
+//            is dequantized once per item and used by every M tile; two
+//            register sets keep the next K tile's weights in flight while
+//            one is multiplied),
 //            v_mfma_f32_16x16x32_f16, SwiGLU epilogue:
 //            h~[row] = w * silu(g) * u * s_t^2  (fp16, sorted-row order).
 //   down     work item x 256-row block of H, 8 waves x 2 row tiles: A = h~

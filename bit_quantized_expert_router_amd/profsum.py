@@ -12,8 +12,9 @@
       dispatch).  Each counter is scaled by the factor that makes it read N
       bytes on the largest device-to-device copy kernel of the same run (a
       plain copy of N bytes reads N and writes N).  With --sources, the
-      sha256 of those files is printed so that a reader can tell whether the
-      kernel has changed since the counters were taken.
+      sha256 of those files (comments and blank lines removed) is printed so
+      that a reader can tell whether the kernel has changed since the
+      counters were taken.
 
 Reads CSV only; runs nothing.
 """
@@ -72,10 +73,39 @@ def counter_per_dispatch(root: str, counter: str) -> dict[str, list[float]]:
     return out
 
 
-def sha256_of(paths) -> str:
+def strip_comments(text: str) -> str:
+    """C/C++ source without its comments and blank lines, and with trailing
+    spaces removed: what the compiler sees, up to layout.  String and
+    character literals are kept as they are (a `//` inside one is code)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c and text[j] != "\n":
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    lines = (l.rstrip() for l in "".join(out).splitlines())
+    return "\n".join(l for l in lines if l) + "\n"
+
+
+def code_sha256(paths) -> str:
+    """sha256 over the listed sources with comments and blank lines removed,
+    so that a change of comments alone does not mark counters as stale."""
     h = hashlib.sha256()
     for p in paths:
-        h.update(open(p, "rb").read())
+        h.update(strip_comments(open(p, encoding="utf-8").read()).encode())
     return h.hexdigest()
 
 
@@ -124,7 +154,7 @@ def main(argv=None):
     print(f"traffic_bytes_per_launch: {res['fetch'][5] + res['write'][5]:.0f}")
     if a.sources:
         print(f"sources: {' '.join(a.sources)}")
-        print(f"source_sha256: {sha256_of(a.sources)}")
+        print(f"source_sha256: {code_sha256(a.sources)}")
 
 
 if __name__ == "__main__":

@@ -1,0 +1,49 @@
+"""Host-side helpers that read rocprofv3 output: the comment-free source hash
+that ties a committed counter summary to the kernel it was measured on, and
+bench.py's use of it."""
+import os
+
+from bit_quantized_expert_router_amd.profsum import code_sha256, strip_comments
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_strip_comments_keeps_code_and_literals():
+    src = ('#include "a.h"  // header\n'
+           '/* block\n   comment */ int x = 1;   \n'
+           '\n'
+           'const char* s = "http://x /* not */";  // tail\n'
+           "char c = '/'; int y = 2 / 3; /* a */ int z;\n")
+    assert strip_comments(src) == ('#include "a.h"\n'
+                                   '  int x = 1;\n'
+                                   'const char* s = "http://x /* not */";\n'
+                                   "char c = '/'; int y = 2 / 3;   int z;\n")
+
+
+def test_code_sha_ignores_comments_only(tmp_path):
+    a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"
+    a.write_text("int f() { return 1; }  // one\n")
+    b.write_text("// a different note\n\nint f() { return 1; }\n")
+    c.write_text("int f() { return 2; }  // one\n")
+    assert code_sha256([a]) == code_sha256([b])
+    assert code_sha256([a]) != code_sha256([c])
+    assert code_sha256([a, c]) != code_sha256([c, a])
+
+
+def test_bench_reads_traffic_only_for_matching_sources(tmp_path, monkeypatch):
+    import bench
+    src = tmp_path / "k.hip"
+    src.write_text("__global__ void k() {}\n")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    body = ("kernel: k\ntraffic_bytes_per_launch: 1234\nsources: k.hip\n"
+            f"source_sha256: {code_sha256([src])}\n")
+    (prof / "t.txt").write_text(body)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.pmc_traffic("t.txt", "k") == 1234.0
+    assert bench.pmc_traffic("t.txt", "other") is None
+    src.write_text("// note\n__global__ void k() {}\n")
+    assert bench.pmc_traffic("t.txt", "k") == 1234.0
+    src.write_text("__global__ void k() { }\n")
+    assert bench.pmc_traffic("t.txt", "k") is None
+    assert bench.pmc_traffic("missing.txt", "k") is None
