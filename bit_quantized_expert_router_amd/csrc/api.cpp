@@ -259,7 +259,7 @@ int moe_route_topk_gemv(const void* x, int32_t x_dtype, int32_t T, const uint16_
 }
 
 static int check_forward(const moe_q2_layer* layer, const void* x, int32_t x_dtype, int32_t T,
-                         const int32_t* ids, const float* w, int32_t k, const void* out,
+                         const int32_t* ids, const float* w, int32_t k, const void* residual, const void* out,
                          int32_t out_dtype, uint32_t flags, void* workspace) {
   int st = check_layer(layer, k);
   if (st) return st;
@@ -270,8 +270,9 @@ static int check_forward(const moe_q2_layer* layer, const void* x, int32_t x_dty
   if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1");
   if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is required");
   if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ids, 4) || !aligned(w, 4))
-    return fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned, topk_ids and topk_w 4-byte aligned");
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(residual, 16) || !aligned(ids, 4) || !aligned(w, 4))
+    return fail(MOE_ERR_INVALID_ARG,
+                "x, out and residual must be 16-byte aligned, topk_ids and topk_w 4-byte aligned");
   return MOE_OK;
 }
 
@@ -279,7 +280,7 @@ int moe_expert_forward_decode(const moe_q2_layer* layer, const void* x, int32_t 
                               int32_t T, const int32_t* topk_ids, const float* topk_w, int32_t k,
                               const void* residual, void* out, int32_t out_dtype, uint32_t flags,
                               void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_forward(layer, x, x_dtype, T, topk_ids, topk_w, k, out, out_dtype, flags, workspace);
+  int st = check_forward(layer, x, x_dtype, T, topk_ids, topk_w, k, residual, out, out_dtype, flags, workspace);
   if (st) return st;
   if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "decode takes at most 8 tokens");
   const size_t need = decode_workspace_bytes(T, k, layer->hidden, layer->inter);
@@ -303,7 +304,7 @@ int moe_expert_forward_decode_routed(const moe_q2_layer* layer, const void* x, i
     return fail(MOE_ERR_INVALID_ARG, "logits, topk_ids and topk_w must be 4-byte aligned");
   // the routing outputs are optional here, so check the rest with stand-ins
   int st = check_forward(layer, x, x_dtype, T, reinterpret_cast<const int32_t*>(logits), logits, k,
-                         out, out_dtype, flags, workspace);
+                         residual, out, out_dtype, flags, workspace);
   if (st) return st;
   if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "decode takes at most 8 tokens");
   const size_t need = decode_workspace_bytes(T, k, layer->hidden, layer->inter);
@@ -321,7 +322,7 @@ int moe_expert_forward_prefill(const moe_q2_layer* layer, const void* x, int32_t
                                const int32_t* sorted_pairs, const int32_t* pair_pos,
                                const void* residual, void* out, int32_t out_dtype, uint32_t flags,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_forward(layer, x, x_dtype, T, topk_ids, topk_w, k, out, out_dtype, flags, workspace);
+  int st = check_forward(layer, x, x_dtype, T, topk_ids, topk_w, k, residual, out, out_dtype, flags, workspace);
   if (st) return st;
   if (!counts || !offsets || !sorted_pairs || !pair_pos)
     return fail(MOE_ERR_INVALID_ARG, "counts, offsets, sorted_pairs and pair_pos are required");

@@ -99,44 +99,90 @@ __device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e)
 }
 
 // --------------------------------------------------------------------- prep --
+constexpr int kPrepTokensPerBlock = 4;                // one wave per token
+
+// One x row as 8-element chunks (16 bytes of bf16 or 32 of fp32); lane l
+// holds chunks l, l + 64, ... (at most NCL of them) in registers, so the row
+// is read once.
+template <bool BF16>
+__device__ __forceinline__ void load_x_chunk(const void* x, size_t e0, u32x4 (&r)[2]) {
+  if constexpr (BF16) {
+    r[0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + e0);
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(x) + e0);
+    r[0] = p[0];
+    r[1] = p[1];
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float x_chunk_elem(const u32x4 (&r)[2], int i) {
+  if constexpr (BF16) {
+    const uint32_t w = r[0][i >> 1];   // element 2j is the low half of word j
+    return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  } else {
+    return __uint_as_float(r[i >> 2][i & 3]);
+  }
+}
+
+// x_hat_t = x_t (* rsqrt(mean x_t^2 + 1e-6)) times the power of two s_t that
+// puts max |x_hat_t s_t| in [0.5, 1), stored fp16; unscale[t] = 1 / s_t.
+template <bool BF16, int NCL>
+__device__ void prep_token(const void* __restrict__ x, int t, int H, int prenorm, const PrefillWs& ws) {
+  const int lane = threadIdx.x & 63;
+  const int nch = H >> 3;
+  u32x4 r[NCL][2];
+#pragma unroll
+  for (int i = 0; i < NCL; ++i)
+    if (64 * i + lane < nch) load_x_chunk<BF16>(x, static_cast<size_t>(t) * H + 8 * (64 * i + lane), r[i]);
+  float ss = 0.0f, mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NCL; ++i) {
+    if (64 * i + lane < nch) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = x_chunk_elem<BF16>(r[i], j);
+        ss += v * v;
+        mx = fmaxf(mx, fabsf(v));
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  mx = wave_max(mx);
+  const float rn = prenorm ? 1.0f / sqrtf(ss / static_cast<float>(H) + 1e-6f) : 1.0f;
+  const float sc = pow2_normaliser(mx * rn);
+#pragma unroll
+  for (int i = 0; i < NCL; ++i) {
+    if (64 * i + lane < nch) {
+      f16x8 h;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = static_cast<_Float16>((x_chunk_elem<BF16>(r[i], j) * rn) * sc);
+      *reinterpret_cast<f16x8*>(ws.x16 + static_cast<size_t>(t) * H + 8 * (64 * i + lane)) = h;
+    }
+  }
+  if (lane == 0) ws.unscale[t] = 1.0f / sc;
+}
+
+// Blocks [0, TB): x_hat of 4 tokens each (TB = ceil(T / 4)); block TB: the
+// work-item list; blocks after it: token and weight of 256 sorted rows each.
+template <bool XBF16, int NCL>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(
-    LayerArgs L, const void* __restrict__ x, int x_bf16, int T, int k, int prenorm,
+    LayerArgs L, const void* __restrict__ x, int T, int k, int prenorm,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, const float* __restrict__ topk_w, int item_cap,
     PrefillWs ws) {
-  __shared__ float s_a[4], s_b[4];
   __shared__ int s_scan[256];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int H = L.H, E = L.E;
   const int P = T * k;
-  if (blockIdx.x < T) {
-    const int t = blockIdx.x;
-    float ss = 0.0f, mx = 0.0f;
-    for (int i = threadIdx.x; i < H; i += 256) {
-      const size_t o = static_cast<size_t>(t) * H + i;
-      const float v = x_bf16 ? bf16_to_float(static_cast<const uint16_t*>(x)[o]) : static_cast<const float*>(x)[o];
-      ss += v * v;
-      mx = fmaxf(mx, fabsf(v));
-    }
-    ss = wave_sum(ss);
-    mx = wave_max(mx);
-    if (lane == 0) { s_a[wid] = ss; s_b[wid] = mx; }
-    __syncthreads();
-    ss = s_a[0] + s_a[1] + s_a[2] + s_a[3];
-    mx = fmaxf(fmaxf(s_b[0], s_b[1]), fmaxf(s_b[2], s_b[3]));
-    const float r = prenorm ? 1.0f / sqrtf(ss / static_cast<float>(H) + 1e-6f) : 1.0f;
-    const float s = pow2_normaliser(mx * r);
-    for (int i = threadIdx.x; i < H; i += 256) {
-      const size_t o = static_cast<size_t>(t) * H + i;
-      const float v = x_bf16 ? bf16_to_float(static_cast<const uint16_t*>(x)[o]) : static_cast<const float*>(x)[o];
-      ws.x16[o] = static_cast<_Float16>((v * r) * s);
-    }
-    if (threadIdx.x == 0) ws.unscale[t] = 1.0f / s;
+  const int TB = (T + kPrepTokensPerBlock - 1) / kPrepTokensPerBlock;
+  if (blockIdx.x < TB) {
+    const int t = blockIdx.x * kPrepTokensPerBlock + (threadIdx.x >> 6);
+    if (t < T) prep_token<XBF16, NCL>(x, t, H, prenorm, ws);
     return;
   }
-  if (blockIdx.x > T) {
+  if (blockIdx.x > TB) {
     // token and weight of every sorted row (an invalid entry contributes nothing)
-    const int r = (blockIdx.x - T - 1) * 256 + threadIdx.x;
+    const int r = (blockIdx.x - TB - 1) * 256 + threadIdx.x;
     if (r < P) {
       const int p = sorted_pairs[r];
       const bool ok = p >= 0 && p < P;
@@ -533,38 +579,64 @@ __global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, Pre
 }
 
 // ------------------------------------------------------------------ combine --
+// One thread per (token, 8-column chunk): the token's k rows of y~ (and the
+// shared row) are all requested before the first is summed, in 16-byte loads;
+// the sum runs over j ascending, then the shared row, in fp32.
 __global__ __launch_bounds__(256) void prefill_combine_kernel(
     int T, int H, int k, int has_shared, const int32_t* __restrict__ pair_pos,
-    const void* __restrict__ residual, void* __restrict__ out, int out_bf16, PrefillWs ws) {
-  const int t = blockIdx.x;
+    const void* residual, void* out, int out_bf16, PrefillWs ws) {   // residual may alias out
+  const int nch = H >> 3;
+  const long long g = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g >= static_cast<long long>(T) * nch) return;
+  const int t = static_cast<int>(g / nch);
+  const int c = static_cast<int>(g - static_cast<long long>(t) * nch);
   const int P = T * k;
+  int pos[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j)
+    pos[j] = j < k ? min(max(pair_pos[static_cast<size_t>(t) * k + j], 0), P - 1) : 0;
+  f16x8 v[MOE_MAX_TOPK + 1];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j)
+    if (j < k) v[j] = *reinterpret_cast<const f16x8*>(ws.y + static_cast<size_t>(pos[j]) * H + 8 * c);
+  if (has_shared) v[MOE_MAX_TOPK] = *reinterpret_cast<const f16x8*>(ws.y + static_cast<size_t>(P + t) * H + 8 * c);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j)
+    if (j < k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += static_cast<float>(v[j][i]);
+  if (has_shared)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += static_cast<float>(v[MOE_MAX_TOPK][i]);
   const float u = ws.unscale[t];
   const float u2 = u * u;
-  for (int c8 = threadIdx.x; c8 < H / 8; c8 += blockDim.x) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int pos = min(max(pair_pos[static_cast<size_t>(t) * k + j], 0), P - 1);
-      const f16x8 v = *reinterpret_cast<const f16x8*>(ws.y + static_cast<size_t>(pos) * H + c8 * 8);
+  const size_t o = static_cast<size_t>(t) * H + 8 * c;
+  if (out_bf16) {
+    u32x4 rs = {0u, 0u, 0u, 0u}, w;
+    if (residual) rs = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(residual) + o);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += static_cast<float>(v[i]);
-    }
-    if (has_shared) {
-      const f16x8 v = *reinterpret_cast<const f16x8*>(ws.y + static_cast<size_t>(P + t) * H + c8 * 8);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += static_cast<float>(v[i]);
-    }
-    const size_t o = static_cast<size_t>(t) * H + c8 * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float v = acc[i] * u2;
-      if (out_bf16) {
-        if (residual) v += bf16_to_float(static_cast<const uint16_t*>(residual)[o + i]);
-        static_cast<uint16_t*>(out)[o + i] = float_to_bf16(v);
-      } else {
-        if (residual) v += static_cast<const float*>(residual)[o + i];
-        static_cast<float*>(out)[o + i] = v;
+    for (int q = 0; q < 4; ++q) {
+      float lo = acc[2 * q] * u2, hi = acc[2 * q + 1] * u2;
+      if (residual) {
+        lo += __uint_as_float(rs[q] << 16);
+        hi += __uint_as_float(rs[q] & 0xFFFF0000u);
       }
+      w[q] = static_cast<uint32_t>(float_to_bf16(lo)) | (static_cast<uint32_t>(float_to_bf16(hi)) << 16);
     }
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + o) = w;
+  } else {
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] = acc[i] * u2; b[i] = acc[4 + i] * u2; }
+    if (residual) {
+      const f32x4* rp = reinterpret_cast<const f32x4*>(static_cast<const float*>(residual) + o);
+      a += rp[0];
+      b += rp[1];
+    }
+    f32x4* op = reinterpret_cast<f32x4*>(static_cast<float*>(out) + o);
+    op[0] = a;
+    op[1] = b;
   }
 }
 
@@ -589,9 +661,22 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
   const long long rows = static_cast<long long>(T) * k + T;
   hipError_t e;
   {
-    const int grid = T + 1 + static_cast<int>((rows + 255) / 256);
-    e = launch_kernel(K_PREFILL_PREP, prefill_prep_kernel, dim3(grid), dim3(256), 0, s, L, x,
-                      x_bf16, T, k, prenorm, counts, offsets, sorted_pairs, w, nitems, ws);
+    const int grid = (T + kPrepTokensPerBlock - 1) / kPrepTokensPerBlock + 1 + static_cast<int>((rows + 255) / 256);
+    // chunks of 8 elements per lane: H / 512, rounded up to a kernel variant
+    const int ncl = (L.H / 8 + 63) / 64;
+    auto prep = [&](auto xbf16, auto n) {
+      return launch_kernel(K_PREFILL_PREP, prefill_prep_kernel<decltype(xbf16)::value, decltype(n)::value>,
+                           dim3(grid), dim3(256), 0, s, L, x, T, k, prenorm, counts, offsets, sorted_pairs,
+                           w, nitems, ws);
+    };
+    using B1 = std::true_type;
+    using B0 = std::false_type;
+    using N2 = std::integral_constant<int, 2>;
+    using N6 = std::integral_constant<int, 6>;
+    using N16 = std::integral_constant<int, MOE_MAX_DIM / 512>;
+    if (ncl <= 2) e = x_bf16 ? prep(B1{}, N2{}) : prep(B0{}, N2{});
+    else if (ncl <= 6) e = x_bf16 ? prep(B1{}, N6{}) : prep(B0{}, N6{});
+    else e = x_bf16 ? prep(B1{}, N16{}) : prep(B0{}, N16{});
   }
   if (e != hipSuccess) return e;
   {
@@ -620,7 +705,9 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
     }
   }
   if (e != hipSuccess) return e;
-  return launch_kernel(K_PREFILL_COMBINE, prefill_combine_kernel, dim3(T), dim3(256), 0, s, T,
+  const long long nthr = static_cast<long long>(T) * (L.H / 8);
+  return launch_kernel(K_PREFILL_COMBINE, prefill_combine_kernel, dim3(static_cast<int>((nthr + 255) / 256)),
+                       dim3(256), 0, s, T,
                        L.H, k, L.shared ? 1 : 0, pair_pos, residual, out, out_bf16, ws);
 }
 

@@ -162,6 +162,7 @@ def test_forward_validation(lib, which):
     assert forward(lib, which, ws=None) == -3
     assert forward(lib, which, wsb=100) == -3
     assert forward(lib, which, ws=FAKE + 8) == -1
+    assert forward(lib, which, res=FAKE + 8) == -1         # unaligned residual
     if which in ("decode", "routed"):
         assert forward(lib, which, T=9) == -2
     if which == "routed":

@@ -398,6 +398,31 @@ def test_prefill_small_config_all_tokens(B, layer_small):
     check_out(to_np(out) - res, ref - res, "prefill cfg0 shapes prenorm+residual")
 
 
+@pytest.mark.parametrize("H,xdt,odt", [(1024, "bf16", torch.bfloat16), (4096, "f32", torch.bfloat16),
+                                        (8192, "bf16", torch.float32)])
+def test_prefill_widths_dtypes_residual(B, H, xdt, odt):
+    """Every x-row staging width (H/512 chunks per lane: <= 2, <= 6, <= 16),
+    fp32 and bf16 x, bf16 and fp32 out, pre-norm and a residual in the
+    output dtype."""
+    L = Layer(B, 8, 8, H, 256)
+    T = 45
+    rng = synth.rng_for(8, T, H)
+    xd, xv = synth.activations(rng, T, H, xdt)
+    ids, w, r = route_both(B, rng.standard_normal((T, 8)).astype(np.float32), 3, True)
+    res = (rng.standard_normal((T, H)) * 0.5).astype(np.float32)
+    if odt == torch.bfloat16:
+        resd = dev(res).to(torch.bfloat16)
+        res = synth.bf16_to_f32(synth.bf16_bits(res)).astype(np.float64)
+    else:
+        resd = dev(res)
+    out = run_prefill(B, L, dev_x(xd, xdt), r, odt, resd, B.MOE_FLAG_PRENORM_RMS)
+    ref = O.moe_layer(xv, ids, w, L.ref, prenorm=True, residual=res)
+    if odt == torch.bfloat16:
+        check_out(to_np(out), ref, f"prefill H={H} x {xdt} bf16 out + residual")
+    else:
+        check_out(to_np(out) - res, ref - res, f"prefill H={H} x {xdt} fp32 out + residual")
+
+
 def test_decode_prefill_agree(B, layer_full):
     L = layer_full
     rng = synth.rng_for(1, 3, 40)
