@@ -50,7 +50,27 @@ def parse():
                     help="layers of the stacked decode/prefill runs (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the device-ceiling microbenchmarks (moe_ceilings)")
     return ap.parse_args()
+
+
+def device_ceilings():
+    """Streaming-read, dispatch, MFMA and dequant ceilings measured by the
+    moe_ceilings program (a child process, run before this process touches
+    the GPU); None when it is not built or fails."""
+    import subprocess
+    exe = os.path.join(ROOT, "bit_quantized_expert_router_amd", "moe_ceilings")
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=180)
+    except subprocess.TimeoutExpired:
+        return None
+    if r.returncode != 0:
+        print(f"bench.py: moe_ceilings failed: {r.stderr.strip()[-300:]}", file=sys.stderr)
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def main():
@@ -59,6 +79,8 @@ def main():
         print("bench.py: this build runs the MoE layer on one GPU only; "
               "--gpus must be 1 (no multi-GPU path is built)", file=sys.stderr)
         sys.exit(2)
+
+    ceilings = None if (args.no_ceilings or args.only) else device_ceilings()
 
     import torch
     from bit_quantized_expert_router_amd import binding as B
@@ -458,6 +480,10 @@ def main():
             "kernel_us": round(d["kernel_ms"]["decode_gateup"] * 1e3, 3),
             "layer_GBps": round(d["GBps"], 1), "layer_frac": round(d["hbm_frac"], 4),
         }
+    if ceilings:
+        line["ceilings"] = ceilings
+        if "roofline" in line:
+            line["roofline"]["measured_stream_GBps"] = ceilings["stream_read_GBps"]
     line["results"] = results
     if cpu:
         line["cpu_baseline"] = cpu

@@ -1,5 +1,6 @@
 """Builds libmoe_q2.so (the HIP library behind the C ABI in include/moe_q2.h)
-for gfx950 with hipcc.  Run as a module or call build()."""
+and the moe_ceilings microbenchmark program for gfx950 with hipcc.  Run as a
+module or call build()."""
 from __future__ import annotations
 
 import os
@@ -12,6 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_q2.so")
+CEILINGS = os.path.join(PKG, "moe_ceilings")        # standalone device-ceiling microbenchmarks
 SOURCES = ["route.hip", "decode.hip", "prefill.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -48,6 +50,16 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    # VGPR-form MFMA operands: otherwise the probe's loop-carried accumulators
+    # are shuffled through AGPR copies every iteration and the probe measures those
+    cmd = [HIPCC, *[f for f in COMMON if f != "-fPIC"], "-mllvm", "-amdgpu-mfma-vgpr-form",
+           os.path.join(CSRC, "ceilings.hip"), "-o", CEILINGS + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on ceilings.hip:\n{r.stdout}{r.stderr}")
+    os.replace(CEILINGS + ".tmp", CEILINGS)
     return LIB
 
 
