@@ -131,6 +131,28 @@ __device__ void build_slots(const int32_t* ids, const float* w, int T, int k, in
   }
 }
 
+// The slot list of one token's own top-k, from the routing wave's registers
+// (lane i < k holds the i-th selected expert and its weight): the ids are
+// distinct, so slot i is pair i and the shared expert takes slot k -- the
+// list build_slots makes for these pairs, without reading them back from LDS.
+__device__ void slots_one_token(DecodeSlots& S, int e, float wt, int k, bool has_shared) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if (lane <= k) {
+#pragma unroll
+    for (int t = 1; t < kMaxT; ++t) S.pidx[lane][t] = -1;
+  }
+  if (lane < k) {
+    S.expert[lane] = e;
+    S.pidx[lane][0] = lane;
+    S.wpair[lane] = wt;
+  } else if (lane == k) {
+    S.expert[k] = -1;
+    S.pidx[k][0] = has_shared ? k : -1;
+    if (has_shared) S.wpair[k] = 1.0f;
+  }
+  if (lane == 0) S.n = k + (has_shared ? 1 : 0);
+}
+
 // Token of x chunk c (chunks of 8 values, cpt chunks per token).
 __device__ __forceinline__ int token_of_chunk(int c, int cpt) {
   int t = 0;
@@ -191,14 +213,16 @@ __device__ __forceinline__ void issue_x(const void* x, int nch, bool xreg, u32x4
 template <int RPER>
 __device__ __forceinline__ void route_topk_waves(const LayerArgs& L, int T, int k,
                                                  const float* logits, int32_t* ids_out,
-                                                 float* w_out, int32_t* s_rid, float* s_rw) {
+                                                 float* w_out, int32_t* s_rid, float* s_rw,
+                                                 int& my_e, float& wt) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = wave_id();
+  my_e = -1;
+  wt = 0.0f;
   if (wid < T) {
-    int my_e;
     float l;
     topk_one_token<RPER>(logits + static_cast<size_t>(wid) * L.E, L.E, k, lane, my_e, l);
-    const float wt = topk_weight(l, k, lane);
+    wt = topk_weight(l, k, lane);
     if (lane < k) {
       s_rid[wid * k + lane] = my_e;
       s_rw[wid * k + lane] = wt;
@@ -529,7 +553,10 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
   if (wid >= xw0) issue_x<BF16, XC>(x, nch, xreg, xr, xt, nxt);
   if (wid < T) {
     if constexpr (RPER > 0) {
-      route_topk_waves<RPER>(L, T, k, logits, ids_out, w_out, s_rid, s_rw);
+      int my_e;
+      float wt;
+      route_topk_waves<RPER>(L, T, k, logits, ids_out, w_out, s_rid, s_rw, my_e, wt);
+      if (T == 1) slots_one_token(S, my_e, wt, k, L.shared != nullptr);
     } else {
       if (wid == 0) build_slots(ids, w, T, k, L.E, L.shared != nullptr, S, s_slot_of, false);
     }
@@ -551,7 +578,7 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
       for (int t = 0; t < kMaxT; ++t) s_smul[t] = smul[t];
     }
     if constexpr (RPER > 0) {
-      if (wid == 0) build_slots(s_rid, s_rw, T, k, L.E, L.shared != nullptr, S, s_slot_of, T == 1);
+      if (wid == 0 && T > 1) build_slots(s_rid, s_rw, T, k, L.E, L.shared != nullptr, S, s_slot_of, false);
     }
     if (wid >= xw0) stage_x<BF16, XC>(x, T, H, xreg, xr, rmul, smul, xs, xt, nxt);
   }
