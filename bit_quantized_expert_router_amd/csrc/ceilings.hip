@@ -9,9 +9,10 @@
 //                 wave, operands in registers), the shader clock it ran at
 //                 (loaded and with one wave) and the cycles between two
 //                 independent MFMAs of one wave
-//   dequant_mfma  the inner step of the gate/up kernels for a one-M-tile item
-//                 with its operands in registers: Q2 tile dequantization and
-//                 the two MFMAs per 32-weight block, in weights per second
+//   dequant_mfma  the inner step of the gate/up kernels with its operands in
+//                 registers: Q2 tile dequantization and two MFMAs per
+//                 32-weight block and M tile, for items of one and of four
+//                 M tiles, in weights per second
 // Standalone program; it shares only q2_device.h with the library.
 #include <hip/hip_runtime.h>
 
@@ -95,8 +96,9 @@ __global__ __launch_bounds__(256) void mfma_probe(int iters, float* out, unsigne
 }
 
 // Every iteration dequantizes the 8 blocks of one gate and one up tile for
-// this lane (128 weights) and multiplies each block into one M tile (2 MFMAs
-// per block), as the gate/up kernels do for an item of at most 16 rows.
+// this lane (128 weights) and multiplies each block into NMT M tiles (2 NMT
+// MFMAs per block), as the gate/up kernels do for an item of NMT 16-row tiles.
+template <int NMT>
 __global__ __launch_bounds__(256) void dequant_probe(int iters, uint32_t seed, float* out) {
   u32x4 cg, sg, cu, su;
 #pragma unroll
@@ -106,22 +108,31 @@ __global__ __launch_bounds__(256) void dequant_probe(int iters, uint32_t seed, f
     sg[i] = 0x24002400u ^ ((threadIdx.x + i) & 0x00030003u);   // fp16 scales near 0.0156
     su[i] = sg[i] ^ 0x00010001u;
   }
-  f16x8 a;
+  f16x8 a[NMT];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = static_cast<_Float16>(0.01f * static_cast<float>(i + 1));
-  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = accg;
+  for (int m = 0; m < NMT; ++m)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[m][i] = static_cast<_Float16>(0.01f * static_cast<float>(i + 1 + m));
+  f32x4 accg[NMT], accu[NMT];
+#pragma unroll
+  for (int m = 0; m < NMT; ++m) { accg[m] = f32x4{0.f, 0.f, 0.f, 0.f}; accu[m] = accg[m]; }
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const f16x8 bg = moeq2::tile_block_weights(cg, sg, j);
       const f16x8 bu = moeq2::tile_block_weights(cu, su, j);
-      accg = moeq2::mfma16(a, bg, accg);
-      accu = moeq2::mfma16(a, bu, accu);
+#pragma unroll
+      for (int m = 0; m < NMT; ++m) {
+        accg[m] = moeq2::mfma16(a[m], bg, accg[m]);
+        accu[m] = moeq2::mfma16(a[m], bu, accu[m]);
+      }
     }
     cg += u32x4{1u, 3u, 5u, 7u};   // new codes each iteration (not hoisted)
     cu += u32x4{7u, 5u, 3u, 1u};
   }
-  const float s = accg[0] + accu[1];
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < NMT; ++m) s += accg[m][0] + accu[m][1];
   if (s == 1234.5f) out[0] = s;
 }
 
@@ -234,21 +245,26 @@ int main() {
   const double cycles_per_mfma = static_cast<double>(h_clk[0]) / (8.0 * mfma_iters);
   CK(hipFree(d_clk));
 
-  // dequant + MFMAs of a one-M-tile step
+  // dequant + MFMAs of a one- and a four-M-tile step
   const int dq_iters = 2048;
-  hipLaunchKernelGGL(dequant_probe, dim3(grid), dim3(256), 0, st, 16, 12345u, reinterpret_cast<float*>(d_out));
-  CK(hipEventRecord(e0, st));
-  hipLaunchKernelGGL(dequant_probe, dim3(grid), dim3(256), 0, st, dq_iters, 12345u, reinterpret_cast<float*>(d_out));
-  CK(hipEventRecord(e1, st));
-  const double dq_mfma = static_cast<double>(grid) * 256 * dq_iters * 128 / (1e9 * time_ms(e0, e1));
+  auto dq = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, 16, 12345u, fout);
+    CK(hipEventRecord(e0, st));
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, st, dq_iters, 12345u, fout);
+    CK(hipEventRecord(e1, st));
+    return static_cast<double>(grid) * 256 * dq_iters * 128 / (1e9 * time_ms(e0, e1));
+  };
+  const double dq_mfma = dq(dequant_probe<1>);
+  const double dq_mfma4 = dq(dequant_probe<4>);
   CK(hipStreamSynchronize(st));
 
   printf("{\"device\": \"%s\", \"compute_units\": %d, \"stream_read_GBps\": %.1f, \"stream_read_workgroups\": %d, "
          "\"burst_24MiB_us\": %.2f, \"empty_kernel_us_eager\": %.3f, \"empty_kernel_us_graph\": %.3f, "
          "\"mfma_f16_TFLOPs\": %.1f, \"mfma_clock_MHz_loaded\": %.0f, \"mfma_clock_MHz_one_wave\": %.0f, "
-         "\"mfma_16x16x32_f16_cycles\": %.2f, \"dequant_mfma_Gweights_per_s\": %.1f}\n",
+         "\"mfma_16x16x32_f16_cycles\": %.2f, \"dequant_mfma_Gweights_per_s\": %.1f, "
+         "\"dequant_mfma4_Gweights_per_s\": %.1f}\n",
          prop.name, prop.multiProcessorCount, best_gbs, best_wgs, burst_us, eager_us, graph_us, mfma_tf, loaded_mhz,
-         single_mhz, cycles_per_mfma, dq_mfma);
+         single_mhz, cycles_per_mfma, dq_mfma, dq_mfma4);
   CK(hipFree(d_out));
   CK(hipStreamDestroy(st));
   return 0;
