@@ -341,6 +341,29 @@ def test_decode_routed(B, routed_layers, lkey, T, k, kind, xdt):
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("T,k", [(1, 1), (1, 16), (2, 3), (3, 16)])
+def test_no_shared_expert_and_extreme_k(B, T, k):
+    """A layer without a shared expert, with one selected expert per token and
+    with every expert selected (k = E): routed decode, the two-call decode and
+    prefill against the oracle; the two decode forms bitwise equal."""
+    L = Layer(B, 9, 16, 512, 256, shared=False)
+    print(f"no shared expert T={T} k={k}", flush=True)
+    rng = synth.rng_for(42, T, k)
+    xd, xv = synth.activations(rng, T, 512, "f32")
+    lg = rng.standard_normal((T, 16)).astype(np.float32)
+    ids, w = O.route_topk(lg, k)
+    ref = O.moe_layer(xv, ids, w, L.ref)
+    xt = dev_x(xd, "f32")
+    out = torch.empty((T, 512), dtype=torch.float32, device="cuda")
+    ws = B.workspace(B.MOE_OP_DECODE, T, 16, k, 512, 256)
+    B.moe_expert_forward_decode_routed(L.dev, xt, dev(lg), k, out, None, None, None, 0, ws)
+    torch.cuda.synchronize()
+    check_out(to_np(out), ref, f"routed decode, no shared, T={T} k={k}")
+    _, _, r = route_both(B, lg, k, True)
+    assert torch.equal(run_decode(B, L, xt, r), out)
+    check_out(to_np(run_prefill(B, L, xt, r)), ref, f"prefill, no shared, T={T} k={k}")
+
+
 def test_decode_routed_prenorm_residual_bf16(B, layer_full):
     L = layer_full
     rng = synth.rng_for(41, 0, 0)
