@@ -326,11 +326,11 @@ __device__ __forceinline__ void gateup_ktile(const u32x4 (&b)[4], const _Float16
 // the last one or two groups are unrolled with uniform conditions, so no
 // weight load past the last tile is issued.  The caller has published tile 0
 // into s_a[0] and loaded tile 1 into activation register set 1.
-template <int RING, typename LoadB, typename ATileT, typename Mul>
-__device__ __forceinline__ void k_loop(int KT, u32x4 (&b)[RING][4], LoadB load_b, ATileT& A,
+template <int RING, int NB, typename LoadB, typename ATileT, typename Mul>
+__device__ __forceinline__ void k_loop(int KT, u32x4 (&b)[RING][NB], LoadB load_b, ATileT& A,
                                        _Float16 (*s_a)[kATileHalves], Mul mul) {
   static_assert(RING % 2 == 0, "the activation double buffer alternates every step");
-  auto step = [&](auto par, u32x4 (&bs)[4], int kt, bool refill) {
+  auto step = [&](auto par, u32x4 (&bs)[NB], int kt, bool refill) {
     constexpr int P = decltype(par)::value;          // kt % 2
     A.template load<P>(min(kt + 2, KT - 1));
     __builtin_amdgcn_sched_barrier(0);
@@ -367,8 +367,8 @@ __device__ __forceinline__ void k_loop(int KT, u32x4 (&b)[RING][4], LoadB load_b
 // the one it waits for (a runtime loop makes it merge the loop-entry and
 // back-edge states conservatively, which drains the weight prefetch once per
 // iteration).
-template <int KTC, int RING, typename LoadB, typename ATileT, typename Mul, int... KS>
-__device__ __forceinline__ void k_loop_fixed(u32x4 (&b)[RING][4], LoadB load_b, ATileT& A,
+template <int KTC, int RING, int NB, typename LoadB, typename ATileT, typename Mul, int... KS>
+__device__ __forceinline__ void k_loop_fixed(u32x4 (&b)[RING][NB], LoadB load_b, ATileT& A,
                                              _Float16 (*s_a)[kATileHalves], Mul mul,
                                              std::integer_sequence<int, KS...>) {
   static_assert(RING % 2 == 0, "the activation double buffer alternates every step");
@@ -483,8 +483,8 @@ __global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, P
 
 // --------------------------------------------------------------------- down --
 template <int NMT>
-__device__ __forceinline__ void down_ktile(const u32x4 (&b)[4], const _Float16* abuf, int lane,
-                                           f32x4 (&acc)[2][4]) {
+__device__ __forceinline__ void down_ktile(const u32x4 (&b)[2 * kDownRTW], const _Float16* abuf, int lane,
+                                           f32x4 (&acc)[kDownRTW][4]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     f16x8 a[NMT];
@@ -510,7 +510,8 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
       __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(I) * H * 5 / 16)));
   const __amdgpu_buffer_rsrc_t rs = expert_rsrc(expert_base(L, e), 3 * mat);
   const uint32_t down = 2 * mat + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(rt0)) * KT * kTileBytes;
-  auto load_b = [&](u32x4 (&b)[4], int kt) {
+  constexpr int NB = 2 * kDownRTW;   // codes and scales of each row tile
+  auto load_b = [&](u32x4 (&b)[NB], int kt) {
     const uint32_t o = down + static_cast<uint32_t>(min(kt, KT - 1)) * kTileBytes;
 #pragma unroll
     for (int q = 0; q < kDownRTW; ++q) {
@@ -518,7 +519,7 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
       b[2 * q + 1] = load_scales(rs, o + q * KT * kTileBytes, lane);
     }
   };
-  u32x4 b[RING][4];
+  u32x4 b[RING][NB];
 #pragma unroll
   for (int u = 0; u < RING; ++u) load_b(b[u], u);
   ATile<NMT> A;   // the item's h rows are consecutive: a resource over just them
@@ -531,13 +532,13 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
   A.template store<0>(s_a[0]);
   __syncthreads();
 
-  f32x4 acc[2][4];
+  f32x4 acc[kDownRTW][4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int q = 0; q < kDownRTW; ++q)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto mul = [&](const u32x4 (&bs)[4], const _Float16* abuf) {
+  auto mul = [&](const u32x4 (&bs)[NB], const _Float16* abuf) {
     down_ktile<NMT>(bs, abuf, lane, acc);
   };
   if constexpr (KTC > 0)
