@@ -29,6 +29,7 @@
 // Workgroup ids are remapped so that every XCD gets an equal share of the
 // real work and the row blocks of one work item (which read the same A rows)
 // run on the same XCD and share its L2.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -658,8 +659,11 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
                           int out_bf16, int prenorm, void* wsp, hipStream_t s) {
   (void)ids;
   const PrefillWs ws = carve(wsp, T, L.E, k, L.H, L.I);
-  const int nitems = max_items(T, L.E, k);
+  const int nitems = max_items(T, L.E, k);   // capacity of the item list
   const long long rows = static_cast<long long>(T) * k + T;
+  // the GEMM grids cover at most one item per row (every item has a row):
+  // far fewer than the list capacity for short chunks
+  const int grid_items = static_cast<int>(std::min<long long>(nitems, rows));
   hipError_t e;
   {
     const int grid = (T + kPrepTokensPerBlock - 1) / kPrepTokensPerBlock + 1 + static_cast<int>((rows + 255) / 256);
@@ -681,7 +685,7 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
   }
   if (e != hipSuccess) return e;
   {
-    const long long nb = static_cast<long long>(nitems) * (L.I / kGateupRowsPerBlock);
+    const long long nb = static_cast<long long>(grid_items) * (L.I / kGateupRowsPerBlock);
     const int grid = static_cast<int>((nb + 7) / 8 * 8);
     const dim3 g(grid), b(kThreads);
     switch (L.H / kTileCols) {   // fully unrolled K loops for the common widths
@@ -694,7 +698,7 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
   }
   if (e != hipSuccess) return e;
   {
-    const long long nb = static_cast<long long>(nitems) * (L.H / kDownRowsPerBlock);
+    const long long nb = static_cast<long long>(grid_items) * (L.H / kDownRowsPerBlock);
     const int grid = static_cast<int>((nb + 7) / 8 * 8);
     const dim3 g(grid), b(kThreads);
     switch (L.I / kTileCols) {
