@@ -213,6 +213,11 @@ int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t
   const size_t cnt_b = (static_cast<size_t>(chunks) * E * 4 + 255) / 256 * 256;
   int32_t* local = reinterpret_cast<int32_t*>(ws + rank_b);
   int32_t* base = reinterpret_cast<int32_t*>(ws + rank_b + cnt_b);
+  if (route_histogram_fused(T, k)) {   // one chunk: the histogram in the same launch
+    e = launch_route_topk(logits, T, E, k, topk_ids, topk_w, rank, local, s, counts, offsets,
+                          sorted_pairs, pair_pos);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "route_topk launch");
+  }
   if ((e = launch_route_topk(logits, T, E, k, topk_ids, topk_w, rank, local, s)) != hipSuccess)
     return hip_fail(e, "route_topk launch");
   if ((e = launch_route_expert_scan(local, base, E, chunks, counts, s)) != hipSuccess)

@@ -54,8 +54,16 @@ constexpr int kRouteMaxChunkTokens = 256;
 inline __host__ __device__ int route_chunk_tokens(int T) {
   return T <= 4096 ? 16 : (T <= 65536 ? 64 : 256);
 }
+// With rank, local_counts and the four histogram outputs given, and when
+// route_histogram_fused(T, k) holds (one chunk of at most 16 tokens), the
+// histogram is finished in this launch: the scan and scatter launches are
+// then not needed.
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                             int32_t* rank, int32_t* local_counts, hipStream_t s);
+                             int32_t* rank, int32_t* local_counts, hipStream_t s,
+                             int32_t* counts = nullptr, int32_t* offsets = nullptr,
+                             int32_t* sorted_pairs = nullptr, int32_t* pair_pos = nullptr);
+// Whether launch_route_topk finishes the histogram itself for this shape.
+bool route_histogram_fused(int T, int k);
 // Router GEMV (fp64 accumulation, bf16 weight [E][H]) + top-k for T <= 4
 // tokens in one kernel; `counter` is a zeroed word the kernel leaves zeroed.
 hipError_t launch_route_gemv_topk(const void* x, int x_bf16, int T, const uint16_t* W, int E, int H,

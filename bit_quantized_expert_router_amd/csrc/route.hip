@@ -27,13 +27,35 @@ namespace moeq2 {
 
 namespace {
 
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(x, o, kWave);
+    if (lane >= o) x += u;
+  }
+  return x;
+}
+
+// fin (nullable): when one chunk holds every token, the same workgroup also
+// finishes the histogram -- counts, offsets, sorted_pairs and pair_pos, the
+// values the scan and scatter kernels would compute with a single chunk.
+struct RouteFinish {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pairs;
+  int32_t* pair_pos;
+};
+constexpr int kRouteFusedPairs = 16 * MOE_MAX_TOPK;   // one chunk of at most 16 tokens
+
 template <int PER>
 __global__ __launch_bounds__(1024) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int chunk_tokens,
     int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ rank,
-    int32_t* __restrict__ local_counts, int n_chunks) {
+    int32_t* __restrict__ local_counts, int n_chunks, RouteFinish fin) {
   __shared__ int32_t s_ids[kRouteMaxChunkTokens * MOE_MAX_TOPK];
   __shared__ int32_t s_cnt[MOE_MAX_EXPERTS];
+  __shared__ int32_t s_rank[kRouteFusedPairs];
+  __shared__ int32_t s_off[MOE_MAX_EXPERTS];
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const int nwaves = blockDim.x / kWave;
@@ -79,22 +101,40 @@ __global__ __launch_bounds__(1024) void route_topk_kernel(
       const int base = active ? s_cnt[e] : 0;
       __builtin_amdgcn_wave_barrier();
       if (active) rank[static_cast<size_t>(t0) * k + p] = base + before;
+      if (fin.counts && active) s_rank[p] = base + before;
       if (active && before == 0) s_cnt[e] = base + cnt;
       __builtin_amdgcn_wave_barrier();
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    local_counts[static_cast<size_t>(e) * n_chunks + chunk] = s_cnt[e];
-}
-
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(x, o, kWave);
-    if (lane >= o) x += u;
+  if (!fin.counts) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+      local_counts[static_cast<size_t>(e) * n_chunks + chunk] = s_cnt[e];
+    return;
   }
-  return x;
+  // single chunk: offsets = exclusive scan of the counts (wave 0, 64 experts
+  // at a time), then every pair's position (expert-major, stable)
+  if (wid == 0) {
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+      const int e = e0 + lane;
+      const int v = e < E ? s_cnt[e] : 0;
+      const int incl = wave_incl_scan(v, lane);
+      if (e < E) {
+        fin.counts[e] = v;
+        fin.offsets[e] = carry + incl - v;
+        s_off[e] = carry + incl - v;
+      }
+      carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) fin.offsets[E] = carry;
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < nt * k; p += blockDim.x) {
+    const int pos = s_off[s_ids[p]] + s_rank[p];
+    fin.sorted_pairs[pos] = p;
+    fin.pair_pos[p] = pos;
+  }
 }
 
 // One wave per expert: the exclusive scan of its row of the expert-major
@@ -281,15 +321,24 @@ __global__ __launch_bounds__(64 * kGemvWaves) void route_gemv_topk_kernel(
 
 }  // namespace
 
+bool route_histogram_fused(int T, int k) {
+  return (T + route_chunk_tokens(T) - 1) / route_chunk_tokens(T) == 1 && T * k <= kRouteFusedPairs;
+}
+
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                             int32_t* rank, int32_t* local_counts, hipStream_t s) {
+                             int32_t* rank, int32_t* local_counts, hipStream_t s, int32_t* counts,
+                             int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos) {
   const int ct = route_chunk_tokens(T);
   const int n_chunks = (T + ct - 1) / ct;
+  // one chunk of at most 16 tokens: the histogram is finished in the same kernel
+  const RouteFinish fin = (rank && counts && route_histogram_fused(T, k))
+                              ? RouteFinish{counts, offsets, sorted_pairs, pair_pos}
+                              : RouteFinish{nullptr, nullptr, nullptr, nullptr};
   const int threads = T <= 4 ? 64 * T : 1024;
   const int per = (E + kWave - 1) / kWave;
 #define MOE_ROUTE_LAUNCH(P)                                                                 \
   launch_kernel(K_ROUTE_TOPK, route_topk_kernel<P>, dim3(n_chunks), dim3(threads), 0, s, logits, \
-                T, E, k, ct, ids, w, rank, local_counts, n_chunks)
+                T, E, k, ct, ids, w, rank, local_counts, n_chunks, fin)
   if (per <= 1) return MOE_ROUTE_LAUNCH(1);
   if (per <= 2) return MOE_ROUTE_LAUNCH(2);
   if (per <= 4) return MOE_ROUTE_LAUNCH(4);
