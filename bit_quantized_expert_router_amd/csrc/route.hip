@@ -16,7 +16,9 @@
 // wave per expert scans that expert's per-chunk counts (laid out
 // expert-major); a scatter kernel adds each expert's offset (every
 // workgroup scans the E expert totals itself) and writes sorted_pairs and
-// pair_pos.  Only integer arithmetic decides the order.
+// pair_pos.  When one chunk holds every token (T <= 16), its workgroup does
+// the scan and the scatter itself and the other two kernels are not
+// launched.  Only integer arithmetic decides the order.
 #include "launch.h"
 #include "q2_device.h"
 #include "topk_device.h"
