@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--layers", type=int, default=16)
-    ap.add_argument("--prefill-steps", type=int, default=40)
+    ap.add_argument("--prefill-steps", type=int, default=80)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="",
@@ -126,9 +126,14 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / n_steps
 
+    spread = {}
+
     def graphed(fn, n_capture, replays):
         """The same steps captured once into a HIP graph and replayed: one
-        graph holds n_capture consecutive steps (all rotating layers)."""
+        graph holds n_capture consecutive steps (all rotating layers).
+        Returns the mean ms per step; `spread` receives the 10th, 50th and
+        90th percentiles over the replays (each the mean of its n_capture
+        steps)."""
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -137,14 +142,18 @@ def main():
         for _ in range(3):
             g.replay()
         torch.cuda.synchronize()
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        for _ in range(replays):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+        evs[0].record()
+        for r in range(replays):
             g.replay()
-        ev1.record()
+            evs[r + 1].record()
         torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1) / (replays * n_capture)
+        per = np.array([evs[r].elapsed_time(evs[r + 1]) / n_capture for r in range(replays)])
+        ms = evs[0].elapsed_time(evs[-1]) / (replays * n_capture)
+        spread.clear()
+        spread.update({"ms_per_layer_p10": float(np.percentile(per, 10)),
+                       "ms_per_layer_p50": float(np.percentile(per, 50)),
+                       "ms_per_layer_p90": float(np.percentile(per, 90)), "replays": replays})
         del g
         return ms
 
@@ -197,6 +206,7 @@ def main():
         ms_eager = timed(step, n_steps, warmup)
         ncap = 2 * len(layers)
         ms = graphed(step, ncap, max(1, n_steps // ncap))
+        pct = dict(spread)
         kern = hooked(step, n_steps, warmup + n_steps)
         idh = ids.cpu().numpy()
         distinct = np.array([len(np.unique(idh[i])) for i in range(total)])
@@ -219,7 +229,7 @@ def main():
             "T": T, "routing": kind,
             "calls": ("route_topk_gemv (logits) + decode_routed (router GEMV included)" if gemv else
                       "decode_routed" if routed else "route_topk+decode"),
-            "launch": "hip_graph", "ms_per_layer": ms,
+            "launch": "hip_graph", "ms_per_layer": ms, **pct,
             "ms_per_layer_eager": ms_eager, "tokens_per_s": T * 1000.0 / ms,
             "tokens_per_s_eager": T * 1000.0 / ms_eager,
             "distinct_experts_per_step": float(slots - 1),
@@ -258,6 +268,7 @@ def main():
 
         ms_eager = timed(step, n_steps, warmup)
         ms = graphed(step, len(layers), max(1, n_steps // len(layers)))
+        pct = dict(spread)
         kern = hooked(step, n_steps, warmup + n_steps)
         nonempty = []
         for v in range(nvar):
@@ -273,7 +284,7 @@ def main():
         gu_flops = (T * K + T) * 2 * 2 * H * I
         gu_bytes = (ne + 1) * 2 * MAT_BYTES + T * H * 2 + (T * K + T) * I * 2   # weights, x, h
         return {
-            "T": T, "routing": "router+bias N(0,0.5)", "launch": "hip_graph", "ms_per_layer": ms,
+            "T": T, "routing": "router+bias N(0,0.5)", "launch": "hip_graph", "ms_per_layer": ms, **pct,
             "ms_per_layer_eager": ms_eager, "tokens_per_s": T * 1000.0 / ms,
             "tokens_per_s_eager": T * 1000.0 / ms_eager, "nonempty_experts": ne,
             "algorithmic_bytes_per_step": float(step_bytes), "flops_per_step": float(flops),
