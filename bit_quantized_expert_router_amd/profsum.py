@@ -5,6 +5,12 @@
       `*kernel_stats.csv` that `rocprofv3 --kernel-trace --stats
       --output-format csv -d DIR` writes.
 
+  python -m bit_quantized_expert_router_amd.profsum counters DIR [--match NAME]
+      per-kernel averages of every counter of a `rocprofv3 --pmc` run, with
+      the shader clock and the MFMA-busy and VALU-issue shares of the SIMD
+      cycles when GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU and
+      SQ_INSTS_MFMA were collected.
+
   python -m bit_quantized_expert_router_amd.profsum traffic FETCH_DIR WRITE_DIR
           --kernel NAME --calib-bytes N [--sources FILE ...]
       HBM bytes per dispatch of kernel NAME from two `rocprofv3 --pmc`
@@ -73,6 +79,41 @@ def counter_per_dispatch(root: str, counter: str) -> dict[str, list[float]]:
     return out
 
 
+def counters(root: str, match: str = "prefill", xcds: int = 8, simds: int = 1024) -> list[dict]:
+    """Per kernel (name containing `match`, split by grid size): dispatches,
+    average duration from the trace timestamps, the average of every counter
+    per dispatch, and, with GRBM_GUI_ACTIVE among them (summed over the
+    `xcds` XCD instances), the shader clock and the share of SIMD cycles with
+    the MFMA unit busy (SQ_VALU_MFMA_BUSY_CYCLES) and with non-MFMA VALU
+    instructions issuing (4 cycles each for a wave of 64 on a 16-lane SIMD)."""
+    per: dict = {}
+    dur: dict = {}
+    for f in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            name = _short(r.get("Kernel_Name", ""))
+            if match not in name:
+                continue
+            key = (name, int(r.get("Grid_Size", 0) or 0))
+            did = r.get("Dispatch_Id", "")
+            per.setdefault(key, {}).setdefault(r["Counter_Name"], {})
+            per[key][r["Counter_Name"]][did] = per[key][r["Counter_Name"]].get(did, 0.0) + float(r["Counter_Value"])
+            dur.setdefault(key, {})[did] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    out = []
+    for key in sorted(per):
+        avg = {c: statistics.mean(v.values()) for c, v in per[key].items()}
+        row = {"kernel": key[0], "grid": key[1], "dispatches": len(dur[key]),
+               "avg_us": statistics.mean(dur[key].values()) / 1e3, "counters": avg}
+        if "GRBM_GUI_ACTIVE" in avg:
+            cyc = avg["GRBM_GUI_ACTIVE"] / xcds
+            row["clock_GHz"] = cyc / (row["avg_us"] * 1e3)
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                row["mfma_busy_pct"] = 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * simds)
+            if "SQ_INSTS_VALU" in avg and "SQ_INSTS_MFMA" in avg:
+                row["valu_issue_pct"] = 100.0 * 4 * (avg["SQ_INSTS_VALU"] - avg["SQ_INSTS_MFMA"]) / (cyc * simds)
+        out.append(row)
+    return out
+
+
 def strip_comments(text: str) -> str:
     """C/C++ source without its comments and blank lines, and with trailing
     spaces removed: what the compiler sees, up to layout.  String and
@@ -114,6 +155,9 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--match", default="prefill")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
@@ -121,6 +165,14 @@ def main(argv=None):
     t.add_argument("--calib-bytes", type=int, required=True)
     t.add_argument("--sources", nargs="*", default=[])
     a = ap.parse_args(argv)
+
+    if a.cmd == "counters":
+        for r in counters(a.dir, a.match):
+            derived = "".join(f"  {k} {r[k]:.2f}" for k in ("clock_GHz", "mfma_busy_pct", "valu_issue_pct") if k in r)
+            print(f"{r['kernel']}  grid {r['grid']}  dispatches {r['dispatches']}  avg_us {r['avg_us']:.2f}{derived}")
+            for cn, v in sorted(r["counters"].items()):
+                print(f"    {cn}: {v:.6g}")
+        return
 
     if a.cmd == "stats":
         print(f"{'kernel':<40} {'calls':>7} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'total_ms':>10}")

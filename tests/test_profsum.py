@@ -47,3 +47,29 @@ def test_bench_reads_traffic_only_for_matching_sources(tmp_path, monkeypatch):
     src.write_text("__global__ void k() { }\n")
     assert bench.pmc_traffic("t.txt", "k") is None
     assert bench.pmc_traffic("missing.txt", "k") is None
+
+
+def test_counters_summary(tmp_path):
+    from bit_quantized_expert_router_amd.profsum import counters
+    d = tmp_path / "run"
+    d.mkdir()
+    head = ("Correlation_Id,Dispatch_Id,Grid_Size,Kernel_Name,Counter_Name,Counter_Value,"
+            "Start_Timestamp,End_Timestamp\n")
+    rows = []
+    name = '"void moeq2::(anonymous namespace)::prefill_gateup_kernel<12>(moeq2::LayerArgs)"'
+    for did, t0 in ((1, 1000), (2, 5000)):
+        # 2 us per dispatch; GRBM over 8 XCDs at 2.4 GHz; MFMA busy a quarter of 1024 SIMDs
+        rows.append(f"{did},{did},4096,{name},GRBM_GUI_ACTIVE,{8 * 4800},{t0},{t0 + 2000}")
+        rows.append(f"{did},{did},4096,{name},SQ_VALU_MFMA_BUSY_CYCLES,{4800 * 1024 / 4},{t0},{t0 + 2000}")
+        rows.append(f"{did},{did},4096,{name},SQ_INSTS_MFMA,100,{t0},{t0 + 2000}")
+        rows.append(f"{did},{did},4096,{name},SQ_INSTS_VALU,{100 + 4800 * 1024 / 8 / 4},{t0},{t0 + 2000}")
+    rows.append(f"3,3,64,\"other_kernel\",GRBM_GUI_ACTIVE,1,0,10")
+    (d / "run_counter_collection.csv").write_text(head + "\n".join(rows) + "\n")
+    out = counters(str(tmp_path))
+    assert len(out) == 1
+    r = out[0]
+    assert r["kernel"] == "prefill_gateup_kernel<12>" and r["grid"] == 4096 and r["dispatches"] == 2
+    assert abs(r["avg_us"] - 2.0) < 1e-9
+    assert abs(r["clock_GHz"] - 2.4) < 1e-9
+    assert abs(r["mfma_busy_pct"] - 25.0) < 1e-9
+    assert abs(r["valu_issue_pct"] - 12.5) < 1e-9
