@@ -101,6 +101,7 @@ __device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e)
 
 // --------------------------------------------------------------------- prep --
 constexpr int kPrepTokensPerBlock = 4;                // one wave per token
+constexpr int kSpreadSharedItems = 64;                // shared-expert items spread up to this many
 
 // One x row as 8-element chunks (16 bytes of bf16 or 32 of fp32); lane l
 // holds chunks l, l + 64, ... (at most NCL of them) in registers, so the row
@@ -227,14 +228,49 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     s_scan[threadIdx.x] += v;
     __syncthreads();
   }
+  // For short chunks the shared expert's items (the last ns of the scan,
+  // full 64-row items, the longest in the list) are spread evenly through
+  // it, one before each ns-th of the routed items, so that no XCD's
+  // contiguous range of units gets all of them.  Routed item p goes to
+  // p + floor(p ns / nr) + 1, shared item g to ceil(g nr / ns) + g.  (For
+  // long chunks nearly every item is full and the shared items stay
+  // together, sharing their weights in one L2.)
+  const int total = s_scan[255];
+  const int ns = L.shared ? (T + kGroupRows - 1) / kGroupRows : 0;
+  const int nr = total - ns;
+  const bool spread = ns > 0 && ns <= kSpreadSharedItems && nr > 0;
   int pos = s_scan[threadIdx.x] - local;
-  for (int q = 0; q < per; ++q) {
-    const int e = threadIdx.x * per + q;
-    if (e < nexp) {
-      int r0, n;
-      rows_of(e, r0, n);
-      for (int g = 0; g * kGroupRows < n && pos < item_cap; ++g) {
-        ws.items[pos++] = make_int4(e, r0 + g * kGroupRows, min(kGroupRows, n - g * kGroupRows), 0);
+  if (spread) {
+    // i, ns, nr < 2^16 here: the products fit in 32 bits.  Routed items by
+    // the thread that owns their expert, shared item g by thread g.
+    const uint32_t uns = static_cast<uint32_t>(ns), unr = static_cast<uint32_t>(nr);
+    for (int q = 0; q < per; ++q) {
+      const int e = threadIdx.x * per + q;
+      if (e < E) {
+        int r0, n;
+        rows_of(e, r0, n);
+        for (int g = 0; g * kGroupRows < n; ++g, ++pos) {
+          const uint32_t ui = static_cast<uint32_t>(pos);
+          const int at = static_cast<int>(ui + ui * uns / unr + 1u);
+          if (at < item_cap)
+            ws.items[at] = make_int4(e, r0 + g * kGroupRows, min(kGroupRows, n - g * kGroupRows), 0);
+        }
+      }
+    }
+    for (int g = threadIdx.x; g < ns; g += blockDim.x) {
+      const uint32_t ug = static_cast<uint32_t>(g);
+      const int at = static_cast<int>((ug * unr + uns - 1u) / uns + ug);
+      if (at < item_cap)
+        ws.items[at] = make_int4(E, P + g * kGroupRows, min(kGroupRows, T - g * kGroupRows), 0);
+    }
+  } else {
+    for (int q = 0; q < per; ++q) {
+      const int e = threadIdx.x * per + q;
+      if (e < nexp) {
+        int r0, n;
+        rows_of(e, r0, n);
+        for (int g = 0; g * kGroupRows < n && pos < item_cap; ++g)
+          ws.items[pos++] = make_int4(e, r0 + g * kGroupRows, min(kGroupRows, n - g * kGroupRows), 0);
       }
     }
   }
