@@ -95,13 +95,28 @@ __device__ __forceinline__ int xcd_unit(int bid, int n) {
   return (i < per && u < n) ? u : -1;
 }
 
+// Work item and row block of a GEMM block (item -1: none).  hdr[1] = 0:
+// units item * RB + rb in contiguous ranges per XCD (xcd_unit); hdr[1] = 1:
+// item i on XCD i % 8, the XCD's items in list order, each item's RB row
+// blocks in a row.  The grid covers 8 * ceil(items / 8) * RB blocks.
+__device__ __forceinline__ int2 work_unit(int bid, const int32_t* hdr, int RB) {
+  const int n = hdr[0];
+  if (hdr[1]) {
+    const int j = bid >> 3;
+    const int item = (bid & 7) + 8 * (j / RB);
+    return item < n ? make_int2(item, j % RB) : make_int2(-1, 0);
+  }
+  const int u = xcd_unit(bid, n * RB);
+  return u < 0 ? make_int2(-1, 0) : make_int2(u / RB, u % RB);
+}
+
 __device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e) {
   return e >= L.E ? L.shared : L.experts + static_cast<int64_t>(e) * L.stride;
 }
 
 // --------------------------------------------------------------------- prep --
 constexpr int kPrepTokensPerBlock = 4;                // one wave per token
-constexpr int kSpreadSharedItems = 64;                // shared-expert items spread up to this many
+constexpr int kSizeOrderMaxTokens = 4096;             // chunks up to this long: items by size, dealt round robin
 
 // One x row as 8-element chunks (16 bytes of bf16 or 32 of fp32); lane l
 // holds chunks l, l + 64, ... (at most NCL of them) in registers, so the row
@@ -174,6 +189,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     const int32_t* __restrict__ sorted_pairs, const float* __restrict__ topk_w, int item_cap,
     PrefillWs ws) {
   __shared__ int s_scan[256];
+  __shared__ uint64_t s_scan64[256];
   const int H = L.H, E = L.E;
   const int P = T * k;
   const int TB = (T + kPrepTokensPerBlock - 1) / kPrepTokensPerBlock;
@@ -211,6 +227,63 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
       n = T;
     }
   };
+  if (T <= kSizeOrderMaxTokens) {
+    // Short chunks: items ordered by size class (M tiles: 4, 3, 2, 1), each
+    // class in expert order; the GEMM kernels deal them to the XCDs round
+    // robin, so every XCD gets the same mix of long and short items and
+    // starts with the long ones.  Per-thread counts of the four classes are
+    // scanned together, 16 bits each (every total is below 2^16 here).
+    auto cls = [](int rows) { return 4 - (rows + 15) / 16; };   // 0 = four M tiles
+    uint64_t local = 0;
+    for (int q = 0; q < per; ++q) {
+      const int e = threadIdx.x * per + q;
+      if (e < nexp) {
+        int r0, n;
+        rows_of(e, r0, n);
+        if (n > 0) {
+          const int full = (n - 1) / kGroupRows;                       // 64-row items before the last
+          local += static_cast<uint64_t>(full);
+          local += 1ull << (16 * cls(n - full * kGroupRows));
+        }
+      }
+    }
+    s_scan64[threadIdx.x] = local;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const uint64_t v = threadIdx.x >= o ? s_scan64[threadIdx.x - o] : 0ull;
+      __syncthreads();
+      s_scan64[threadIdx.x] += v;
+      __syncthreads();
+    }
+    const uint64_t tot = s_scan64[255];
+    const uint64_t excl = s_scan64[threadIdx.x] - local;
+    int pos[4];
+    int base = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      pos[c] = base + static_cast<int>((excl >> (16 * c)) & 0xFFFFu);
+      base += static_cast<int>((tot >> (16 * c)) & 0xFFFFu);
+    }
+    for (int q = 0; q < per; ++q) {
+      const int e = threadIdx.x * per + q;
+      if (e < nexp) {
+        int r0, n;
+        rows_of(e, r0, n);
+        for (int g = 0; g * kGroupRows < n; ++g) {
+          const int rows = min(kGroupRows, n - g * kGroupRows);
+          const int at = pos[cls(rows)]++;
+          if (at < item_cap) ws.items[at] = make_int4(e, r0 + g * kGroupRows, rows, 0);
+        }
+      }
+    }
+    if (threadIdx.x == 255) {
+      ws.hdr[0] = min(base, item_cap);
+      ws.hdr[1] = 1;
+    }
+    return;
+  }
+  // Long chunks: items in expert order; the GEMM kernels give each XCD one
+  // contiguous range of units, so an expert's items share an L2.
   int local = 0;
   for (int q = 0; q < per; ++q) {
     const int e = threadIdx.x * per + q;
@@ -228,53 +301,20 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     s_scan[threadIdx.x] += v;
     __syncthreads();
   }
-  // For short chunks the shared expert's items (the last ns of the scan,
-  // full 64-row items, the longest in the list) are spread evenly through
-  // it, one before each ns-th of the routed items, so that no XCD's
-  // contiguous range of units gets all of them.  Routed item p goes to
-  // p + floor(p ns / nr) + 1, shared item g to ceil(g nr / ns) + g.  (For
-  // long chunks nearly every item is full and the shared items stay
-  // together, sharing their weights in one L2.)
-  const int total = s_scan[255];
-  const int ns = L.shared ? (T + kGroupRows - 1) / kGroupRows : 0;
-  const int nr = total - ns;
-  const bool spread = ns > 0 && ns <= kSpreadSharedItems && nr > 0;
   int pos = s_scan[threadIdx.x] - local;
-  if (spread) {
-    // i, ns, nr < 2^16 here: the products fit in 32 bits.  Routed items by
-    // the thread that owns their expert, shared item g by thread g.
-    const uint32_t uns = static_cast<uint32_t>(ns), unr = static_cast<uint32_t>(nr);
-    for (int q = 0; q < per; ++q) {
-      const int e = threadIdx.x * per + q;
-      if (e < E) {
-        int r0, n;
-        rows_of(e, r0, n);
-        for (int g = 0; g * kGroupRows < n; ++g, ++pos) {
-          const uint32_t ui = static_cast<uint32_t>(pos);
-          const int at = static_cast<int>(ui + ui * uns / unr + 1u);
-          if (at < item_cap)
-            ws.items[at] = make_int4(e, r0 + g * kGroupRows, min(kGroupRows, n - g * kGroupRows), 0);
-        }
-      }
-    }
-    for (int g = threadIdx.x; g < ns; g += blockDim.x) {
-      const uint32_t ug = static_cast<uint32_t>(g);
-      const int at = static_cast<int>((ug * unr + uns - 1u) / uns + ug);
-      if (at < item_cap)
-        ws.items[at] = make_int4(E, P + g * kGroupRows, min(kGroupRows, T - g * kGroupRows), 0);
-    }
-  } else {
-    for (int q = 0; q < per; ++q) {
-      const int e = threadIdx.x * per + q;
-      if (e < nexp) {
-        int r0, n;
-        rows_of(e, r0, n);
-        for (int g = 0; g * kGroupRows < n && pos < item_cap; ++g)
-          ws.items[pos++] = make_int4(e, r0 + g * kGroupRows, min(kGroupRows, n - g * kGroupRows), 0);
-      }
+  for (int q = 0; q < per; ++q) {
+    const int e = threadIdx.x * per + q;
+    if (e < nexp) {
+      int r0, n;
+      rows_of(e, r0, n);
+      for (int g = 0; g * kGroupRows < n && pos < item_cap; ++g)
+        ws.items[pos++] = make_int4(e, r0 + g * kGroupRows, min(kGroupRows, n - g * kGroupRows), 0);
     }
   }
-  if (threadIdx.x == 255) ws.hdr[0] = min(s_scan[255], item_cap);
+  if (threadIdx.x == 255) {
+    ws.hdr[0] = min(s_scan[255], item_cap);
+    ws.hdr[1] = 0;
+  }
 }
 
 // A tile staging, fragment-major: the MFMA A fragment of (block j, M tile
@@ -496,10 +536,10 @@ __global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, P
   __shared__ float s_w[kGroupRows];
   __shared__ float s_u[kGroupRows];
   const int RB = L.I / kGateupRowsPerBlock;
-  const int unit = xcd_unit(blockIdx.x, ws.hdr[0] * RB);
-  if (unit < 0) return;
-  const int item = unit / RB;
-  const int rb = unit % RB;
+  const int2 wu = work_unit(blockIdx.x, ws.hdr, RB);
+  if (wu.x < 0) return;
+  const int item = wu.x;
+  const int rb = wu.y;
   const int4 it = ws.items[item];
   const int e = it.x, row0 = it.y, nrows = it.z;
   if (threadIdx.x < nrows) {
@@ -601,10 +641,10 @@ template <int KTC>   // I / 256 when fixed at compile time, else 0
 __global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, PrefillWs ws) {
   __shared__ __align__(16) _Float16 s_a[2][kATileHalves];
   const int RB = L.H / kDownRowsPerBlock;
-  const int unit = xcd_unit(blockIdx.x, ws.hdr[0] * RB);
-  if (unit < 0) return;
-  const int item = unit / RB;
-  const int rb = unit % RB;
+  const int2 wu = work_unit(blockIdx.x, ws.hdr, RB);
+  if (wu.x < 0) return;
+  const int item = wu.x;
+  const int rb = wu.y;
   const int4 it = ws.items[item];
   const int e = it.x, row0 = it.y, nrows = it.z;
   const int rt0 = (rb * kGemmWaves + static_cast<int>(threadIdx.x >> 6)) * kDownRTW;
@@ -721,8 +761,8 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
   }
   if (e != hipSuccess) return e;
   {
-    const long long nb = static_cast<long long>(grid_items) * (L.I / kGateupRowsPerBlock);
-    const int grid = static_cast<int>((nb + 7) / 8 * 8);
+    const long long nb = (static_cast<long long>(grid_items) + 7) / 8 * 8 * (L.I / kGateupRowsPerBlock);
+    const int grid = static_cast<int>(nb);
     const dim3 g(grid), b(kThreads);
     switch (L.H / kTileCols) {   // fully unrolled K loops for the common widths
       case 4: e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel<4>, g, b, 0, s, L, ws, T); break;
@@ -734,8 +774,8 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
   }
   if (e != hipSuccess) return e;
   {
-    const long long nb = static_cast<long long>(grid_items) * (L.H / kDownRowsPerBlock);
-    const int grid = static_cast<int>((nb + 7) / 8 * 8);
+    const long long nb = (static_cast<long long>(grid_items) + 7) / 8 * 8 * (L.H / kDownRowsPerBlock);
+    const int grid = static_cast<int>(nb);
     const dim3 g(grid), b(kThreads);
     switch (L.I / kTileCols) {
       case 1: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<1>, g, b, 0, s, L, ws); break;
