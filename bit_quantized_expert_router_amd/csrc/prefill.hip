@@ -28,7 +28,10 @@
 //            (+ residual), j ascending: fixed order, no atomics.
 // Workgroup ids are remapped so that every XCD gets an equal share of the
 // real work and the row blocks of one work item (which read the same A rows)
-// run on the same XCD and share its L2.
+// run on the same XCD and share its L2.  Chunks of up to 4096 tokens list
+// the items by size (longest first) and deal them to the XCDs in turn;
+// longer chunks list them in expert order and give each XCD one contiguous
+// range, so that an expert's items share its weights in one L2.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
