@@ -478,6 +478,26 @@ def _sampled_prefill(B, L, T, kind, seed, n_sample=12, flags=0):
     check_out(to_np(out[torch.from_numpy(toks).cuda()]), ref, f"prefill T={T} {kind} sampled")
 
 
+@pytest.mark.parametrize("T,shared", [(4096, True), (4096, False), (4097, False), (5000, True)])
+def test_prefill_item_orders(B, T, shared):
+    """Both work-item orders of the prefill kernels: lists in size order dealt
+    to the XCDs in turn (chunks of up to 4096 tokens) and lists in expert
+    order split into contiguous ranges (longer chunks), with and without a
+    shared expert; Zipf routing gives one expert many 64-row items.  Sampled
+    tokens against the oracle."""
+    L = Layer(B, 11, 64, 1024, 256, shared=shared)
+    print(f"prefill item order T={T} shared={shared}", flush=True)
+    rng = synth.rng_for(44, T, int(shared))
+    xd, xv = synth.activations(rng, T, 1024, "bf16")
+    lg = synth.zipf_logits(rng, T, 64)
+    ids, w, r = route_both(B, lg, 4, True)
+    assert_route_exact(ids, w, r, 64, True)
+    out = run_prefill(B, L, dev_x(xd, "bf16"), r)
+    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 30, replace=False)]))
+    ref = O.moe_layer(xv, ids, w, L.ref, tokens=toks)
+    check_out(to_np(out[torch.from_numpy(toks).cuda()]), ref, f"prefill T={T} shared={shared} sampled")
+
+
 def test_prefill_1024_biased_sampled(B, layer_full):
     _sampled_prefill(B, layer_full, 1024, "biased", 0)
 
