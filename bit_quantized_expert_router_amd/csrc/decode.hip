@@ -477,10 +477,10 @@ __device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int
 }
 
 // Sum of the 8 waves' accumulators (wave order) and the output rows of tile
-// rt: out = acc * unscale^2 (+ residual); NaN rows when `poison`.
+// rt: out = acc * unscale^2 (+ residual).
 __device__ void down_store(const f32x4& acc, f32x4 (*s_red)[32], int rt, int T, int H,
                            const float (&unscale)[kMaxT], const void* residual,
-                           void* out, int out_bf16, bool poison) {
+                           void* out, int out_bf16) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = wave_id();
   if (lane < 32) s_red[wid][lane] = acc;
@@ -496,7 +496,6 @@ __device__ void down_store(const f32x4& acc, f32x4 (*s_red)[32], int rt, int T, 
       if (t >= T) break;
       const float u = hi ? unscale[4 + r] : unscale[r];
       float v = Y[r] * (u * u);
-      if (poison) v = __builtin_nanf("");
       const size_t o = static_cast<size_t>(t) * H + row;
       if (out_bf16) {
         if (residual) v += bf16_to_float(static_cast<const uint16_t*>(residual)[o]);
@@ -688,7 +687,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   float uns[kMaxT];
 #pragma unroll
   for (int t = 0; t < kMaxT; ++t) uns[t] = s_uns[t];
-  down_store(acc, s_red, rt, T, L.H, uns, residual, out, out_bf16, false);
+  down_store(acc, s_red, rt, T, L.H, uns, residual, out, out_bf16);
 }
 
 // -------------------------------------------------------------- launching --
