@@ -24,7 +24,7 @@ Sources (the pages are cited by title and section):
     README (bittide.aicompass.dev), section 它是什么; chunk size 1024 tokens --
     "32GB Mac mini ..." section 一.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   R1 tile layout of the 2-bit codes and fp16 scales (our own device format);
   R2 top-k ties go to the lower expert id, output slots in descending logit;
   R3 weights are the softmax over the selected k (== full softmax renormalised);
