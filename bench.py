@@ -13,7 +13,7 @@ and reports them in the same JSON line.  Weights rotate over 16 distinct layers 
 that no step finds its experts in the 256 MB last-level cache.
 
 Prints one JSON line (see the keys below).  `--gpus N` with N > 1 exits with
-an error: this build runs on one GPU.
+an error: the library runs the layer on one GPU.
 """
 from __future__ import annotations
 
@@ -76,7 +76,7 @@ def device_ceilings():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs the MoE layer on one GPU only; "
+        print("bench.py: the library runs the MoE layer on one GPU only; "
               "--gpus must be 1 (no multi-GPU path is built)", file=sys.stderr)
         sys.exit(2)
 

@@ -1,5 +1,5 @@
 // Measured ceilings of the device, printed as one JSON object: the rates the
-// expert-layer kernels are judged against besides the vendor peaks.
+// expert-layer kernels are measured against besides the vendor peaks.
 //   stream_read   HBM streaming read of 1 GiB (four buffers in rotation, so
 //                 nothing is served from the 256 MB MALL), best of three grid
 //                 shapes; and the time of one 24 MiB burst (the weight bytes

@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1,  /* null pointer, bad size, bad alignment      */
-  MOE_ERR_UNSUPPORTED = -2,  /* valid but outside this build's limits      */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but outside the library's limits    */
   MOE_ERR_WORKSPACE = -3,    /* workspace smaller than moe_workspace_bytes */
   MOE_ERR_HIP = -4           /* a kernel launch failed                     */
 } moe_status;
@@ -76,7 +76,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 enum { MOE_OP_ROUTE = 0, MOE_OP_DECODE = 1, MOE_OP_PREFILL = 2, MOE_OP_ROUTE_GEMV = 3 };
 
-/* Limits of this build (validated): */
+/* Limits of the library (validated): */
 #define MOE_MAX_EXPERTS 1024     /* E                                        */
 #define MOE_MAX_TOPK 16          /* k                                        */
 #define MOE_MAX_DECODE_TOKENS 8  /* T of moe_expert_forward_decode           */
