@@ -88,6 +88,8 @@ ROUTE_CASES = [
     (65, 512, 10, "const"), (32768, 512, 10, "zipf"),
     # chunk sizes 32 / 64 / 256 tokens, with and without the fused scan + scatter
     (4096, 512, 10, "biased"), (5000, 64, 4, "normal"), (70000, 64, 4, "normal"),
+    # the single-launch histogram at its limit (one chunk, 256 pairs) and just past it
+    (16, 64, 16, "ties"), (17, 64, 15, "ties"),
 ]
 
 
