@@ -44,8 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="",
-                    help="decode1|decode1_two_calls|decode1_gemv|decode2|decode3|prefill|windows|stack "
-                         "(profiling runs)")
+                    help="decode1|decode1_two_calls|decode1_gemv|decode2|decode3|prefill|prefill32768|"
+                         "windows|stack (profiling runs)")
     ap.add_argument("--stack-layers", type=int, default=48,
                     help="layers of the stacked decode/prefill runs (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -241,14 +241,17 @@ def main():
         }
 
     # --------------------------------------------------------------- prefill
-    def prefill_case(T, n_steps, warmup):
+    def prefill_case(T, n_steps, warmup, routing="biased"):
         total = n_steps * 2 + warmup
         rng = synth.rng_for(3, 0, T)
-        nvar = 4
+        nvar = 4 if routing == "biased" else 2
         xd, xv = synth.activations(rng, nvar * T, H, "bf16")
         xs = torch.from_numpy(xd.view(np.int16)).view(torch.bfloat16).to(dev).view(nvar, T, H)
-        lgs = [synth.biased_logits(rng, synth.router_logits(rng, xv[v * T:(v + 1) * T], E))
-               for v in range(nvar)]
+        if routing == "biased":
+            lgs = [synth.biased_logits(rng, synth.router_logits(rng, xv[v * T:(v + 1) * T], E))
+                   for v in range(nvar)]
+        else:
+            lgs = [synth.zipf_logits(rng, T, E) for v in range(nvar)]
         logits = torch.from_numpy(np.stack(lgs)).to(dev)
         r = {n: torch.empty(s, dtype=dt, device=dev) for n, s, dt in [
             ("ids", (T, K), torch.int32), ("w", (T, K), torch.float32), ("counts", (E,), torch.int32),
@@ -283,6 +286,18 @@ def main():
         gu_ms = kms.get("prefill_gateup", float("nan"))
         gu_flops = (T * K + T) * 2 * 2 * H * I
         gu_bytes = (ne + 1) * 2 * MAT_BYTES + T * H * 2 + (T * K + T) * I * 2   # weights, x, h
+        if T > 4096:   # long chunks: the gate/up kernel is bound by the MFMA rate
+            roof = {"bound": "mfma", "kernel": "prefill_gateup_kernel",
+                    "achieved": round(gu_flops / gu_ms / 1e9, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(gu_flops / gu_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+                    "traffic": None, "algorithmic_flops_per_launch": float(gu_flops),
+                    "kernel_us": round(gu_ms * 1e3, 2), "hbm_GBps": round(gu_bytes / gu_ms / 1e6, 1)}
+            return {
+                "T": T, "routing": "zipf(1.1)", "launch": "hip_graph", "ms_per_layer": ms, **pct,
+                "ms_per_layer_eager": ms_eager, "tokens_per_s": T * 1000.0 / ms,
+                "nonempty_experts": ne, "flops_per_step": float(flops),
+                "TFLOPs": flops / ms / 1e9, "mfma_frac": flops / ms / 1e9 / MFMA_F16_PEAK_TFLOPS,
+                "kernel_ms": kms, "grouped_gemm_ms": gemm_ms, "roofline": roof}
         return {
             "T": T, "routing": "router+bias N(0,0.5)", "launch": "hip_graph", "ms_per_layer": ms, **pct,
             "ms_per_layer_eager": ms_eager, "tokens_per_s": T * 1000.0 / ms,
@@ -370,6 +385,8 @@ def main():
         results["decode_T3"] = decode_case(3, "zipf", args.steps // 2, args.warmup)
     if only in ("", "prefill"):
         results["prefill_T1024"] = prefill_case(1024, args.prefill_steps, max(4, args.warmup // 4))
+    if only == "prefill32768":   # profiling runs only: one 32768-token chunk, Zipf routing
+        results["prefill_T32768"] = prefill_case(32768, max(4, args.prefill_steps // 10), 2, "zipf")
     if only in ("", "windows"):
         results["verify_windows"] = verify_windows([4, 5, 6, 7, 8], max(32, args.steps // 8),
                                                    max(4, args.warmup // 2))
