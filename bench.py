@@ -290,7 +290,8 @@ def main():
             roof = {"bound": "mfma", "kernel": "prefill_gateup_kernel",
                     "achieved": round(gu_flops / gu_ms / 1e9, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(gu_flops / gu_ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
-                    "traffic": None, "algorithmic_flops_per_launch": float(gu_flops),
+                    "traffic": pmc_traffic("prefill_gateup_T32768_pmc_traffic.txt", "prefill_gateup_kernel"),
+                    "algorithmic_flops_per_launch": float(gu_flops),
                     "kernel_us": round(gu_ms * 1e3, 2), "hbm_GBps": round(gu_bytes / gu_ms / 1e6, 1)}
             return {
                 "T": T, "routing": "zipf(1.1)", "launch": "hip_graph", "ms_per_layer": ms, **pct,
