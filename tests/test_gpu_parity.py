@@ -480,6 +480,22 @@ def _sampled_prefill(B, L, T, kind, seed, n_sample=12, flags=0):
     check_out(to_np(out[torch.from_numpy(toks).cuda()]), ref, f"prefill T={T} {kind} sampled")
 
 
+@pytest.mark.parametrize("E,k,T", [(1024, 16, 300), (300, 7, 129)])
+def test_prefill_expert_counts(B, E, k, T):
+    """Prefill with the largest expert count (five experts per thread of the
+    work-item scan) and with a count that is not a multiple of 64, every
+    token against the oracle."""
+    L = Layer(B, 12, E, 512, 256)
+    print(f"prefill E={E} k={k} T={T}", flush=True)
+    rng = synth.rng_for(45, E, T)
+    xd, xv = synth.activations(rng, T, 512, "f32")
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w, r = route_both(B, lg, k, True)
+    assert_route_exact(ids, w, r, E, True)
+    out = run_prefill(B, L, dev_x(xd, "f32"), r)
+    check_out(to_np(out), O.moe_layer(xv, ids, w, L.ref), f"prefill E={E} k={k} T={T}")
+
+
 @pytest.mark.parametrize("T,shared", [(4096, True), (4096, False), (4097, False), (5000, True)])
 def test_prefill_item_orders(B, T, shared):
     """Both work-item orders of the prefill kernels: lists in size order dealt
