@@ -480,6 +480,42 @@ def _sampled_prefill(B, L, T, kind, seed, n_sample=12, flags=0):
     check_out(to_np(out[torch.from_numpy(toks).cuda()]), ref, f"prefill T={T} {kind} sampled")
 
 
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_residual_in_place(B, layer_small, odt):
+    """residual may be the output buffer itself (the residual stream updated
+    in place): routed decode and prefill against the oracle with that
+    residual.  The expert part (out - residual) is held to the usual bound,
+    TOL * rms of the oracle's expert part; a bf16 output may in addition
+    differ by its own rounding, at most half a bf16 ulp, 2^-9 |value|."""
+    L = layer_small
+    for T, what in ((3, "decode"), (100, "prefill")):
+        print(f"in-place residual {what} T={T} {odt}", flush=True)
+        rng = synth.rng_for(46, T, int(odt == torch.bfloat16))
+        xd, xv = synth.activations(rng, T, 1024, "f32")
+        lg = rng.standard_normal((T, 64)).astype(np.float32)
+        ids, w = O.route_topk(lg, 4)
+        res = (rng.standard_normal((T, 1024)) * 0.5).astype(np.float32)
+        buf = dev(res).to(odt)
+        resv = buf.float().cpu().numpy().astype(np.float64)
+        if what == "decode":
+            ws = B.workspace(B.MOE_OP_DECODE, T, 64, 4, 1024, 256)
+            B.moe_expert_forward_decode_routed(L.dev, dev_x(xd, "f32"), dev(lg), 4, buf, None, None, buf, 0, ws)
+        else:
+            _, _, r = route_both(B, lg, 4, True)
+            ws = B.workspace(B.MOE_OP_PREFILL, T, 64, 4, 1024, 256)
+            B.moe_expert_forward_prefill(L.dev, dev_x(xd, "f32"), r["topk_ids"], r["topk_w"], r["counts"],
+                                         r["offsets"], r["sorted_pairs"], r["pair_pos"], buf, buf, 0, ws)
+        torch.cuda.synchronize()
+        ref = O.moe_layer(xv, ids, w, L.ref, residual=resv)
+        got = to_np(buf)
+        moe_rms = np.sqrt(np.mean((ref - resv) ** 2))
+        err = np.abs(got - ref)
+        print(f"in-place residual {what} {odt}: max|err| = {err.max():.3e}  rms(expert part) = {moe_rms:.3e}")
+        assert np.all(np.isfinite(got))
+        rounding = np.abs(ref) * 2.0 ** -9 if odt == torch.bfloat16 else 0.0
+        assert np.all(err <= TOL * moe_rms + rounding), (what, odt, float(err.max()), moe_rms)
+
+
 @pytest.mark.parametrize("E,k,T", [(1024, 16, 300), (300, 7, 129)])
 def test_prefill_expert_counts(B, E, k, T):
     """Prefill with the largest expert count (five experts per thread of the
