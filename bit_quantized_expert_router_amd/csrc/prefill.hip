@@ -118,26 +118,6 @@ __device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e)
 }
 
 // --------------------------------------------------------------------- prep --
-// Inclusive scan over the 256 threads of a workgroup (4 waves): shuffles
-// within each wave, then the wave totals through LDS behind one barrier.
-// Also returns the workgroup total.  V is int or uint64_t (packed counts).
-template <typename V>
-__device__ __forceinline__ V block256_incl_scan(V v, V* s_tot, V& total) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const V u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  if (lane == 63) s_tot[wid] = v;
-  __syncthreads();
-  V before = 0;
-#pragma unroll
-  for (int q = 0; q < 3; ++q) before += q < wid ? s_tot[q] : V(0);
-  total = s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
-  return before + v;
-}
-
 constexpr int kPrepTokensPerBlock = 4;                // one wave per token
 constexpr int kSizeOrderMaxTokens = 4096;             // chunks up to this long: items by size, dealt round robin
 
@@ -211,8 +191,8 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, const float* __restrict__ topk_w, int item_cap,
     PrefillWs ws) {
-  __shared__ int s_scan[4];
-  __shared__ uint64_t s_scan64[4];
+  __shared__ int s_scan[256];
+  __shared__ uint64_t s_scan64[256];
   const int H = L.H, E = L.E;
   const int P = T * k;
   const int TB = (T + kPrepTokensPerBlock - 1) / kPrepTokensPerBlock;
@@ -270,8 +250,16 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
         }
       }
     }
-    uint64_t tot;
-    const uint64_t excl = block256_incl_scan<uint64_t>(local, s_scan64, tot) - local;
+    s_scan64[threadIdx.x] = local;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const uint64_t v = threadIdx.x >= o ? s_scan64[threadIdx.x - o] : 0ull;
+      __syncthreads();
+      s_scan64[threadIdx.x] += v;
+      __syncthreads();
+    }
+    const uint64_t tot = s_scan64[255];
+    const uint64_t excl = s_scan64[threadIdx.x] - local;
     int pos[4];
     int base = 0;
 #pragma unroll
@@ -308,8 +296,15 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
       local += (n + kGroupRows - 1) / kGroupRows;
     }
   }
-  int total;
-  int pos = block256_incl_scan<int>(local, s_scan, total) - local;
+  s_scan[threadIdx.x] = local;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = threadIdx.x >= o ? s_scan[threadIdx.x - o] : 0;
+    __syncthreads();
+    s_scan[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int pos = s_scan[threadIdx.x] - local;
   for (int q = 0; q < per; ++q) {
     const int e = threadIdx.x * per + q;
     if (e < nexp) {
@@ -320,7 +315,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     }
   }
   if (threadIdx.x == 255) {
-    ws.hdr[0] = min(total, item_cap);
+    ws.hdr[0] = min(s_scan[255], item_cap);
     ws.hdr[1] = 0;
   }
 }
