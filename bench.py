@@ -50,9 +50,43 @@ def parse():
                     help="layers of the stacked decode/prefill runs (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
+    ap.add_argument("--counters", action="store_true",
+                    help="eager 1-token decode steps only (hardware-counter runs)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the device-ceiling microbenchmarks (moe_ceilings)")
     return ap.parse_args()
+
+
+_T0 = time.time()
+
+
+def progress(msg: str):
+    """One line on stderr per finished case (the JSON line goes to stdout)."""
+    print(f"bench: {msg} ({time.time() - _T0:.1f} s)", file=sys.stderr, flush=True)
+
+
+def case_steps(steps: int) -> dict:
+    """Timed steps of the secondary cases for `--steps K` (the headline case
+    times exactly K): at least one each."""
+    return {"half": max(1, steps // 2), "windows": max(32, steps // 8)}
+
+
+def step_plan(n_steps: int, warmup: int) -> dict:
+    """Rows (per-step inputs and routing outputs) that each phase of a case
+    uses: eager warmup, eager timing, the untimed warm graph, the graph-timed
+    region (exactly n_steps steps) and the hooked per-kernel pass.  The warm
+    and timed graphs cover different rows, so the timed steps run other
+    rotating layers than the ones just before them."""
+    if n_steps < 1 or warmup < 0:
+        raise ValueError("need n_steps >= 1 and warmup >= 0")
+    w, k = warmup, n_steps
+    return {"warmup": range(0, w), "eager_timed": range(w, w + k), "graph_warm": range(w, w + k),
+            "graph_timed": range(w + k, w + 2 * k), "hooked": range(w + 2 * k, w + 3 * k)}
+
+
+def rows_needed(n_steps: int, warmup: int) -> int:
+    """Rows a case must allocate: one past the last index step_plan uses."""
+    return max(r.stop for r in step_plan(n_steps, warmup).values())
 
 
 def device_ceilings():
@@ -79,8 +113,12 @@ def main():
         print("bench.py: the library runs the MoE layer on one GPU only; "
               "--gpus must be 1 (no multi-GPU path is built)", file=sys.stderr)
         sys.exit(2)
+    if args.counters:
+        counters_run(args)
+        return
 
     ceilings = None if (args.no_ceilings or args.only) else device_ceilings()
+    progress("ceilings")
 
     import torch
     from bit_quantized_expert_router_amd import binding as B
@@ -109,68 +147,97 @@ def main():
         layers.append(B.Layer(ex, sh, E, H, I, synth.expert_stride(H, I)))
     torch.cuda.synchronize()
     gen_s = time.time() - t0
+    progress(f"{args.layers} layers of weights generated")
 
     results = {}
     prof_kernels = {}
 
-    def timed(fn, n_steps, warmup):
-        for i in range(warmup):
-            fn(i)
+    def timed(fn, idx):
+        """Eager steps fn(i) for i in idx (a range), bracketed by events on
+        the stream the library launches on; ms per step."""
         torch.cuda.synchronize()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
-        for i in range(n_steps):
-            fn(warmup + i)
+        for i in idx:
+            fn(i)
         ev1.record(stream)
         torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / n_steps
+        return ev0.elapsed_time(ev1) / len(idx)
 
     spread = {}
 
-    def graphed(fn, n_capture, replays):
-        """The same steps captured once into a HIP graph and replayed: one
-        graph holds n_capture consecutive steps (all rotating layers).
-        Returns the mean ms per step; `spread` receives the 10th, 50th and
-        90th percentiles over the replays (each the mean of its n_capture
-        steps)."""
-        torch.cuda.synchronize()
+    def capture(fn, idx):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(n_capture):
+            for i in idx:
                 fn(i)
-        for _ in range(3):
-            g.replay()
+        return g
+
+    def graphed(fn, plan, extra_replays=4):
+        """The timed region: plan["graph_timed"] (exactly the K timed steps)
+        captured into one HIP graph and replayed once between a
+        synchronisation on each side, after one untimed replay of a graph
+        over plan["graph_warm"] (the K steps before, on other rotating
+        layers, so the timed steps do not find their weights in the
+        last-level cache).  Returns ms per step; `spread` receives the 10th,
+        50th and 90th percentiles of ms per step over the timed replay and
+        `extra_replays` more, each preceded by a replay of the warm graph."""
         torch.cuda.synchronize()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
-        evs[0].record()
-        for r in range(replays):
-            g.replay()
-            evs[r + 1].record()
+        gw = capture(fn, plan["graph_warm"])
+        gt = capture(fn, plan["graph_timed"])
+        n = len(plan["graph_timed"])
+        gw.replay()
         torch.cuda.synchronize()
-        per = np.array([evs[r].elapsed_time(evs[r + 1]) / n_capture for r in range(replays)])
-        ms = evs[0].elapsed_time(evs[-1]) / (replays * n_capture)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        gt.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / n
+        per = [ms]
+        for _ in range(extra_replays):
+            gw.replay()
+            ev0.record()
+            gt.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            per.append(ev0.elapsed_time(ev1) / n)
         spread.clear()
         spread.update({"ms_per_layer_p10": float(np.percentile(per, 10)),
                        "ms_per_layer_p50": float(np.percentile(per, 50)),
-                       "ms_per_layer_p90": float(np.percentile(per, 90)), "replays": replays})
-        del g
+                       "ms_per_layer_p90": float(np.percentile(per, 90)), "replays": len(per)})
+        del gw, gt
         return ms
 
-    def hooked(fn, n_steps, start):
-        """Same steps again with the library's per-kernel hipEvent hooks on."""
+    def hooked(fn, idx):
+        """Same steps again with the library's per-kernel hipEvent hooks on
+        (each launch's events stamped with its dispatch's begin and end)."""
         torch.cuda.synchronize()
         B.profile_reset()
         B.profile_enable(True)
-        for i in range(n_steps):
-            fn(start + i)
+        for i in idx:
+            fn(i)
         torch.cuda.synchronize()
         B.profile_enable(False)
         return {k: v for k, v in B.profile_results().items() if v[0] > 0}
 
+    def run_phases(step, n_steps, warmup):
+        """Eager warmup, eager timing, the graph-timed region and the hooked
+        pass of one case, on the rows step_plan assigns to each."""
+        plan = step_plan(n_steps, warmup)
+        for i in plan["warmup"]:
+            step(i)
+        ms_eager = timed(step, plan["eager_timed"])
+        ms = graphed(step, plan)
+        pct = dict(spread)
+        kern = hooked(step, plan["hooked"])
+        return plan, ms, ms_eager, pct, kern
+
     # ---------------------------------------------------------------- decode
     def decode_case(T, kind, n_steps, warmup, routed=True, gemv=False):
-        total = n_steps * 2 + warmup
+        total = rows_needed(n_steps, warmup)
         rng = synth.rng_for(1, 100 + T, 0)
         xd, xv = synth.activations(rng, min(total, 64) * T, H, "bf16")
         xs = torch.from_numpy(xd.view(np.int16)).view(torch.bfloat16).to(dev).view(-1, T, H)
@@ -203,14 +270,13 @@ def main():
                 B.moe_route_topk(logits[i], K, ids[i], wts[i])
                 B.moe_expert_forward_decode(L, xs[i % nx], ids[i], wts[i], out, None, 0, ws)
 
-        ms_eager = timed(step, n_steps, warmup)
-        ncap = 2 * len(layers)
-        ms = graphed(step, ncap, max(1, n_steps // ncap))
-        pct = dict(spread)
-        kern = hooked(step, n_steps, warmup + n_steps)
+        plan, ms, ms_eager, pct, kern = run_phases(step, n_steps, warmup)
         idh = ids.cpu().numpy()
         distinct = np.array([len(np.unique(idh[i])) for i in range(total)])
-        slots = distinct[warmup:warmup + n_steps].mean() + 1
+        # routed experts + the shared one, over the graph-timed steps (the
+        # headline) and over the hooked steps (the per-kernel times)
+        slots = distinct[list(plan["graph_timed"])].mean() + 1
+        slots_hook = distinct[list(plan["hooked"])].mean() + 1
         wbytes = slots * EXPERT_BYTES
         io = T * H * 2 + T * H * 4 + T * E * 4 + T * K * 8
         step_bytes = wbytes + io
@@ -224,7 +290,7 @@ def main():
         if "route_gemv_topk_kernel" in kern:
             rt = kern["route_gemv_topk_kernel"]
             kms = {"route_gemv_topk": rt[1] / rt[0], **kms}
-        gu_bytes = slots * 2 * MAT_BYTES + T * H * 2 + (T * K + T) * I * 2   # weights, x, h
+        gu_bytes = slots_hook * 2 * MAT_BYTES + T * H * 2 + (T * K + T) * I * 2   # weights, x, h
         return {
             "T": T, "routing": kind,
             "calls": ("route_topk_gemv (logits) + decode_routed (router GEMV included)" if gemv else
@@ -242,7 +308,6 @@ def main():
 
     # --------------------------------------------------------------- prefill
     def prefill_case(T, n_steps, warmup, routing="biased"):
-        total = n_steps * 2 + warmup
         rng = synth.rng_for(3, 0, T)
         nvar = 4 if routing == "biased" else 2
         xd, xv = synth.activations(rng, nvar * T, H, "bf16")
@@ -269,10 +334,7 @@ def main():
             B.moe_expert_forward_prefill(L, xs[v], r["ids"], r["w"], r["counts"], r["offsets"],
                                          r["sp"], r["pp"], out, None, 0, ws)
 
-        ms_eager = timed(step, n_steps, warmup)
-        ms = graphed(step, len(layers), max(1, n_steps // len(layers)))
-        pct = dict(spread)
-        kern = hooked(step, n_steps, warmup + n_steps)
+        plan, ms, ms_eager, pct, kern = run_phases(step, n_steps, warmup)
         nonempty = []
         for v in range(nvar):
             ids_v = torch.topk(logits[v], K, dim=1).indices.cpu().numpy()
@@ -324,7 +386,7 @@ def main():
     # inside) and through the grouped prefill path (routing histogram +
     # grouped GEMMs), to find where decode should hand over.
     def grouped_window(T, n_steps, warmup):
-        total = n_steps * 2 + warmup
+        total = rows_needed(n_steps, warmup)
         rng = synth.rng_for(1, 100 + T, 0)
         xd, _ = synth.activations(rng, min(total, 64) * T, H, "bf16")
         xs = torch.from_numpy(xd.view(np.int16)).view(torch.bfloat16).to(dev).view(-1, T, H)
@@ -346,9 +408,7 @@ def main():
             B.moe_expert_forward_prefill(L, xs[i % nx], r["ids"], r["w"], r["counts"], r["offsets"],
                                          r["sp"], r["pp"], out, None, 0, ws)
 
-        timed(step, n_steps, warmup)
-        ncap = 2 * len(layers)
-        return graphed(step, ncap, max(1, n_steps // ncap))
+        return run_phases(step, n_steps, warmup)[1]
 
     def verify_windows(Ts, n_steps, warmup):
         rows = {}
@@ -372,25 +432,34 @@ def main():
                 "grouped_first_faster_at_T": handover}
 
     only = args.only
+    half = case_steps(args.steps)["half"]
     if only in ("", "decode1"):
         results["decode_T1"] = decode_case(1, "router", args.steps, args.warmup)
+        progress("decode_T1")
     if only in ("", "decode1_two_calls"):
-        results["decode_T1_two_calls"] = decode_case(1, "router", args.steps // 2, args.warmup,
+        results["decode_T1_two_calls"] = decode_case(1, "router", half, args.warmup,
                                                      routed=False)
+        progress("decode_T1_two_calls")
     if only in ("", "decode1_gemv"):
-        results["decode_T1_router_gemv"] = decode_case(1, "router", args.steps // 2, args.warmup,
+        results["decode_T1_router_gemv"] = decode_case(1, "router", half, args.warmup,
                                                        routed=False, gemv=True)
+        progress("decode_T1_router_gemv")
     if only in ("", "decode2"):
-        results["decode_T2"] = decode_case(2, "zipf", args.steps // 2, args.warmup)
+        results["decode_T2"] = decode_case(2, "zipf", half, args.warmup)
+        progress("decode_T2")
     if only in ("", "decode3"):
-        results["decode_T3"] = decode_case(3, "zipf", args.steps // 2, args.warmup)
+        results["decode_T3"] = decode_case(3, "zipf", half, args.warmup)
+        progress("decode_T3")
     if only in ("", "prefill"):
         results["prefill_T1024"] = prefill_case(1024, args.prefill_steps, max(4, args.warmup // 4))
+        progress("prefill_T1024")
     if only == "prefill32768":   # profiling runs only: one 32768-token chunk, Zipf routing
         results["prefill_T32768"] = prefill_case(32768, max(4, args.prefill_steps // 10), 2, "zipf")
+        progress("prefill_T32768")
     if only in ("", "windows"):
-        results["verify_windows"] = verify_windows([4, 5, 6, 7, 8], max(32, args.steps // 8),
+        results["verify_windows"] = verify_windows([4, 5, 6, 7, 8], case_steps(args.steps)["windows"],
                                                    max(4, args.warmup // 2))
+        progress("verify_windows")
 
     # ------------------------------------------------- 48 stacked layers
     # 48 distinct layers (54.5 GB), x_{l+1} = x_l + MoE_l(rmsnorm(x_l)) in a
@@ -419,7 +488,18 @@ def main():
                     B.moe_expert_forward_decode_routed(stack[l], x, lg[l], K, o, None, None, x,
                                                        B.MOE_FLAG_PRENORM_RMS, ws)
                     x = o
-            ms = graphed(step, 1, steps)
+            g = capture(step, range(1))      # one step = all NL layers
+            g.replay()
+            torch.cuda.synchronize()
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            for _ in range(steps):
+                g.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / steps
+            del g
             return {"T": T, "layers": NL, "launch": "hip_graph", "ms_per_step": ms,
                     "us_per_layer": ms * 1e3 / NL, "tokens_per_s": T * 1000.0 / ms}
 
@@ -463,8 +543,10 @@ def main():
 
         for T in (1, 2, 3):
             results[f"stack{NL}_decode_T{T}"] = stack_decode(T, 20)
+            progress(f"stack{NL}_decode_T{T}")
         for T in (1024, 32768):
             results[f"stack{NL}_prefill_T{T}"] = stack_prefill(T, 1)
+            progress(f"stack{NL}_prefill_T{T}")
         del stack
         torch.cuda.empty_cache()
 
@@ -472,6 +554,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and only == "":
         cpu = cpu_baseline(args.cpu_seconds)
+        progress("cpu_baseline")
 
     head = results.get("decode_T1") or next(
         (v for v in results.values() if "tokens_per_s" in v and "ms_per_layer" in v),
@@ -495,7 +578,7 @@ def main():
                         "hidden 3072, inter 768, Q2 2-bit weights (2,211,840 B/expert), "
                         f"{args.layers} rotating layers",
             "tokens_per_step": 1, "experts": E, "top_k": K, "hidden": H, "inter": I,
-            "parallelism": "single_gpu", "launch": "hip_graph (32 steps per graph)",
+            "parallelism": "single_gpu", "launch": "hip_graph (the timed steps in one graph)",
         },
     }
     if "decode_T1" in results:
@@ -545,10 +628,15 @@ def pmc_traffic(name: str, kernel: str):
     return float(kv["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(seconds: float):
-    """The fp64 oracle on the host cores, decode of one token on the same
-    workload shape (512 experts top-10 + shared, H 3072, I 768), for a bounded
-    number of steps (about `seconds` of CPU work)."""
+def cpu_baseline(seconds: float, prefill_tokens: int = 1024):
+    """The fp64 oracle on the host cores, on the same workload shape (512
+    experts top-10 + shared, H 3072, I 768): decode of one token for a
+    bounded number of steps (about `seconds` of oracle time), then one full
+    prefill chunk of `prefill_tokens` tokens with the skewed router (logits
+    from a bf16 router weight plus a per-expert N(0, 0.5) bias): routing,
+    histogram and the expert layer, every used expert decoded from its 2-bit
+    bytes once."""
+    import platform
     import oracle as O
     from bit_quantized_expert_router_amd import synth
     try:
@@ -556,6 +644,12 @@ def cpu_baseline(seconds: float):
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     except Exception:
         threads = 1
+    cpu_model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     rng = synth.rng_for(1, 500, 0)
     blob = synth.expert_blob(rng, E, H, I)
     sh = synth.expert_blob(rng, 1, H, I)
@@ -570,11 +664,69 @@ def cpu_baseline(seconds: float):
         O.moe_layer(xv, ids, w, ob)
         spent += time.perf_counter() - t1
         steps += 1
-    return {"value": round(steps / spent, 4), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{steps} decode steps of 1 token (route + 11 experts decoded from the 2-bit "
-                      f"bytes and evaluated in float64), {spent:.1f} s of oracle time; input "
-                      f"generation excluded; cores = BLAS threads"}
+    res = {"value": round(steps / spent, 4), "unit": "tokens/s", "cores": int(threads),
+           "kind": "oracle", "cpu": cpu_model,
+           "sample": f"{steps} decode steps of 1 token (route + 11 experts decoded from the 2-bit "
+                     f"bytes and evaluated in float64), {spent:.1f} s of oracle time; input "
+                     f"generation excluded; cores = BLAS threads"}
+    if prefill_tokens:
+        T = prefill_tokens
+        rngp = synth.rng_for(3, 500, T)
+        _, xv = synth.activations(rngp, T, H, "bf16")
+        lg = synth.biased_logits(rngp, synth.router_logits(rngp, xv, E))
+        ob = O.ExpertBlob(blob, E, H, I, shared=sh, cache=0)
+        t1 = time.perf_counter()
+        ids, w = O.route_topk(lg, K)
+        O.route_histogram(ids, E)
+        O.moe_layer(xv, ids, w, ob)
+        sp = time.perf_counter() - t1
+        res["prefill_T1024"] = {
+            "value": round(T / sp, 3), "unit": "tokens/s", "seconds": round(sp, 2),
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"one full {T}-token prefill layer (router N(0,0.5) bias; "
+                      f"{len(np.unique(ids))} non-empty experts + shared, each decoded once from its "
+                      f"2-bit bytes, float64)"}
+    return res
+
+
+def counters_run(args):
+    """Eager 1-token decode steps only (no graph capture, no measurement
+    hooks, no ceilings, no oracle), for hardware-counter collection: every
+    dispatch is an ordinary stream launch."""
+    import torch
+    from bit_quantized_expert_router_amd import binding as B
+    from bit_quantized_expert_router_amd import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    layers = []
+    for l in range(args.layers):
+        ex = synth.device_expert_blob(E, H, I, synth.torch_seed(1, l, 1), dev)
+        sh = synth.device_expert_blob(1, H, I, synth.torch_seed(1, l, 2), dev)
+        layers.append(B.Layer(ex, sh, E, H, I, synth.expert_stride(H, I)))
+    rng = synth.rng_for(1, 101, 0)
+    n = args.steps
+    xd, xv = synth.activations(rng, n, H, "bf16")
+    xs = torch.from_numpy(xd.view(np.int16)).view(torch.bfloat16).to(dev)
+    logits = torch.from_numpy(synth.router_logits(rng, xv, E)).to(dev)
+    out = torch.empty((1, H), dtype=torch.float32, device=dev)
+    ws = B.workspace(B.MOE_OP_DECODE, 1, E, K, H, I, dev)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    for i in range(n):
+        B.moe_expert_forward_decode_routed(layers[i % len(layers)], xs[i:i + 1], logits[i:i + 1], K, out,
+                                           None, None, None, 0, ws)
+    torch.cuda.synchronize()
+    print(json.dumps({"counters_run": "decode_T1 eager", "steps": n, "wall_s": round(time.time() - t0, 4),
+                      "out_finite": bool(torch.isfinite(out).all().item())}))
 
 
 if __name__ == "__main__":
