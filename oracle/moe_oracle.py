@@ -314,7 +314,8 @@ def moe_layer(x, ids, w, blob: ExpertBlob, prenorm=False, residual=None,
     for e in np.unique(ids_s):
         rows, slots = np.nonzero(ids_s == e)
         y = expert_ffn(xh[rows], *blob.weights(int(e)))
-        out[rows] += w_s[rows, slots][:, None] * y
+        # np.add.at: a token listing expert e twice adds both of its pairs
+        np.add.at(out, rows, w_s[rows, slots][:, None] * y)
     if blob.shared is not None:
         out += expert_ffn(xh, *blob.weights("shared"))
     if residual is not None:

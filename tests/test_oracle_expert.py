@@ -188,3 +188,48 @@ def test_every_token_same_experts_reduces_to_dense_gemms():
     Wg, Wu, Wd = (O.dequantize(q, d) for q, d in kept[E])
     ref += ((x @ Wg.T) / (1 + np.exp(-(x @ Wg.T))) * (x @ Wu.T)) @ Wd.T
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_repeated_expert_in_a_token_adds_both_pairs():
+    """A routing in which a token lists one expert twice: the layer is the sum
+    over every listed pair (brute force), so both pairs count."""
+    rng = np.random.default_rng(18)
+    E, H, I, T = 4, 256, 256, 2
+    blob, kept = make_blob(rng, E, H, I)
+    x = rng.standard_normal((T, H))
+    ids = np.array([[2, 2, 0], [1, 3, 1]], dtype=np.int32)
+    w = np.array([[0.5, 0.3, 0.2], [0.1, 0.6, 0.3]])
+    out = O.moe_layer(x, ids, w, blob)
+    for t in range(T):
+        ref = brute_ffn(x[t], kept[E])
+        for j in range(3):
+            ref = ref + w[t, j] * brute_ffn(x[t], kept[ids[t, j]])
+        assert np.allclose(out[t], ref, rtol=1e-11, atol=1e-11)
+        assert np.allclose(out[t], O.moe_token(x[t], ids[t], w[t], blob), rtol=1e-12, atol=1e-12)
+
+
+def test_stack_against_brute_force():
+    """Two stacked layers on a tiny shape against element-by-element loops:
+    rms pre-norm written as a loop, every FFN by brute_ffn, residual added."""
+    rng = np.random.default_rng(19)
+    E, H, I, k, T = 3, 256, 256, 2, 2
+    made = [make_blob(rng, E, H, I) for _ in range(2)]
+    W = [rng.standard_normal((H, E)) for _ in range(2)]
+    x0 = rng.standard_normal((T, H))
+    fns = [lambda x, Wl=Wl: (x @ Wl).astype(np.float32) for Wl in W]
+    out = O.moe_stack(x0, zip(fns, [m[0] for m in made]), k)
+    x = x0.copy()
+    for (blob, kept), fn in zip(made, fns):
+        ids, w = O.route_topk(fn(x), k)
+        nxt = x.copy()
+        for t in range(T):
+            ss = 0.0
+            for c in range(H):
+                ss += x[t, c] * x[t, c]
+            xh = x[t] / math.sqrt(ss / H + 1e-6)
+            acc = brute_ffn(xh, kept[E])
+            for j in range(k):
+                acc = acc + w[t, j] * brute_ffn(xh, kept[ids[t, j]])
+            nxt[t] = x[t] + acc
+        x = nxt
+    assert np.allclose(out, x, rtol=1e-10, atol=1e-10)
