@@ -35,6 +35,12 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Whether the byte ranges [a, a + an) and [b, b + bn) share a byte.
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return an > 0 && bn > 0 && x < y + bn && y < x + an;
+}
+
 // ------------------------------------------------------ measurement hooks --
 struct Profiler {
   std::mutex mu;
@@ -269,10 +275,18 @@ static int check_forward(const moe_q2_layer* layer, const void* x, int32_t x_dty
   int st = check_layer(layer, k);
   if (st) return st;
   if (!x || !ids || !w || !out) return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, topk_w and out are required");
-  if (x == out) return fail(MOE_ERR_INVALID_ARG, "out must not alias x");
   if (!valid_dtype(x_dtype) || !valid_dtype(out_dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
   if (flags & ~MOE_FLAG_PRENORM_RMS) return fail(MOE_ERR_INVALID_ARG, "unknown flag");
   if (T < 1) return fail(MOE_ERR_INVALID_ARG, "T must be >= 1");
+  {
+    // out must not share a byte with x; residual is either out itself or
+    // disjoint from it
+    const size_t n = static_cast<size_t>(T) * static_cast<size_t>(layer->hidden);
+    const size_t xb = n * (x_dtype == MOE_BF16 ? 2 : 4), ob = n * (out_dtype == MOE_BF16 ? 2 : 4);
+    if (overlaps(x, xb, out, ob)) return fail(MOE_ERR_INVALID_ARG, "out must not overlap x");
+    if (residual && residual != out && overlaps(residual, ob, out, ob))
+      return fail(MOE_ERR_INVALID_ARG, "residual must be out itself or not overlap it");
+  }
   if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is required");
   if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(residual, 16) || !aligned(ids, 4) || !aligned(w, 4))

@@ -1,5 +1,5 @@
-// Decode-time expert layer: T = 1..4 tokens (one decode step or a small
-// verify window), reading only the selected experts' 2-bit tiles.
+// Decode-time expert layer: T = 1..8 tokens (one decode step or a verify
+// window), reading only the selected experts' 2-bit tiles.
 //
 // Reading the selected experts' weights is what decode time goes to ("Strata
 // 实测 ...", kefong.net, section 四: a higher expert-cache hit rate gave +39 %
@@ -14,19 +14,24 @@
 //
 // Slots: the distinct selected experts in first-occurrence order of topk_ids,
 // then the shared expert.  Pairs: routed pair p = t*k + j, shared pair T*k + t;
-// h~ has one row per pair.
+// h~ has one row per pair.  A token that lists one expert twice gets one pair
+// for it (the lower pair id) carrying the sum of the two weights.
 //
-// Kernel 1 (gate/up + SwiGLU): one workgroup of 8 waves per (slot, two 16-row
-//   tiles of I); 4 waves per row tile split the H/256 K tiles.  Each
-//   workgroup derives the slots from topk_ids (or takes the top-k of the
-//   logits itself), issues its weight loads, then stages x_hat * s_t as fp16
-//   in LDS (s_t: per-token power of two, max |x_hat s_t| in [0.5, 1)).
-//   h~[pair][I] (fp16) = w * silu(g) * u * s_t^2.
+// Kernel 1 (gate/up + SwiGLU): groups of 4 waves, one per (slot, 16-row tile
+//   of I), the 4 waves splitting the H/256 K tiles.  Each workgroup derives
+//   the slots from topk_ids (or takes the top-k of the logits itself), stages
+//   x_hat * s_t as fp16 in LDS (s_t: per-token power of two, max |x_hat s_t|
+//   in [0.5, 1)), then issues its weight loads.  Epilogue: h = w * silu(g) * u
+//   in float32; each (pair, row tile) of 16 values is stored as fp16
+//   h * 2^-e with its own exponent e (so |h~| < 1: fp16 cannot overflow,
+//   whatever the weights' scales), e in a byte array beside h~.
 // Kernel 2 (down + weighted combine + shared + residual): one workgroup of 8
 //   waves per 16-row tile of H; work items (slot, K tile) of all slots, item i
-//   to wave i % 8.  h~ is staged in LDS once per workgroup; the MFMA
-//   accumulator sums W_down(e) h~(e) over all slots, so the weighted combine
-//   is exact and in a fixed order; out = acc / s_t^2 (+ residual).
+//   to wave i % 8.  Every workgroup first takes, per token, the largest
+//   exponent E_t over the token's pairs and row tiles, and moves h~ into LDS
+//   as h * 2^-E_t (a power-of-two rescale); the MFMA accumulator then sums
+//   W_down(e) h~(e) over all slots in a fixed order, so the weighted combine
+//   is exact, and out = acc * 2^E_t (+ residual).
 // The two halves meet at a kernel boundary.  A grid-wide barrier inside one
 // kernel was measured as no faster on this device: with the workgroups spread
 // over 8 XCDs every cross-XCD signal is a round trip through memory, and the
@@ -63,15 +68,28 @@ struct DecodeHeader {          // start of the workspace, written by block 0 of 
   int32_t pad0[3];
   int32_t expert[kMaxSlots];                       // -1 = shared expert
   int32_t pidx[kMaxSlots][kMaxT];                  // pair of (slot, token) or -1
-  float unscale[kMaxT];                            // 1 / s_t
 };
 constexpr size_t kHeaderBytes = 8192;            // h~ starts here
 static_assert(sizeof(DecodeHeader) <= kHeaderBytes, "header size");
+
+// Workspace after the header: h~ [pairs][I] fp16, then the exponents
+// [pairs][I/16] (int8, one per pair and 16-row tile of I).
+__host__ __device__ inline size_t decode_h_bytes(int T, int k, int I) {
+  const size_t pairs = static_cast<size_t>(T) * k + T;
+  return (pairs * I * sizeof(_Float16) + 255) / 256 * 256;
+}
+__host__ __device__ inline size_t decode_hexp_bytes(int T, int k, int I) {
+  const size_t pairs = static_cast<size_t>(T) * k + T;
+  return (pairs * (I / kTileRows) + 255) / 256 * 256;
+}
+
+constexpr int kNoPair = 0x7FFFFFFF;
 
 struct DecodeSlots {
   int n;
   int expert[kMaxSlots];
   int pidx[kMaxSlots][kMaxT];
+  int pslot[kMaxPairs];                            // slot of each routed pair, -1 if invalid
   float wpair[kMaxPairs];
 };
 
@@ -85,7 +103,8 @@ __device__ __forceinline__ int wave_id() {
 // id already given a slot by an earlier group is found in slot_of (LDS, E
 // entries, used only when there is more than one group), duplicates inside a
 // group by lane matching -- skipped when the caller knows the ids are
-// distinct (one token's own top-k).
+// distinct (one token's own top-k).  A token listing one expert twice keeps
+// the lower pair for that (slot, token), with the weights summed in pair order.
 __device__ void build_slots(const int32_t* ids, const float* w, int T, int k, int E,
                             bool has_shared, DecodeSlots& S, int* slot_of, bool distinct) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -94,7 +113,7 @@ __device__ void build_slots(const int32_t* ids, const float* w, int T, int k, in
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
   // only the rows of slots that can exist (at most T*k + 1) are read later
-  for (int i = lane; i < (np + 1) * kMaxT; i += kWave) (&S.pidx[0][0])[i] = -1;
+  for (int i = lane; i < (np + 1) * kMaxT; i += kWave) (&S.pidx[0][0])[i] = kNoPair;
   if (multi)
     for (int i = lane; i < E; i += kWave) slot_of[i] = -1;
   __builtin_amdgcn_wave_barrier();
@@ -116,11 +135,31 @@ __device__ void build_slots(const int32_t* ids, const float* w, int T, int k, in
       S.expert[slot] = e;
       if (multi) slot_of[e] = slot;
     }
-    if (valid) S.pidx[slot][p / k] = p;
-    if (p < np) S.wpair[p] = valid ? wl : 0.0f;
+    if (valid) atomicMin(&S.pidx[slot][p / k], p);
+    if (p < np) {
+      S.wpair[p] = valid ? wl : 0.0f;
+      S.pslot[p] = valid ? slot : -1;
+    }
     nd += __popcll(fm);
     __builtin_amdgcn_wave_barrier();
   }
+  // repeated ids of one token: the lowest pair of each (slot, token) keeps
+  // it and collects the others' weights, in ascending pair order
+  bool dup = false;
+  for (int p = lane; p < np; p += kWave) {
+    const int s = S.pslot[p];
+    dup = dup || (s >= 0 && S.pidx[s][p / k] != p);
+  }
+  if (__ballot(dup) != 0ull && lane == 0) {
+    for (int p = 0; p < np; ++p) {
+      const int s = S.pslot[p];
+      const int q = s >= 0 ? S.pidx[s][p / k] : p;
+      if (q != p) S.wpair[q] += S.wpair[p];
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int i = lane; i < (np + 1) * kMaxT; i += kWave)
+    if ((&S.pidx[0][0])[i] == kNoPair) (&S.pidx[0][0])[i] = -1;
   if (has_shared && lane < T) {
     S.pidx[nd][lane] = np + lane;
     S.wpair[np + lane] = 1.0f;
@@ -374,12 +413,14 @@ __device__ __forceinline__ void load_gateup(const uint8_t* expert, bool live, in
 
 // Gate/up products of one row tile from LDS x (xs), K split over a group of
 // 4 waves, summed in LDS in wave order; the group's first wave writes h~ of
-// every (slot, token) pair (not for an inactive group).
+// every (slot, token) pair (not for an inactive group): the 16 values of a
+// pair in this row tile as fp16 h * 2^-e, e = block_exponent of their
+// largest |h|, and e in hexp[pair][rt].
 template <int KTW>
 __device__ void gateup_compute(const GateUpTiles<KTW>& R, const _Float16* xs, int T, int H, int I,
                                int rt, int kq, int slot, bool active, const DecodeSlots& S,
                                const float* s_smul,
-                               f32x4 (*s_red)[2][32], _Float16* hout) {
+                               f32x4 (*s_red)[2][32], _Float16* hout, int8_t* hexp) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = wave_id();
   const int KT = H / kTileCols;
@@ -407,16 +448,19 @@ __device__ void gateup_compute(const GateUpTiles<KTW>& R, const _Float16* xs, in
     for (int q = 1; q < 4; ++q) { G += s_red[wid + q][0][lane]; U += s_red[wid + q][1][lane]; }
     const int row = rt * kTileRows + (lane & 15);
     const bool hi = lane >= 16;
+    const int RTI = I / kTileRows;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+      // one token per 16-lane row: p, and so the branch, is uniform in it
       const int t = (hi ? 4 : 0) + r;
       const int p = t < T ? S.pidx[slot][t] : -1;
-      if (p < 0) continue;
-      const float s = s_smul[t];
-      const float u = 1.0f / s;
-      const float gv = G[r] * u, uv = U[r] * u;
-      const float h = S.wpair[p] * silu(gv) * uv * (s * s);
-      hout[static_cast<size_t>(p) * I + row] = static_cast<_Float16>(h);
+      const float u = 1.0f / s_smul[t];
+      const float h = p >= 0 ? S.wpair[p] * silu(G[r] * u) * (U[r] * u) : 0.0f;
+      const int e = block_exponent(row16_max(fabsf(h)));
+      if (p >= 0) {
+        hout[static_cast<size_t>(p) * I + row] = static_cast<_Float16>(ldexpf(h, -e));
+        if ((lane & 15) == 0) hexp[static_cast<size_t>(p) * RTI + rt] = static_cast<int8_t>(e);
+      }
     }
   }
 }
@@ -451,13 +495,28 @@ __device__ __forceinline__ void load_down(const LayerArgs& L, const int* expert,
   }
 }
 
-template <int DB>
+// Token of pair p (routed pairs t*k + j, then one shared pair per token).
+__device__ __forceinline__ int pair_token(int p, int T, int k) {
+  return p < T * k ? p / k : p - T * k;
+}
+
+// The wave's items j0..j0+DB-1 on the MFMA.  A = h~ rows of the item's slot,
+// one per token (row m = token m).  STAGED: hsrc is the LDS copy, already
+// rescaled to each token's exponent; otherwise hsrc is the workspace copy
+// and each fragment is rescaled here: its 8 values lie in one 16-row tile
+// of I, whose exponent is hexp[p][tile].
+template <int DB, bool STAGED>
 __device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int KTd, int j0,
                                          int lane, const _Float16* hsrc,
                                          const int (*pidx)[kMaxT], int T, int I,
+                                         const int8_t* hexp, const int (&et)[kMaxT],
                                          f32x4& acc) {
   const int wid = wave_id();
   const int m = lane & 15, g = lane >> 4;
+  const int RTI = I / kTileRows;
+  int my_et = et[0];
+#pragma unroll
+  for (int t = 1; t < kMaxT; ++t) my_et = (m == t) ? et[t] : my_et;
 #pragma unroll
   for (int b = 0; b < DB; ++b) {
     const int wi = wid + kWaves * (j0 + b);
@@ -466,10 +525,14 @@ __device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int
       const int kt = wi % KTd;
       const int p = (m < T) ? pidx[slot][m] : -1;
       const _Float16* arow = hsrc + static_cast<size_t>(p < 0 ? 0 : p) * I + kt * kTileCols + 8 * g;
+      const int8_t* erow = hexp + static_cast<size_t>(p < 0 ? 0 : p) * RTI + kt * (kTileCols / kTileRows) + (g >> 1);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         f16x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (p >= 0) a = *reinterpret_cast<const f16x8*>(arow + 32 * j);
+        if (p >= 0) {
+          a = *reinterpret_cast<const f16x8*>(arow + 32 * j);
+          if constexpr (!STAGED) a = scale_pow2(a, static_cast<int>(erow[2 * j]) - my_et);
+        }
         acc = mfma16(a, tile_block_weights(D.c[b], D.s[b], j), acc);
       }
     }
@@ -477,9 +540,9 @@ __device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int
 }
 
 // Sum of the 8 waves' accumulators (wave order) and the output rows of tile
-// rt: out = acc * unscale^2 (+ residual).
+// rt: out = acc * 2^E_t (+ residual).
 __device__ void down_store(const f32x4& acc, f32x4 (*s_red)[32], int rt, int T, int H,
-                           const float (&unscale)[kMaxT], const void* residual,
+                           const int (&et)[kMaxT], const void* residual,
                            void* out, int out_bf16) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = wave_id();
@@ -494,8 +557,7 @@ __device__ void down_store(const f32x4& acc, f32x4 (*s_red)[32], int rt, int T, 
     for (int r = 0; r < 4; ++r) {
       const int t = (hi ? 4 : 0) + r;
       if (t >= T) break;
-      const float u = hi ? unscale[4 + r] : unscale[r];
-      float v = Y[r] * (u * u);
+      float v = ldexpf(Y[r], hi ? et[4 + r] : et[r]);
       const size_t o = static_cast<size_t>(t) * H + row;
       if (out_bf16) {
         if (residual) v += bf16_to_float(static_cast<const uint16_t*>(residual)[o]);
@@ -506,6 +568,16 @@ __device__ void down_store(const f32x4& acc, f32x4 (*s_red)[32], int rt, int T, 
       }
     }
   }
+}
+
+// Largest signed byte of a 16-byte vector.
+__device__ __forceinline__ int max_i8x16(const u32x4& v) {
+  int m = kZeroExp;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) m = max(m, static_cast<int>(static_cast<int8_t>(v[w] >> (8 * b))));
+  return m;
 }
 
 // ------------------------------------------------------------ the kernels --
@@ -590,44 +662,69 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
 
   GateUpTiles<KTW> R;
   load_gateup<KTW>(expert_base(L, active ? S.expert[slot] : 0), active, H, I, rt, kq, lane, R);
+  int8_t* hexp = reinterpret_cast<int8_t*>(ws + kHeaderBytes + decode_h_bytes(T, k, I));
   if (blockIdx.x == 0) {
     DecodeHeader* hdr = reinterpret_cast<DecodeHeader*>(ws);
-    if (threadIdx.x < T) hdr->unscale[threadIdx.x] = 1.0f / s_smul[threadIdx.x];
     for (int i = threadIdx.x; i < S.n * kMaxT; i += NT)
       (&hdr->pidx[0][0])[i] = (&S.pidx[0][0])[i];
     if (threadIdx.x < S.n) hdr->expert[threadIdx.x] = S.expert[threadIdx.x];
     if (threadIdx.x == 0) hdr->n_slots = S.n;
+    if (!(RPER > 0 && T == 1)) {
+      // routed pairs that own no h~ row (an id outside [0, E), or a repeat
+      // of a token's id): their exponents, read by kernel 2's per-token
+      // maximum, are set to kZeroExp (no other block writes these rows)
+      const int RTI = I / kTileRows;
+      for (int q = threadIdx.x; q < T * k * RTI; q += NT) {
+        const int p = q / RTI;
+        const int s = S.pslot[p];
+        if (s < 0 || S.pidx[s][p / k] != p) hexp[q] = static_cast<int8_t>(kZeroExp);
+      }
+    }
   }
   if (static_cast<int>(blockIdx.x) >= n_rows) return;
   gateup_compute<KTW>(R, xs, T, H, I, rt, kq, slot, active, S, s_smul, s_red,
-                      reinterpret_cast<_Float16*>(ws + kHeaderBytes));
+                      reinterpret_cast<_Float16*>(ws + kHeaderBytes), hexp);
 }
 
 // Kernel 2: down row tile blockIdx.x.
+constexpr int kExpPre = 2;               // exponent vectors per lane loaded at kernel entry
+
+template <bool STAGED>
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     LayerArgs L, int T, int k, const void* __restrict__ residual, void* __restrict__ out,
-    int out_bf16, const uint8_t* __restrict__ ws, int stage_lds) {
+    int out_bf16, const uint8_t* __restrict__ ws) {
   extern __shared__ __align__(16) uint8_t dyn[];
   _Float16* hs = reinterpret_cast<_Float16*>(dyn);     // [T*k + T][I] when staged
   __shared__ int s_expert[kMaxSlots];
   __shared__ int s_pidx[kMaxSlots][kMaxT];
   __shared__ int s_n;
-  __shared__ float s_uns[kMaxT];
   __shared__ f32x4 s_red[kWaves][32];
   const DecodeHeader* hdr = reinterpret_cast<const DecodeHeader*>(ws);
   const _Float16* hin = reinterpret_cast<const _Float16*>(ws + kHeaderBytes);
   const int I = L.I;
   const int KTd = I / kTileCols;
+  const int RTI = I / kTileRows;
   const int rt = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
+  const int8_t* hexp = reinterpret_cast<const int8_t*>(ws + kHeaderBytes + decode_h_bytes(T, k, I));
 
   // h~ of all pairs: its layout does not depend on the header, so these
   // loads go first (always issued, so that later waits count them exactly)
   const int hch = (T * k + T) * I / 8;
   u32x4 hreg[kDownStage];
+  if constexpr (STAGED) {
 #pragma unroll
-  for (int q = 0; q < kDownStage; ++q)
-    hreg[q] = *reinterpret_cast<const u32x4*>(hin + 8 * min(static_cast<int>(threadIdx.x) + kThreads * q, hch - 1));
+    for (int q = 0; q < kDownStage; ++q)
+      hreg[q] = *reinterpret_cast<const u32x4*>(hin + 8 * min(static_cast<int>(threadIdx.x) + kThreads * q, hch - 1));
+  }
+  // the exponents of the pairs' h~ tiles (16 per vector), read by every
+  // wave: each wave derives every token's largest exponent E_t itself
+  const int vpp = RTI / 16;                                       // vectors per pair
+  const int nvec = (T * k + (L.shared ? T : 0)) * vpp;
+  u32x4 evec[kExpPre];
+#pragma unroll
+  for (int q = 0; q < kExpPre; ++q)
+    evec[q] = *reinterpret_cast<const u32x4*>(hexp + 16 * min(lane + kWave * q, nvec - 1));
 
   {
     // the header loads are issued together (clamped, unconditional)
@@ -639,24 +736,57 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     for (int q = 0; q < kPidxLoads; ++q)
       pv[q] = (&hdr->pidx[0][0])[min(i + kThreads * q, kMaxSlots * kMaxT - 1)];
     const int nv = hdr->n_slots;
-    const float uv = hdr->unscale[min(i, kMaxT - 1)];
     if (i < kMaxSlots) s_expert[i] = ev;
 #pragma unroll
     for (int q = 0; q < kPidxLoads; ++q)
       if (i + kThreads * q < kMaxSlots * kMaxT) (&s_pidx[0][0])[i + kThreads * q] = pv[q];
     if (i == 0) s_n = nv;
-    if (i < kMaxT) s_uns[i] = uv;
+  }
+
+  // E_t: the largest exponent over the token's pairs and row tiles (pairs
+  // without a row carry kZeroExp, which never wins)
+  int et[kMaxT];
+  {
+    int lm[kMaxT];
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t) lm[t] = kZeroExp;
+    auto take = [&](int v, const u32x4& e16) {
+      const int t = pair_token(v / vpp, T, k);
+      const int mx = max_i8x16(e16);
+#pragma unroll
+      for (int q = 0; q < kMaxT; ++q) lm[q] = (q == t) ? max(lm[q], mx) : lm[q];
+    };
+#pragma unroll
+    for (int q = 0; q < kExpPre; ++q)
+      if (lane + kWave * q < nvec) take(lane + kWave * q, evec[q]);
+    for (int v = lane + kWave * kExpPre; v < nvec; v += kWave)
+      take(v, *reinterpret_cast<const u32x4*>(hexp + 16 * v));
+#pragma unroll
+    for (int t = 0; t < kMaxT; ++t)
+      et[t] = t < T ? static_cast<int>(__ockl_wfred_max_u32(static_cast<uint32_t>(lm[t] + 256))) - 256 : 0;
   }
   __syncthreads();
   const int nitems = s_n * KTd;
 
   DownTiles<kDownBatch> D;
   load_down<kDownBatch>(L, s_expert, nitems, KTd, rt, 0, lane, D);
-  if (stage_lds) {
+  if constexpr (STAGED) {
+    // h~ into LDS, each 8-value chunk (one pair, half of a 16-row tile of I)
+    // rescaled from its tile's exponent to its token's E_t
+    const int cpp = I / 8;                                        // chunks per pair
+    auto put = [&](int ch, const u32x4& raw) {
+      const int p = ch / cpp;
+      const int t = pair_token(p, T, k);
+      int e_t = et[0];
+#pragma unroll
+      for (int q = 1; q < kMaxT; ++q) e_t = (q == t) ? et[q] : e_t;
+      const int d = static_cast<int>(hexp[static_cast<size_t>(p) * RTI + (ch % cpp) / 2]) - e_t;
+      *reinterpret_cast<f16x8*>(hs + 8 * ch) = scale_pow2(__builtin_bit_cast(f16x8, raw), min(d, 0));
+    };
 #pragma unroll
     for (int q = 0; q < kDownStage; ++q) {
       const int ch = threadIdx.x + kThreads * q;
-      if (ch < hch) *reinterpret_cast<u32x4*>(hs + 8 * ch) = hreg[q];
+      if (ch < hch) put(ch, hreg[q]);
     }
     for (int ch0 = threadIdx.x + kThreads * kDownStage; ch0 < hch; ch0 += 4 * kThreads) {
       u32x4 r[4];
@@ -665,29 +795,20 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
         r[u] = *reinterpret_cast<const u32x4*>(hin + 8 * min(ch0 + kThreads * u, hch - 1));
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (ch0 + kThreads * u < hch) *reinterpret_cast<u32x4*>(hs + 8 * (ch0 + kThreads * u)) = r[u];
+        if (ch0 + kThreads * u < hch) put(ch0 + kThreads * u, r[u]);
     }
   }
   __syncthreads();
 
-  // h~ from LDS or from global memory: two separate calls, so that each
-  // keeps its own address space (one pointer selected between them would
-  // make every h~ read a flat load, waited for before each MFMA)
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int per_wave = (nitems + kWaves - 1) / kWaves;
-  auto run = [&](const _Float16* hsrc) {
-    mma_down<kDownBatch>(D, nitems, KTd, 0, lane, hsrc, s_pidx, T, I, acc);
-    for (int j0 = kDownBatch; j0 < per_wave; j0 += kDownBatch) {
-      load_down<kDownBatch>(L, s_expert, nitems, KTd, rt, j0, lane, D);
-      mma_down<kDownBatch>(D, nitems, KTd, j0, lane, hsrc, s_pidx, T, I, acc);
-    }
-  };
-  if (stage_lds) run(hs);
-  else run(hin);
-  float uns[kMaxT];
-#pragma unroll
-  for (int t = 0; t < kMaxT; ++t) uns[t] = s_uns[t];
-  down_store(acc, s_red, rt, T, L.H, uns, residual, out, out_bf16);
+  const _Float16* hsrc = STAGED ? hs : hin;
+  mma_down<kDownBatch, STAGED>(D, nitems, KTd, 0, lane, hsrc, s_pidx, T, I, hexp, et, acc);
+  for (int j0 = kDownBatch; j0 < per_wave; j0 += kDownBatch) {
+    load_down<kDownBatch>(L, s_expert, nitems, KTd, rt, j0, lane, D);
+    mma_down<kDownBatch, STAGED>(D, nitems, KTd, j0, lane, hsrc, s_pidx, T, I, hexp, et, acc);
+  }
+  down_store(acc, s_red, rt, T, L.H, et, residual, out, out_bf16);
 }
 
 // -------------------------------------------------------------- launching --
@@ -760,9 +881,7 @@ int device_cus() {
 
 size_t decode_workspace_bytes(int T, int k, int H, int I) {
   (void)H;
-  const size_t pairs = static_cast<size_t>(T) * k + T;
-  const size_t h = pairs * I * sizeof(_Float16);
-  return kHeaderBytes + (h + 255) / 256 * 256;
+  return kHeaderBytes + decode_h_bytes(T, k, I) + decode_hexp_bytes(T, k, I);
 }
 
 hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
@@ -803,9 +922,12 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
     }
   }
   if (e != hipSuccess) return e;
-  return launch_kernel(K_DECODE_DOWN, decode_down_kernel, dim3(L.H / kTileRows), dim3(kThreads),
-                       static_cast<uint32_t>(stage_h ? lds_h : 0), s, L, T, k, residual, out,
-                       out_bf16, static_cast<const uint8_t*>(ws), stage_h);
+  if (stage_h)
+    return launch_kernel(K_DECODE_DOWN, decode_down_kernel<true>, dim3(L.H / kTileRows), dim3(kThreads),
+                         static_cast<uint32_t>(lds_h), s, L, T, k, residual, out, out_bf16,
+                         static_cast<const uint8_t*>(ws));
+  return launch_kernel(K_DECODE_DOWN, decode_down_kernel<false>, dim3(L.H / kTileRows), dim3(kThreads),
+                       0u, s, L, T, k, residual, out, out_bf16, static_cast<const uint8_t*>(ws));
 }
 
 }  // namespace moeq2

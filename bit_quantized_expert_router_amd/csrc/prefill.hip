@@ -20,12 +20,16 @@
 //            is dequantized once per item and used by every M tile; two
 //            register sets keep the next K tile's weights in flight while
 //            one is multiplied),
-//            v_mfma_f32_16x16x32_f16, SwiGLU epilogue:
-//            h~[row] = w * silu(g) * u * s_t^2  (fp16, sorted-row order).
-//   down     work item x 256-row block of H, 8 waves x 2 row tiles: A = h~
-//            rows (LDS), B = down tiles; y~[row] = W_down h~ (fp16).
-//   combine  token t: out = (sum_j y~[pair_pos[t,j]] + y~[shared row]) / s_t^2
-//            (+ residual), j ascending: fixed order, no atomics.
+//            v_mfma_f32_16x16x32_f16, SwiGLU epilogue: h = w * silu(g) * u
+//            in float32, stored (sorted-row order) as fp16 h * 2^-e with one
+//            exponent e per (row, 16-row tile of I) in a byte array, so that
+//            |h~| < 1 and fp16 cannot overflow whatever the weights' scales.
+//   down     work item x 256-row block of H, 8 waves x 2 row tiles: A = h
+//            rows rescaled to one exponent per row (the row's largest) while
+//            they are moved into LDS, B = down tiles; y = acc * 2^E_row, stored
+//            as fp16 y * 2^-F with one exponent F per (row, 32 columns).
+//   combine  token t: out = sum_j y~[pair_pos[t,j]] * 2^F + y~[shared row]
+//            * 2^F (+ residual), j ascending: fixed order, no atomics.
 // Workgroup ids are remapped so that every XCD gets an equal share of the
 // real work and the row blocks of one work item (which read the same A rows)
 // run on the same XCD and share its L2.  Chunks of up to 4096 tokens list
@@ -59,9 +63,12 @@ struct PrefillWs {
   int32_t* row_tok;    // [rows] token of each sorted row
   float* row_w;        // [rows] routing weight of each sorted row (1 for the shared expert)
   _Float16* x16;       // [T][H]
-  _Float16* h;         // [rows][I]
-  _Float16* y;         // [rows][H]
+  _Float16* h;         // [rows][I]     h * 2^-hexp
+  _Float16* y;         // [rows][H]     y * 2^-yexp
+  int8_t* hexp;        // [rows][I/16]  exponent of each 16-row tile of I
+  int8_t* yexp;        // [rows][H/32]  exponent of each 32 columns of H
 };
+constexpr int kYGroup = 16 * kDownRTW;       // columns of y per exponent (one wave's row tiles)
 
 __host__ __device__ inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
@@ -81,7 +88,9 @@ __host__ __device__ inline PrefillWs carve(void* base, int T, int E, int k, int 
   w.row_w = reinterpret_cast<float*>(p); p += align256(sizeof(float) * rows);
   w.x16 = reinterpret_cast<_Float16*>(p); p += align256(sizeof(_Float16) * static_cast<size_t>(T) * H);
   w.h = reinterpret_cast<_Float16*>(p); p += align256(sizeof(_Float16) * rows * I);
-  w.y = reinterpret_cast<_Float16*>(p);
+  w.y = reinterpret_cast<_Float16*>(p); p += align256(sizeof(_Float16) * rows * H);
+  w.hexp = reinterpret_cast<int8_t*>(p); p += align256(rows * (I / kTileRows));
+  w.yexp = reinterpret_cast<int8_t*>(p);
   return w;
 }
 
@@ -377,6 +386,63 @@ __device__ __forceinline__ f16x8 a_frag(const _Float16* buf, int j, int mt, int 
   return *reinterpret_cast<const f16x8*>(buf + ((4 * j + mt) * 64 + lane) * 8);
 }
 
+// A tile staging of the down GEMM: the item's h rows, laid out as ATile,
+// but each fragment (8 values of one row inside one 16-row tile of I) is
+// rescaled from its tile's exponent to the row's exponent E_row on its way
+// into LDS, so every MFMA row shares one scale.  The tile exponents come
+// through a byte buffer resource over the item's hexp rows, loaded with the
+// fragment they belong to.
+template <int NMT>
+struct HTile {
+  static constexpr int NR = NMT;
+  __amdgpu_buffer_rsrc_t rs, re;
+  uint32_t off[NR], eoff[NR];
+  int slot[NR];
+  int er[NR];        // E_row of each fragment's row
+  u32x4 r[2][NR];
+  int ex[2][NR];     // tile exponent of each fragment, per register set
+  __device__ __forceinline__ int row_of(int i) const {
+    const int lane = threadIdx.x & 63;
+    return i * 16 + (lane & 15);
+  }
+  __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t hrsrc, __amdgpu_buffer_rsrc_t ersrc,
+                                       uint32_t row_bytes, int RTI, int nrows) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int j = w & 7, m = lane & 15, g = lane >> 4;
+    rs = hrsrc;
+    re = ersrc;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int row = min(i * 16 + m, nrows - 1);
+      slot[i] = 4 * j + i;
+      off[i] = static_cast<uint32_t>(row) * row_bytes + 2u * static_cast<uint32_t>(32 * j + 8 * g);
+      eoff[i] = static_cast<uint32_t>(row * RTI + 2 * j + (g >> 1));
+    }
+  }
+  template <int SET>
+  __device__ __forceinline__ void load(int kt) {
+    const uint32_t k0 = static_cast<uint32_t>(kt) * (2 * kTileCols);
+    const uint32_t e0 = static_cast<uint32_t>(kt) * (kTileCols / kTileRows);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      r[SET][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], k0, 0);
+      ex[SET][i] = static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(re, eoff[i], e0, 0));
+    }
+  }
+  __device__ __forceinline__ void set_row_exponents(const int* s_erow, int nrows) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) er[i] = s_erow[min(row_of(i), nrows - 1)];
+  }
+  template <int SET>
+  __device__ __forceinline__ void store(_Float16* buf) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      *reinterpret_cast<f16x8*>(buf + (slot[i] * 64 + lane) * 8) =
+          scale_pow2(__builtin_bit_cast(f16x8, r[SET][i]), min(ex[SET][i] - er[i], 0));
+  }
+};
+
 // One K tile of the gate/up product for NMT 16-row M tiles.
 template <int NMT>
 __device__ __forceinline__ void gateup_ktile(const u32x4 (&b)[4], const _Float16* abuf, int lane,
@@ -513,18 +579,21 @@ __device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs&
   else
     k_loop<RING>(KT, b, load_b, A, s_a, mul);
 
+  // h rows of this wave's 16-row tile of I: one exponent per (row, tile)
   const int col = rt * 16 + m;
+  const int RTI = I / kTileRows;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int rl = mt * 16 + 4 * g + r;
-      if (rl < nrows) {
-        const float u = s_u[rl];
-        const float s = 1.0f / u;
-        const float gv = acc_g[mt][r] * u, uv = acc_u[mt][r] * u;
-        const float h = s_w[rl] * silu(gv) * uv * (s * s);
-        ws.h[static_cast<size_t>(row0 + rl) * I + col] = static_cast<_Float16>(h);
+      const int rl = mt * 16 + 4 * g + r;            // uniform in each 16-lane row
+      const bool ok = rl < nrows;
+      const float u = ok ? s_u[rl] : 1.0f;
+      const float h = ok ? s_w[rl] * silu(acc_g[mt][r] * u) * (acc_u[mt][r] * u) : 0.0f;
+      const int e = block_exponent(row16_max(fabsf(h)));
+      if (ok) {
+        ws.h[static_cast<size_t>(row0 + rl) * I + col] = static_cast<_Float16>(ldexpf(h, -e));
+        if (m == 0) ws.hexp[static_cast<size_t>(row0 + rl) * RTI + rt] = static_cast<int8_t>(e);
       }
     }
   }
@@ -581,11 +650,13 @@ __device__ __forceinline__ void down_ktile(const u32x4 (&b)[2 * kDownRTW], const
 
 template <int NMT, int RING, int KTC>
 __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& ws, int e, int row0,
-                                          int nrows, int rt0, _Float16 (*s_a)[kATileHalves]) {
+                                          int nrows, int rt0, _Float16 (*s_a)[kATileHalves],
+                                          int* s_erow) {
   const int H = L.H, I = L.I;
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
   const int KT = I / kTileCols;
+  const int RTI = I / kTileRows;
   const uint32_t mat = static_cast<uint32_t>(
       __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(I) * H * 5 / 16)));
   const __amdgpu_buffer_rsrc_t rs = expert_rsrc(expert_base(L, e), 3 * mat);
@@ -602,13 +673,30 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
   u32x4 b[RING][NB];
 #pragma unroll
   for (int u = 0; u < RING; ++u) load_b(b[u], u);
-  ATile<NMT> A;   // the item's h rows are consecutive: a resource over just them
+  HTile<NMT> A;   // the item's h rows and their exponents are consecutive: resources over just them
   const uint32_t row_bytes = static_cast<uint32_t>(I) * 2u;
+  const int8_t* erows = ws.hexp + static_cast<size_t>(row0) * RTI;
   A.init(expert_rsrc(reinterpret_cast<const uint8_t*>(ws.h + static_cast<size_t>(row0) * I),
                      static_cast<uint32_t>(nrows) * row_bytes),
-         [&](int i) { return static_cast<uint32_t>(i) * row_bytes; }, nrows);
+         expert_rsrc(reinterpret_cast<const uint8_t*>(erows), static_cast<uint32_t>(nrows * RTI)),
+         row_bytes, RTI, nrows);
   A.template load<0>(0);
   A.template load<1>(min(1, KT - 1));
+  // E_row: the largest tile exponent of each row (RTI is a multiple of 16)
+  if (static_cast<int>(threadIdx.x) < nrows) {
+    const u32x4* v = reinterpret_cast<const u32x4*>(erows + static_cast<size_t>(threadIdx.x) * RTI);
+    int mx = kZeroExp;
+    for (int q = 0; q < RTI / 16; ++q) {
+      const u32x4 w = v[q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) mx = max(mx, static_cast<int>(static_cast<int8_t>(w[c] >> (8 * s))));
+    }
+    s_erow[threadIdx.x] = mx;
+  }
+  __syncthreads();
+  A.set_row_exponents(s_erow, nrows);
   A.template store<0>(s_a[0]);
   __syncthreads();
 
@@ -626,15 +714,29 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
   else
     k_loop<RING>(KT, b, load_b, A, s_a, mul);
 
+  // y = acc * 2^E_row; one exponent per (row, this wave's 32 columns)
+  const int yg = rt0 / kDownRTW;
+  const int NYG = H / kYGroup;
 #pragma unroll
-  for (int q = 0; q < kDownRTW; ++q) {
-    const int col = (rt0 + q) * 16 + m;
+  for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
+    for (int r = 0; r < 4; ++r) {
+      const int rl = mt * 16 + 4 * g + r;            // uniform in each 16-lane row
+      const bool ok = rl < nrows;
+      const int erw = ok ? s_erow[rl] : 0;
+      float yv[kDownRTW];
+      float mx = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = mt * 16 + 4 * g + r;
-        if (rl < nrows) ws.y[static_cast<size_t>(row0 + rl) * H + col] = static_cast<_Float16>(acc[q][mt][r]);
+      for (int q = 0; q < kDownRTW; ++q) {
+        yv[q] = ok ? ldexpf(acc[q][mt][r], erw) : 0.0f;
+        mx = fmaxf(mx, fabsf(yv[q]));
+      }
+      const int f = block_exponent(row16_max(mx));
+      if (ok) {
+#pragma unroll
+        for (int q = 0; q < kDownRTW; ++q)
+          ws.y[static_cast<size_t>(row0 + rl) * H + (rt0 + q) * 16 + m] = static_cast<_Float16>(ldexpf(yv[q], -f));
+        if (m == 0) ws.yexp[static_cast<size_t>(row0 + rl) * NYG + yg] = static_cast<int8_t>(f);
       }
     }
   }
@@ -643,6 +745,7 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
 template <int KTC>   // I / 256 when fixed at compile time, else 0
 __global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, PrefillWs ws) {
   __shared__ __align__(16) _Float16 s_a[2][kATileHalves];
+  __shared__ int s_erow[kGroupRows];
   const int RB = L.H / kDownRowsPerBlock;
   const int2 wu = work_unit(blockIdx.x, ws.hdr, RB);
   if (wu.x < 0) return;
@@ -652,17 +755,18 @@ __global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, Pre
   const int e = it.x, row0 = it.y, nrows = it.z;
   const int rt0 = (rb * kGemmWaves + static_cast<int>(threadIdx.x >> 6)) * kDownRTW;
   switch ((nrows + 15) / 16) {
-    case 1: down_body<1, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a); break;
-    case 2: down_body<2, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a); break;
-    case 3: down_body<3, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a); break;
-    default: down_body<4, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a); break;
+    case 1: down_body<1, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow); break;
+    case 2: down_body<2, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow); break;
+    case 3: down_body<3, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow); break;
+    default: down_body<4, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow); break;
   }
 }
 
 // ------------------------------------------------------------------ combine --
 // One thread per (token, 8-column chunk): the token's k rows of y~ (and the
-// shared row) are all requested before the first is summed, in 16-byte loads;
-// the sum runs over j ascending, then the shared row, in fp32.
+// shared row) are all requested before the first is summed, in 16-byte loads,
+// with each row's exponent for these columns; the sum runs over j ascending,
+// then the shared row, in fp32.
 __global__ __launch_bounds__(256) void prefill_combine_kernel(
     int T, int H, int k, int has_shared, const int32_t* __restrict__ pair_pos,
     const void* residual, void* out, int out_bf16, PrefillWs ws) {   // residual may alias out
@@ -672,33 +776,38 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(
   const int t = static_cast<int>(g / nch);
   const int c = static_cast<int>(g - static_cast<long long>(t) * nch);
   const int P = T * k;
-  int pos[MOE_MAX_TOPK];
+  const int NYG = H / kYGroup;
+  const int yg = c / (kYGroup / 8);
+  int pos[MOE_MAX_TOPK + 1];
 #pragma unroll
   for (int j = 0; j < MOE_MAX_TOPK; ++j)
     pos[j] = j < k ? min(max(pair_pos[static_cast<size_t>(t) * k + j], 0), P - 1) : 0;
+  pos[MOE_MAX_TOPK] = P + t;
   f16x8 v[MOE_MAX_TOPK + 1];
+  int f[MOE_MAX_TOPK + 1];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j)
-    if (j < k) v[j] = *reinterpret_cast<const f16x8*>(ws.y + static_cast<size_t>(pos[j]) * H + 8 * c);
-  if (has_shared) v[MOE_MAX_TOPK] = *reinterpret_cast<const f16x8*>(ws.y + static_cast<size_t>(P + t) * H + 8 * c);
+  for (int j = 0; j <= MOE_MAX_TOPK; ++j) {
+    if (j < k || (j == MOE_MAX_TOPK && has_shared)) {
+      v[j] = *reinterpret_cast<const f16x8*>(ws.y + static_cast<size_t>(pos[j]) * H + 8 * c);
+      f[j] = ws.yexp[static_cast<size_t>(pos[j]) * NYG + yg];
+    }
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j)
-    if (j < k)
+  for (int j = 0; j <= MOE_MAX_TOPK; ++j) {
+    if (j < k || (j == MOE_MAX_TOPK && has_shared)) {
+      const float sc = ldexpf(1.0f, f[j]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += static_cast<float>(v[j][i]);
-  if (has_shared)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += static_cast<float>(v[MOE_MAX_TOPK][i]);
-  const float u = ws.unscale[t];
-  const float u2 = u * u;
+      for (int i = 0; i < 8; ++i) acc[i] += static_cast<float>(v[j][i]) * sc;
+    }
+  }
   const size_t o = static_cast<size_t>(t) * H + 8 * c;
   if (out_bf16) {
     u32x4 rs = {0u, 0u, 0u, 0u}, w;
     if (residual) rs = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(residual) + o);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float lo = acc[2 * q] * u2, hi = acc[2 * q + 1] * u2;
+      float lo = acc[2 * q], hi = acc[2 * q + 1];
       if (residual) {
         lo += __uint_as_float(rs[q] << 16);
         hi += __uint_as_float(rs[q] & 0xFFFF0000u);
@@ -709,7 +818,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(
   } else {
     f32x4 a, b;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { a[i] = acc[i] * u2; b[i] = acc[4 + i] * u2; }
+    for (int i = 0; i < 4; ++i) { a[i] = acc[i]; b[i] = acc[4 + i]; }
     if (residual) {
       const f32x4* rp = reinterpret_cast<const f32x4*>(static_cast<const float*>(residual) + o);
       a += rp[0];
@@ -728,7 +837,8 @@ size_t prefill_workspace_bytes(int T, int E, int k, int H, int I) {
   return 256 + align256(sizeof(int4) * max_items(T, E, k)) + align256(sizeof(float) * T) +
          align256(sizeof(int32_t) * rows) + align256(sizeof(float) * rows) +
          align256(sizeof(_Float16) * static_cast<size_t>(T) * H) + align256(sizeof(_Float16) * rows * I) +
-         align256(sizeof(_Float16) * rows * H);
+         align256(sizeof(_Float16) * rows * H) + align256(rows * (I / kTileRows)) +
+         align256(rows * (H / kYGroup));
 }
 
 hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,

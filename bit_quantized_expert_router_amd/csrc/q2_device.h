@@ -106,13 +106,49 @@ __device__ __forceinline__ u32x4 load_scales(__amdgpu_buffer_rsrc_t r, uint32_t 
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
-// Per-token power-of-two normaliser: returns s with max_abs * s in [0.5, 1)
-// (s = 1 for an all-zero token).
+// Per-token power-of-two normaliser of the activations: returns s = 2^-e
+// with max_abs * s in [0.5, 1) (s = 1 for an all-zero token), e clamped to
+// [-60, 60] so that s and 1/s stay normal float32 numbers.  A token whose
+// largest |x_hat| is beyond 2^60 has outputs (degree 2 in x) beyond float32.
 __device__ __forceinline__ float pow2_normaliser(float max_abs) {
   if (!(max_abs > 0.0f)) return 1.0f;
   int e;
   frexpf(max_abs, &e);
+  e = e < -60 ? -60 : (e > 60 ? 60 : e);
   return ldexpf(1.0f, -e);
+}
+
+// Exponent of a block of intermediate values (h or y rows): e with
+// max_abs * 2^-e in [0.5, 1), so the block stored as fp16 v * 2^-e lies in
+// (-1, 1) and cannot overflow; clamped to [-120, 127].  An all-zero block
+// gets kZeroExp, below every other exponent, so it never sets a maximum.
+constexpr int kZeroExp = -128;
+__device__ __forceinline__ int block_exponent(float max_abs) {
+  if (!(max_abs > 0.0f)) return kZeroExp;
+  int e;
+  frexpf(max_abs, &e);
+  return e < -120 ? -120 : (e > 127 ? 127 : e);
+}
+
+// Maximum over the 16 lanes of this lane's DPP row (lanes 16r..16r+15),
+// returned in every lane of the row; all 16 lanes must be active.
+__device__ __forceinline__ float row16_max(float v) {
+  int x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false)));  // quad [1,0,3,2]
+  x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false)));  // quad [2,3,0,1]
+  x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false))); // half-row mirror
+  x = __float_as_int(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false))); // row mirror
+  return v;
+}
+
+// 8 fp16 values times 2^d for d <= 0 (exact unless the result is subnormal;
+// below 2^-24 of the input the values become zero).
+__device__ __forceinline__ f16x8 scale_pow2(const f16x8& a, int d) {
+  const _Float16 s = d < -24 ? static_cast<_Float16>(0.0f) : static_cast<_Float16>(ldexpf(1.0f, d));
+  return a * s;
 }
 
 __device__ __forceinline__ float bf16_to_float(uint16_t b) {

@@ -69,6 +69,26 @@ def expert_blob(rng: np.random.Generator, E: int, H: int, I: int,
     return buf
 
 
+def constant_expert_blob(E: int, H: int, I: int, code: int, scale: float) -> np.ndarray:
+    """E experts whose every 2-bit code is `code` (0..3) and every block scale
+    fp16(`scale`), in the same byte layout as expert_blob: each code byte
+    repeats the code four times and every record's scale bytes hold the fp16
+    value.  Inputs for closed-form cases (all weights equal)."""
+    if not 0 <= code <= 3:
+        raise ValueError("code must be in 0..3")
+    stride = expert_stride(H, I)
+    nb = expert_nbytes(H, I)
+    buf = np.zeros(E * stride, dtype=np.uint8)
+    nrec = nb // TILE_BYTES
+    byte = code | (code << 2) | (code << 4) | (code << 6)
+    sc = np.full(128, scale, dtype="<f2").view(np.uint8)
+    for e in range(E):
+        rec = buf[e * stride:e * stride + nb].reshape(nrec, TILE_BYTES)
+        rec[:, :SCALE_OFFSET] = byte
+        rec[:, SCALE_OFFSET:] = sc[None, :]
+    return buf
+
+
 def device_expert_blob(E: int, H: int, I: int, seed: int, device="cuda",
                        scale_lo: float = 0.01, scale_hi: float = 0.05):
     """Same recipe, generated with torch's RNG straight into device memory

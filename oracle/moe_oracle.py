@@ -272,7 +272,10 @@ def rms_prenorm(x: np.ndarray) -> np.ndarray:
 
 
 def silu(a: np.ndarray) -> np.ndarray:
-    return a / (1.0 + np.exp(-a))
+    # for a below about -709, exp(-a) is inf in float64 and a / inf = -0.0,
+    # the correctly rounded value; the overflow is expected, not reported
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
 
 
 def expert_ffn(xh: np.ndarray, Wg, Wu, Wd) -> np.ndarray:

@@ -119,7 +119,7 @@ def test_route_validation(lib):
 def forward(lib, which, **kw):
     from bit_quantized_expert_router_amd.binding import _Layer
     a = dict(experts=FAKE, shared=FAKE, stride=245760, E=64, H=1024, I=256, x=FAKE, xd=0, T=1,
-             ids=FAKE, w=FAKE, k=4, res=None, out=FAKE + 4096, od=0, flags=0, ws=FAKE, wsb=1 << 30)
+             ids=FAKE, w=FAKE, k=4, res=None, out=FAKE + (1 << 34), od=0, flags=0, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     L = _Layer(a["experts"], a["shared"], a["stride"], a["E"], a["H"], a["I"])
     if which == "routed":
@@ -163,6 +163,14 @@ def test_forward_validation(lib, which):
     assert forward(lib, which, wsb=100) == -3
     assert forward(lib, which, ws=FAKE + 8) == -1
     assert forward(lib, which, res=FAKE + 8) == -1         # unaligned residual
+    # out shares bytes with x: fp32 x of T = 1, H = 1024 covers 4096 bytes
+    assert forward(lib, which, out=FAKE + 16) == -1
+    assert forward(lib, which, out=FAKE - 4096 + 16) == -1
+    assert forward(lib, which, out=FAKE + 2048, xd=1, od=1, T=2) == -1   # bf16 x of T = 2 covers 4096
+    assert b"overlap" in lib.moe_last_error()
+    # residual partly over out (residual == out itself is allowed)
+    assert forward(lib, which, res=FAKE + (1 << 34) + 1024) == -1
+    assert b"residual" in lib.moe_last_error()
     if which in ("decode", "routed"):
         assert forward(lib, which, T=9) == -2
     if which == "routed":

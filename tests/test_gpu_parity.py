@@ -463,7 +463,10 @@ def test_decode_prefill_agree(B, layer_full):
     assert np.abs(a - b).max() <= 1e-2 * rms
 
 
-def _sampled_prefill(B, L, T, kind, seed, n_sample=12, flags=0):
+def _prefill_check(B, L, T, kind, seed, pick=None, flags=0):
+    """One prefill call at the 512-expert layer's widths (the call the
+    benchmark makes), run twice (bitwise equal); the tokens `pick(ids,
+    hist)` returns -- every token when pick is None -- against the oracle."""
     rng = synth.rng_for(3, seed, T)
     xd, xv = synth.activations(rng, T, 3072, "bf16")
     if kind == "biased":
@@ -475,9 +478,49 @@ def _sampled_prefill(B, L, T, kind, seed, n_sample=12, flags=0):
     out = run_prefill(B, L, dev_x(xd, "bf16"), r, flags=flags)
     a = run_prefill(B, L, dev_x(xd, "bf16"), r, flags=flags)
     assert torch.equal(out, a)   # deterministic
-    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_sample - 2, replace=False)]))
+    if pick is None:
+        ref = O.moe_layer(xv, ids, w, L.ref, prenorm=bool(flags))
+        check_out(to_np(out), ref, f"prefill T={T} {kind} every token")
+        return
+    toks = np.unique(np.concatenate([[0, T - 1], pick(ids, O.route_histogram(ids, 512))]))
     ref = O.moe_layer(xv, ids, w, L.ref, prenorm=bool(flags), tokens=toks)
-    check_out(to_np(out[torch.from_numpy(toks).cuda()]), ref, f"prefill T={T} {kind} sampled")
+    check_out(to_np(out[torch.from_numpy(toks).cuda()]), ref, f"prefill T={T} {kind}, {toks.size} tokens")
+
+
+def expert_order_tokens(ids, hist, T, k, E, row_blocks, rows_per_item=64):
+    """Tokens that the chunks longer than 4096 tokens place at the edges of
+    their work: every row of the most loaded expert's first and last 64-row
+    items, and the first and last row of the first and last item of each
+    XCD's contiguous range of (item, row block) units, for each GEMM's count
+    of row blocks per item (items in expert order, the shared expert's T
+    rows last)."""
+    counts, offsets, sp, _ = hist
+    items = []                                      # (first sorted row, rows)
+    for e in range(E):
+        for g in range(0, int(counts[e]), rows_per_item):
+            items.append((int(offsets[e]) + g, min(rows_per_item, int(counts[e]) - g)))
+    for g in range(0, T, rows_per_item):
+        items.append((T * k + g, min(rows_per_item, T - g)))
+
+    def tok(row):
+        return int(sp[row]) // k if row < T * k else row - T * k
+
+    picked = set()
+    head = int(np.argmax(counts))
+    first = int(offsets[head])
+    last = first + (int(counts[head]) - 1) // rows_per_item * rows_per_item
+    for r0 in (first, last):
+        n = min(rows_per_item, first + int(counts[head]) - r0)
+        picked.update(tok(r) for r in range(r0, r0 + n))
+    for RB in row_blocks:
+        units = len(items) * RB
+        per = (units + 7) // 8
+        for x in range(8):
+            for u in (x * per, min((x + 1) * per, units) - 1):
+                if 0 <= u < units:
+                    r0, n = items[u // RB]
+                    picked.update((tok(r0), tok(r0 + n - 1)))
+    return np.array(sorted(picked))
 
 
 @pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
@@ -537,8 +580,8 @@ def test_prefill_item_orders(B, T, shared):
     """Both work-item orders of the prefill kernels: lists in size order dealt
     to the XCDs in turn (chunks of up to 4096 tokens) and lists in expert
     order split into contiguous ranges (longer chunks), with and without a
-    shared expert; Zipf routing gives one expert many 64-row items.  Sampled
-    tokens against the oracle."""
+    shared expert; Zipf routing gives one expert many 64-row items.  Every
+    token against the oracle."""
     L = Layer(B, 11, 64, 1024, 256, shared=shared)
     print(f"prefill item order T={T} shared={shared}", flush=True)
     rng = synth.rng_for(44, T, int(shared))
@@ -547,17 +590,26 @@ def test_prefill_item_orders(B, T, shared):
     ids, w, r = route_both(B, lg, 4, True)
     assert_route_exact(ids, w, r, 64, True)
     out = run_prefill(B, L, dev_x(xd, "bf16"), r)
-    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 30, replace=False)]))
-    ref = O.moe_layer(xv, ids, w, L.ref, tokens=toks)
-    check_out(to_np(out[torch.from_numpy(toks).cuda()]), ref, f"prefill T={T} shared={shared} sampled")
+    ref = O.moe_layer(xv, ids, w, L.ref)
+    check_out(to_np(out), ref, f"prefill T={T} shared={shared} every token")
 
 
-def test_prefill_1024_biased_sampled(B, layer_full):
-    _sampled_prefill(B, layer_full, 1024, "biased", 0)
+def test_prefill_1024_biased_every_token(B, layer_full):
+    """The 1024-token chunk with the skewed router (bias N(0, 0.5)): every
+    token of the whole chunk against the oracle."""
+    _prefill_check(B, layer_full, 1024, "biased", 0)
 
 
-def test_prefill_32768_zipf_sampled(B, layer_full):
-    _sampled_prefill(B, layer_full, 32768, "zipf", 1, n_sample=8, flags=1)
+def test_prefill_32768_zipf(B, layer_full):
+    """A 32768-token Zipf chunk with the pre-norm: every row of the most
+    loaded expert's first and last items, the edges of every XCD's range of
+    work for both GEMM kernels (6 and 12 row blocks per item), and 16 more
+    random tokens, against the oracle."""
+    def pick(ids, hist):
+        rng = np.random.default_rng(5)
+        edge = expert_order_tokens(ids, hist, 32768, 10, 512, (768 // 128, 3072 // 256))
+        return np.concatenate([edge, rng.choice(32768, 16, replace=False)])
+    _prefill_check(B, layer_full, 32768, "zipf", 1, pick=pick, flags=1)
 
 
 def test_graph_replay_matches_eager(B, layer_full):

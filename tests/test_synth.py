@@ -43,3 +43,14 @@ def test_zipf_logits_skew():
     ids, _ = O.route_topk(lg, 1)
     counts = np.bincount(ids[:, 0], minlength=512)
     assert counts.max() > 10 * np.median(counts[counts > 0])
+
+
+def test_constant_blob_decodes_to_one_code_and_scale():
+    for code in (0, 2, 3):
+        a = synth.constant_expert_blob(2, 512, 256, code, 0.05)
+        blob = O.ExpertBlob(a, 2, 512, 256)
+        for e in range(2):
+            for off, (R, K) in ((0, (256, 512)), (40960, (256, 512)), (81920, (512, 256))):
+                codes, sc = O.decode_matrix(a, e * blob.stride + off, R, K)
+                assert np.all(codes == code)
+                assert np.all(sc == np.float16(0.05))
