@@ -509,14 +509,11 @@ template <int DB, bool STAGED>
 __device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int KTd, int j0,
                                          int lane, const _Float16* hsrc,
                                          const int (*pidx)[kMaxT], int T, int I,
-                                         const int8_t* hexp, const int (&et)[kMaxT],
-                                         f32x4& acc) {
+                                         const int8_t* hexp, const int* s_et, f32x4& acc) {
   const int wid = wave_id();
   const int m = lane & 15, g = lane >> 4;
   const int RTI = I / kTileRows;
-  int my_et = et[0];
-#pragma unroll
-  for (int t = 1; t < kMaxT; ++t) my_et = (m == t) ? et[t] : my_et;
+  const int my_et = STAGED ? 0 : s_et[m < T ? m : 0];
 #pragma unroll
   for (int b = 0; b < DB; ++b) {
     const int wi = wid + kWaves * (j0 + b);
@@ -542,7 +539,7 @@ __device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int
 // Sum of the 8 waves' accumulators (wave order) and the output rows of tile
 // rt: out = acc * 2^E_t (+ residual).
 __device__ void down_store(const f32x4& acc, f32x4 (*s_red)[32], int rt, int T, int H,
-                           const int (&et)[kMaxT], const void* residual,
+                           const int* s_et, const void* residual,
                            void* out, int out_bf16) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = wave_id();
@@ -557,7 +554,7 @@ __device__ void down_store(const f32x4& acc, f32x4 (*s_red)[32], int rt, int T, 
     for (int r = 0; r < 4; ++r) {
       const int t = (hi ? 4 : 0) + r;
       if (t >= T) break;
-      float v = ldexpf(Y[r], hi ? et[4 + r] : et[r]);
+      float v = ldexpf(Y[r], s_et[t]);
       const size_t o = static_cast<size_t>(t) * H + row;
       if (out_bf16) {
         if (residual) v += bf16_to_float(static_cast<const uint16_t*>(residual)[o]);
@@ -669,10 +666,11 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
       (&hdr->pidx[0][0])[i] = (&S.pidx[0][0])[i];
     if (threadIdx.x < S.n) hdr->expert[threadIdx.x] = S.expert[threadIdx.x];
     if (threadIdx.x == 0) hdr->n_slots = S.n;
-    if (!(RPER > 0 && T == 1)) {
+    if constexpr (RPER == 0) {
       // routed pairs that own no h~ row (an id outside [0, E), or a repeat
-      // of a token's id): their exponents, read by kernel 2's per-token
-      // maximum, are set to kZeroExp (no other block writes these rows)
+      // of a token's id; the top-k of the logits never makes one): their
+      // exponents, read by kernel 2's per-token maximum, are set to
+      // kZeroExp (no other block writes these rows)
       const int RTI = I / kTileRows;
       for (int q = threadIdx.x; q < T * k * RTI; q += NT) {
         const int p = q / RTI;
@@ -698,6 +696,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   __shared__ int s_expert[kMaxSlots];
   __shared__ int s_pidx[kMaxSlots][kMaxT];
   __shared__ int s_n;
+  __shared__ int s_et[kMaxT];       // E_t of each token
   __shared__ f32x4 s_red[kWaves][32];
   const DecodeHeader* hdr = reinterpret_cast<const DecodeHeader*>(ws);
   const _Float16* hin = reinterpret_cast<const _Float16*>(ws + kHeaderBytes);
@@ -711,11 +710,18 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   // h~ of all pairs: its layout does not depend on the header, so these
   // loads go first (always issued, so that later waits count them exactly)
   const int hch = (T * k + T) * I / 8;
+  const int cpp = I / 8;                                          // 8-value chunks per pair
+  // exponent of chunk ch: that of its pair's 16-row tile of I
+  auto chunk_exp = [&](int ch) { return hexp + static_cast<size_t>(ch / cpp) * RTI + (ch % cpp) / 2; };
   u32x4 hreg[kDownStage];
+  int hx[kDownStage];
   if constexpr (STAGED) {
 #pragma unroll
-    for (int q = 0; q < kDownStage; ++q)
-      hreg[q] = *reinterpret_cast<const u32x4*>(hin + 8 * min(static_cast<int>(threadIdx.x) + kThreads * q, hch - 1));
+    for (int q = 0; q < kDownStage; ++q) {
+      const int ch = min(static_cast<int>(threadIdx.x) + kThreads * q, hch - 1);
+      hreg[q] = *reinterpret_cast<const u32x4*>(hin + 8 * ch);
+      hx[q] = *chunk_exp(ch);
+    }
   }
   // the exponents of the pairs' h~ tiles (16 per vector), read by every
   // wave: each wave derives every token's largest exponent E_t itself
@@ -744,7 +750,8 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   }
 
   // E_t: the largest exponent over the token's pairs and row tiles (pairs
-  // without a row carry kZeroExp, which never wins)
+  // without a row carry kZeroExp, which never wins); every wave derives it,
+  // wave 0 publishes it in LDS (indexed by a per-lane token later)
   int et[kMaxT];
   {
     int lm[kMaxT];
@@ -764,6 +771,10 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
 #pragma unroll
     for (int t = 0; t < kMaxT; ++t)
       et[t] = t < T ? static_cast<int>(__ockl_wfred_max_u32(static_cast<uint32_t>(lm[t] + 256))) - 256 : 0;
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int t = 0; t < kMaxT; ++t) s_et[t] = et[t];
+    }
   }
   __syncthreads();
   const int nitems = s_n * KTd;
@@ -772,30 +783,28 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   load_down<kDownBatch>(L, s_expert, nitems, KTd, rt, 0, lane, D);
   if constexpr (STAGED) {
     // h~ into LDS, each 8-value chunk (one pair, half of a 16-row tile of I)
-    // rescaled from its tile's exponent to its token's E_t
-    const int cpp = I / 8;                                        // chunks per pair
-    auto put = [&](int ch, const u32x4& raw) {
-      const int p = ch / cpp;
-      const int t = pair_token(p, T, k);
-      int e_t = et[0];
-#pragma unroll
-      for (int q = 1; q < kMaxT; ++q) e_t = (q == t) ? et[q] : e_t;
-      const int d = static_cast<int>(hexp[static_cast<size_t>(p) * RTI + (ch % cpp) / 2]) - e_t;
-      *reinterpret_cast<f16x8*>(hs + 8 * ch) = scale_pow2(__builtin_bit_cast(f16x8, raw), min(d, 0));
+    // rescaled from its tile's exponent (ex) to its token's E_t
+    auto put = [&](int ch, const u32x4& raw, int ex) {
+      const int e_t = s_et[pair_token(ch / cpp, T, k)];
+      *reinterpret_cast<f16x8*>(hs + 8 * ch) = scale_pow2(__builtin_bit_cast(f16x8, raw), min(ex - e_t, 0));
     };
 #pragma unroll
     for (int q = 0; q < kDownStage; ++q) {
       const int ch = threadIdx.x + kThreads * q;
-      if (ch < hch) put(ch, hreg[q]);
+      if (ch < hch) put(ch, hreg[q], hx[q]);
     }
     for (int ch0 = threadIdx.x + kThreads * kDownStage; ch0 < hch; ch0 += 4 * kThreads) {
       u32x4 r[4];
+      int ex[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ch = min(ch0 + kThreads * u, hch - 1);
+        r[u] = *reinterpret_cast<const u32x4*>(hin + 8 * ch);
+        ex[u] = *chunk_exp(ch);
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        r[u] = *reinterpret_cast<const u32x4*>(hin + 8 * min(ch0 + kThreads * u, hch - 1));
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (ch0 + kThreads * u < hch) put(ch0 + kThreads * u, r[u]);
+        if (ch0 + kThreads * u < hch) put(ch0 + kThreads * u, r[u], ex[u]);
     }
   }
   __syncthreads();
@@ -803,12 +812,12 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int per_wave = (nitems + kWaves - 1) / kWaves;
   const _Float16* hsrc = STAGED ? hs : hin;
-  mma_down<kDownBatch, STAGED>(D, nitems, KTd, 0, lane, hsrc, s_pidx, T, I, hexp, et, acc);
+  mma_down<kDownBatch, STAGED>(D, nitems, KTd, 0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
   for (int j0 = kDownBatch; j0 < per_wave; j0 += kDownBatch) {
     load_down<kDownBatch>(L, s_expert, nitems, KTd, rt, j0, lane, D);
-    mma_down<kDownBatch, STAGED>(D, nitems, KTd, j0, lane, hsrc, s_pidx, T, I, hexp, et, acc);
+    mma_down<kDownBatch, STAGED>(D, nitems, KTd, j0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
   }
-  down_store(acc, s_red, rt, T, L.H, et, residual, out, out_bf16);
+  down_store(acc, s_red, rt, T, L.H, s_et, residual, out, out_bf16);
 }
 
 // -------------------------------------------------------------- launching --

@@ -27,7 +27,9 @@
 //   down     work item x 256-row block of H, 8 waves x 2 row tiles: A = h
 //            rows rescaled to one exponent per row (the row's largest) while
 //            they are moved into LDS, B = down tiles; y = acc * 2^E_row, stored
-//            as fp16 y * 2^-F with one exponent F per (row, 32 columns).
+//            as fp16 y * 2^-F with one exponent F per (row, 8 columns): each
+//            wave turns its accumulators around through LDS so that a lane
+//            holds 8 consecutive columns of one row.
 //   combine  token t: out = sum_j y~[pair_pos[t,j]] * 2^F + y~[shared row]
 //            * 2^F (+ residual), j ascending: fixed order, no atomics.
 // Workgroup ids are remapped so that every XCD gets an equal share of the
@@ -66,9 +68,9 @@ struct PrefillWs {
   _Float16* h;         // [rows][I]     h * 2^-hexp
   _Float16* y;         // [rows][H]     y * 2^-yexp
   int8_t* hexp;        // [rows][I/16]  exponent of each 16-row tile of I
-  int8_t* yexp;        // [rows][H/32]  exponent of each 32 columns of H
+  int8_t* yexp;        // [rows][H/8]   exponent of each 8 columns of H
 };
-constexpr int kYGroup = 16 * kDownRTW;       // columns of y per exponent (one wave's row tiles)
+constexpr int kYGroup = 8;                   // columns of y per exponent (one 16-byte chunk)
 
 __host__ __device__ inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
@@ -374,7 +376,7 @@ struct ATile {
       r[SET][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], k0, 0);
   }
   template <int SET>
-  __device__ __forceinline__ void store(_Float16* buf) const {
+  __device__ __forceinline__ void store(_Float16* buf, int /*kt*/) const {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NR; ++i)
@@ -389,57 +391,52 @@ __device__ __forceinline__ f16x8 a_frag(const _Float16* buf, int j, int mt, int 
 // A tile staging of the down GEMM: the item's h rows, laid out as ATile,
 // but each fragment (8 values of one row inside one 16-row tile of I) is
 // rescaled from its tile's exponent to the row's exponent E_row on its way
-// into LDS, so every MFMA row shares one scale.  The tile exponents come
-// through a byte buffer resource over the item's hexp rows, loaded with the
-// fragment they belong to.
+// into LDS, so every MFMA row shares one scale.  The exponents come from the
+// item's table in LDS, tile-major (s_hx[tile * 64 + row]), so that each
+// lane's lookups are one base address plus compile-time offsets; s_erow
+// holds E_row.  Rows at or beyond nrows hold stale exponents: their MFMA
+// rows are never stored.
 template <int NMT>
 struct HTile {
   static constexpr int NR = NMT;
-  __amdgpu_buffer_rsrc_t rs, re;
-  uint32_t off[NR], eoff[NR];
-  int slot[NR];
-  int er[NR];        // E_row of each fragment's row
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t off0;     // byte offset of this lane's fragment in row m; row i*16 + m adds i*16 rows
+  uint32_t row_bytes;
+  int last;          // the last row: rows at or beyond nrows repeat it
   u32x4 r[2][NR];
-  int ex[2][NR];     // tile exponent of each fragment, per register set
-  __device__ __forceinline__ int row_of(int i) const {
-    const int lane = threadIdx.x & 63;
-    return i * 16 + (lane & 15);
-  }
-  __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t hrsrc, __amdgpu_buffer_rsrc_t ersrc,
-                                       uint32_t row_bytes, int RTI, int nrows) {
+  const int8_t* s_hx;
+  const int* s_erow;
+  __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t hrsrc, uint32_t row_bytes_, int nrows,
+                                       const int8_t* hx, const int* erow) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int j = w & 7, m = lane & 15, g = lane >> 4;
     rs = hrsrc;
-    re = ersrc;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int row = min(i * 16 + m, nrows - 1);
-      slot[i] = 4 * j + i;
-      off[i] = static_cast<uint32_t>(row) * row_bytes + 2u * static_cast<uint32_t>(32 * j + 8 * g);
-      eoff[i] = static_cast<uint32_t>(row * RTI + 2 * j + (g >> 1));
-    }
+    row_bytes = row_bytes_;
+    last = nrows - 1;
+    off0 = 2u * static_cast<uint32_t>(32 * j + 8 * g);
+    s_hx = hx + (2 * j + (g >> 1)) * kGroupRows + m;     // tile 2j + g/2 of K tile 0, row m
+    s_erow = erow + m;
   }
   template <int SET>
   __device__ __forceinline__ void load(int kt) {
+    const int m = threadIdx.x & 15;
     const uint32_t k0 = static_cast<uint32_t>(kt) * (2 * kTileCols);
-    const uint32_t e0 = static_cast<uint32_t>(kt) * (kTileCols / kTileRows);
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      r[SET][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], k0, 0);
-      ex[SET][i] = static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(re, eoff[i], e0, 0));
-    }
-  }
-  __device__ __forceinline__ void set_row_exponents(const int* s_erow, int nrows) {
-#pragma unroll
-    for (int i = 0; i < NR; ++i) er[i] = s_erow[min(row_of(i), nrows - 1)];
-  }
-  template <int SET>
-  __device__ __forceinline__ void store(_Float16* buf) const {
-    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NR; ++i)
-      *reinterpret_cast<f16x8*>(buf + (slot[i] * 64 + lane) * 8) =
-          scale_pow2(__builtin_bit_cast(f16x8, r[SET][i]), min(ex[SET][i] - er[i], 0));
+      r[SET][i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rs, static_cast<uint32_t>(min(i * 16 + m, last)) * row_bytes + off0, k0, 0);
+  }
+  template <int SET>
+  __device__ __forceinline__ void store(_Float16* buf, int kt) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int j = w & 7;
+    const int8_t* hx = s_hx + kt * (kTileCols / kTileRows) * kGroupRows;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int d = static_cast<int>(hx[i * 16]) - s_erow[i * 16];
+      *reinterpret_cast<f16x8*>(buf + ((4 * j + i) * 64 + lane) * 8) =
+          scale_pow2(__builtin_bit_cast(f16x8, r[SET][i]), min(d, 0));
+    }
   }
 };
 
@@ -483,7 +480,7 @@ __device__ __forceinline__ void k_loop(int KT, u32x4 (&b)[RING][NB], LoadB load_
     mul(bs, s_a[P]);
     __builtin_amdgcn_sched_barrier(0);
     if (refill) load_b(bs, kt + RING);
-    A.template store<P ^ 1>(s_a[P ^ 1]);
+    A.template store<P ^ 1>(s_a[P ^ 1], min(kt + 1, KT - 1));
     __syncthreads();
   };
   using P0 = std::integral_constant<int, 0>;
@@ -527,7 +524,7 @@ __device__ __forceinline__ void k_loop_fixed(u32x4 (&b)[RING][NB], LoadB load_b,
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kt + RING < KTC) load_b(b[kt % RING], kt + RING);
     if constexpr (kt + 1 < KTC) {
-      A.template store<P ^ 1>(s_a[P ^ 1]);
+      A.template store<P ^ 1>(s_a[P ^ 1], kt + 1);
       __syncthreads();
     }
   };
@@ -564,7 +561,7 @@ __device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs&
          [&](int i) { return s_off[i]; }, nrows);
   A.template load<0>(0);
   A.template load<1>(min(1, KT - 1));
-  A.template store<0>(s_a[0]);
+  A.template store<0>(s_a[0], 0);
   __syncthreads();
 
   f32x4 acc_g[4], acc_u[4];
@@ -631,19 +628,22 @@ __global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, P
 }
 
 // --------------------------------------------------------------------- down --
+// Per block: both row tiles' weights dequantized first, then one activation
+// fragment at a time (fewer live registers than holding every M tile's
+// fragment).
 template <int NMT>
 __device__ __forceinline__ void down_ktile(const u32x4 (&b)[2 * kDownRTW], const _Float16* abuf, int lane,
                                            f32x4 (&acc)[kDownRTW][4]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    f16x8 a[NMT];
+    f16x8 bq[kDownRTW];
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) a[mt] = a_frag(abuf, j, mt, lane);
+    for (int q = 0; q < kDownRTW; ++q) bq[q] = tile_block_weights(b[2 * q], b[2 * q + 1], j);
 #pragma unroll
-    for (int q = 0; q < kDownRTW; ++q) {
-      const f16x8 bq = tile_block_weights(b[2 * q], b[2 * q + 1], j);
+    for (int mt = 0; mt < NMT; ++mt) {
+      const f16x8 a = a_frag(abuf, j, mt, lane);
 #pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) acc[q][mt] = mfma16(a[mt], bq, acc[q][mt]);
+      for (int q = 0; q < kDownRTW; ++q) acc[q][mt] = mfma16(a, bq[q], acc[q][mt]);
     }
   }
 }
@@ -651,7 +651,7 @@ __device__ __forceinline__ void down_ktile(const u32x4 (&b)[2 * kDownRTW], const
 template <int NMT, int RING, int KTC>
 __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& ws, int e, int row0,
                                           int nrows, int rt0, _Float16 (*s_a)[kATileHalves],
-                                          int* s_erow) {
+                                          int* s_erow, int8_t* s_hx) {
   const int H = L.H, I = L.I;
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
@@ -670,34 +670,47 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
       b[2 * q + 1] = load_scales(rs, o + q * KT * kTileBytes, lane);
     }
   };
+  // the item's tile exponents are requested first: they are waited for
+  // first, and loads complete in issue order (RTI / 16 = KT vectors per row)
+  constexpr int kEPre = 4;
+  const u32x4* ev_src = reinterpret_cast<const u32x4*>(
+      ws.hexp + static_cast<size_t>(row0 + min(static_cast<int>(threadIdx.x), nrows - 1)) * RTI);
+  u32x4 ev[kEPre];
+#pragma unroll
+  for (int q = 0; q < kEPre; ++q) ev[q] = ev_src[min(q, KT - 1)];
   u32x4 b[RING][NB];
 #pragma unroll
   for (int u = 0; u < RING; ++u) load_b(b[u], u);
-  HTile<NMT> A;   // the item's h rows and their exponents are consecutive: resources over just them
+  HTile<NMT> A;   // the item's h rows are consecutive: a resource over just them
   const uint32_t row_bytes = static_cast<uint32_t>(I) * 2u;
-  const int8_t* erows = ws.hexp + static_cast<size_t>(row0) * RTI;
   A.init(expert_rsrc(reinterpret_cast<const uint8_t*>(ws.h + static_cast<size_t>(row0) * I),
                      static_cast<uint32_t>(nrows) * row_bytes),
-         expert_rsrc(reinterpret_cast<const uint8_t*>(erows), static_cast<uint32_t>(nrows * RTI)),
-         row_bytes, RTI, nrows);
+         row_bytes, nrows, s_hx, s_erow);
   A.template load<0>(0);
   A.template load<1>(min(1, KT - 1));
-  // E_row: the largest tile exponent of each row (RTI is a multiple of 16)
+  // the item's tile exponents into LDS, tile-major (its rows are consecutive
+  // in hexp, RTI a multiple of 16), and E_row, the largest exponent of each row
   if (static_cast<int>(threadIdx.x) < nrows) {
-    const u32x4* v = reinterpret_cast<const u32x4*>(erows + static_cast<size_t>(threadIdx.x) * RTI);
+    const int row = threadIdx.x;
     int mx = kZeroExp;
-    for (int q = 0; q < RTI / 16; ++q) {
-      const u32x4 w = v[q];
+    auto take = [&](int q, const u32x4& wv) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) mx = max(mx, static_cast<int>(static_cast<int8_t>(w[c] >> (8 * s))));
-    }
-    s_erow[threadIdx.x] = mx;
+        for (int s = 0; s < 4; ++s) {
+          const int ex = static_cast<int8_t>(wv[c] >> (8 * s));
+          s_hx[(16 * q + 4 * c + s) * kGroupRows + row] = static_cast<int8_t>(ex);
+          mx = max(mx, ex);
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < kEPre; ++q)
+      if (q < KT) take(q, ev[q]);
+    for (int q = kEPre; q < KT; ++q) take(q, ev_src[q]);
+    s_erow[row] = mx;
   }
   __syncthreads();
-  A.set_row_exponents(s_erow, nrows);
-  A.template store<0>(s_a[0]);
+  A.template store<0>(s_a[0], 0);
   __syncthreads();
 
   f32x4 acc[kDownRTW][4];
@@ -714,30 +727,48 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
   else
     k_loop<RING>(KT, b, load_b, A, s_a, mul);
 
-  // y = acc * 2^E_row; one exponent per (row, this wave's 32 columns)
-  const int yg = rt0 / kDownRTW;
+  // y = acc * 2^E_row, one exponent per (row, 8 columns).  The wave's
+  // accumulators (its rows x 32 columns, fp32) go through its own 8 KB of
+  // the A tile buffer (free after the K loop) so that a lane then holds 8
+  // consecutive columns of one row: the block maximum needs no cross-lane
+  // step and the store is one 16-byte write.  Rows are 32 floats; the 8-float
+  // chunks of row r sit at chunk ^ ((r >> 2) & 3), which spreads the four
+  // lane groups of an accumulator write over all 32 chunk positions.
+  static_assert(kDownRTW == 2 && 8 * kGroupRows * 32 * 4 == sizeof(_Float16) * 2 * kATileHalves,
+                "one wave's rows x 32 fp32 columns fill an eighth of the A tile buffer");
+  __syncthreads();                                   // every wave is done with the A tiles
+  float* tb = reinterpret_cast<float*>(&s_a[0][0]) + (threadIdx.x >> 6) * (kGroupRows * 32);
+  auto at = [](int row, int col) { return row * 32 + ((((col >> 3) ^ (row >> 2)) & 3) << 3) + (col & 7); };
+#pragma unroll
+  for (int q = 0; q < kDownRTW; ++q)
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tb[at(mt * 16 + 4 * g + r, q * 16 + m)] = acc[q][mt][r];
+  __builtin_amdgcn_wave_barrier();
   const int NYG = H / kYGroup;
 #pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rl = mt * 16 + 4 * g + r;            // uniform in each 16-lane row
-      const bool ok = rl < nrows;
-      const int erw = ok ? s_erow[rl] : 0;
-      float yv[kDownRTW];
+  for (int it = 0; it < NMT; ++it) {                 // 16 rows x 4 chunks per step
+    const int rl = it * 16 + (lane >> 2), ch = lane & 3;
+    if (rl < nrows) {
+      const f32x4* src4 = reinterpret_cast<const f32x4*>(tb + at(rl, 8 * ch));
+      const f32x4 lo = src4[0], hi = src4[1];
       float mx = 0.0f;
 #pragma unroll
-      for (int q = 0; q < kDownRTW; ++q) {
-        yv[q] = ok ? ldexpf(acc[q][mt][r], erw) : 0.0f;
-        mx = fmaxf(mx, fabsf(yv[q]));
-      }
-      const int f = block_exponent(row16_max(mx));
-      if (ok) {
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(fabsf(lo[i]), fabsf(hi[i])));
+      // y = acc * 2^E_row = y~ * 2^F, F = exponent of the chunk's largest |y|
+      const int er = s_erow[rl];
+      const int f = block_exponent(mx);
+      const int F = f == kZeroExp ? kZeroExp : max(-126, min(127, f + er));
+      f16x8 o;
 #pragma unroll
-        for (int q = 0; q < kDownRTW; ++q)
-          ws.y[static_cast<size_t>(row0 + rl) * H + (rt0 + q) * 16 + m] = static_cast<_Float16>(ldexpf(yv[q], -f));
-        if (m == 0) ws.yexp[static_cast<size_t>(row0 + rl) * NYG + yg] = static_cast<int8_t>(f);
+      for (int i = 0; i < 4; ++i) {
+        o[i] = static_cast<_Float16>(ldexpf(lo[i], er - F));
+        o[4 + i] = static_cast<_Float16>(ldexpf(hi[i], er - F));
       }
+      const int col = rt0 * 16 + ch * 8;
+      *reinterpret_cast<f16x8*>(ws.y + static_cast<size_t>(row0 + rl) * H + col) = o;
+      ws.yexp[static_cast<size_t>(row0 + rl) * NYG + col / kYGroup] = static_cast<int8_t>(F);
     }
   }
 }
@@ -746,6 +777,7 @@ template <int KTC>   // I / 256 when fixed at compile time, else 0
 __global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, PrefillWs ws) {
   __shared__ __align__(16) _Float16 s_a[2][kATileHalves];
   __shared__ int s_erow[kGroupRows];
+  extern __shared__ __align__(16) int8_t s_hx[];     // [kGroupRows][I/16] tile exponents
   const int RB = L.H / kDownRowsPerBlock;
   const int2 wu = work_unit(blockIdx.x, ws.hdr, RB);
   if (wu.x < 0) return;
@@ -755,10 +787,10 @@ __global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, Pre
   const int e = it.x, row0 = it.y, nrows = it.z;
   const int rt0 = (rb * kGemmWaves + static_cast<int>(threadIdx.x >> 6)) * kDownRTW;
   switch ((nrows + 15) / 16) {
-    case 1: down_body<1, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow); break;
-    case 2: down_body<2, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow); break;
-    case 3: down_body<3, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow); break;
-    default: down_body<4, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow); break;
+    case 1: down_body<1, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow, s_hx); break;
+    case 2: down_body<2, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow, s_hx); break;
+    case 3: down_body<3, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow, s_hx); break;
+    default: down_body<4, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow, s_hx); break;
   }
 }
 
@@ -777,7 +809,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(
   const int c = static_cast<int>(g - static_cast<long long>(t) * nch);
   const int P = T * k;
   const int NYG = H / kYGroup;
-  const int yg = c / (kYGroup / 8);
+  const int yg = c;                                   // one exponent per 8-column chunk
   int pos[MOE_MAX_TOPK + 1];
 #pragma unroll
   for (int j = 0; j < MOE_MAX_TOPK; ++j)
@@ -890,12 +922,13 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
     const long long nb = (static_cast<long long>(grid_items) + 7) / 8 * 8 * (L.H / kDownRowsPerBlock);
     const int grid = static_cast<int>(nb);
     const dim3 g(grid), b(kThreads);
+    const uint32_t lds = static_cast<uint32_t>(kGroupRows * (L.I / kTileRows));   // tile-exponent table
     switch (L.I / kTileCols) {
-      case 1: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<1>, g, b, 0, s, L, ws); break;
-      case 2: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<2>, g, b, 0, s, L, ws); break;
-      case 3: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<3>, g, b, 0, s, L, ws); break;
-      case 4: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<4>, g, b, 0, s, L, ws); break;
-      default: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<0>, g, b, 0, s, L, ws); break;
+      case 1: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<1>, g, b, lds, s, L, ws); break;
+      case 2: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<2>, g, b, lds, s, L, ws); break;
+      case 3: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<3>, g, b, lds, s, L, ws); break;
+      case 4: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<4>, g, b, lds, s, L, ws); break;
+      default: e = launch_kernel(K_PREFILL_DOWN, prefill_down_kernel<0>, g, b, lds, s, L, ws); break;
     }
   }
   if (e != hipSuccess) return e;

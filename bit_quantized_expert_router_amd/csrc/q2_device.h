@@ -144,11 +144,30 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
+// fp16 bits of 2^d in both halves of a word, d <= 0: a normal number for
+// d >= -14, a subnormal for -24 <= d < -14, zero below.  Built with integer
+// operations so that the multiply takes it as an ordinary register operand
+// (a half-word broadcast through the packed instruction's operand-select
+// bits gave wrong products on gfx950 in a direct comparison).
+__device__ __forceinline__ uint32_t pow2_f16x2_bits(int d) {
+  const uint32_t b = d >= -14 ? static_cast<uint32_t>(d + 15) << 10
+                              : (d >= -24 ? 1u << (d + 24) : 0u);
+  return b | (b << 16);
+}
+
 // 8 fp16 values times 2^d for d <= 0 (exact unless the result is subnormal;
 // below 2^-24 of the input the values become zero).
 __device__ __forceinline__ f16x8 scale_pow2(const f16x8& a, int d) {
-  const _Float16 s = d < -24 ? static_cast<_Float16>(0.0f) : static_cast<_Float16>(ldexpf(1.0f, d));
-  return a * s;
+  const f16x2 s = __builtin_bit_cast(f16x2, pow2_f16x2_bits(d));
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 v = {a[2 * i], a[2 * i + 1]};
+    const f16x2 p = v * s;
+    r[2 * i] = p[0];
+    r[2 * i + 1] = p[1];
+  }
+  return r;
 }
 
 __device__ __forceinline__ float bf16_to_float(uint16_t b) {

@@ -160,9 +160,12 @@ int moe_route_topk_gemv(const void* x, int32_t x_dtype, int32_t T, const uint16_
  *   layer     [host] weights descriptor (above).
  *   x         [device] [T, H] activations, x_dtype MOE_F32 or MOE_BF16;
  *             16-byte aligned (as are out and residual).
- *   topk_ids, topk_w  [device] [T, k] as produced by moe_route_topk.
- *   residual  [device] [T, H] in out_dtype, or NULL; may alias `out`.
- *   out       [device] [T, H] in out_dtype; must not alias x:
+ *   topk_ids, topk_w  [device] [T, k] as produced by moe_route_topk.  A
+ *             token may list an expert more than once (its weights then add
+ *             up); an id outside [0, E) contributes nothing.
+ *   residual  [device] [T, H] in out_dtype, or NULL; either `out` itself
+ *             (updated in place) or not overlapping it.
+ *   out       [device] [T, H] in out_dtype; must not overlap x:
  *             out[t] = sum_j topk_w[t,j] * FFN_{topk_ids[t,j]}(x_hat_t)
  *                      + FFN_shared(x_hat_t) (+ residual[t]),
  *             FFN(x) = W_down (silu(W_gate x) * (W_up x)).
