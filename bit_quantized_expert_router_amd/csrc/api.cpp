@@ -269,9 +269,10 @@ int moe_route_topk_gemv(const void* x, int32_t x_dtype, int32_t T, const uint16_
   return e == hipSuccess ? MOE_OK : hip_fail(e, "route_gemv_topk launch");
 }
 
-static int check_forward(const moe_q2_layer* layer, const void* x, int32_t x_dtype, int32_t T,
-                         const int32_t* ids, const float* w, int32_t k, const void* residual, const void* out,
-                         int32_t out_dtype, uint32_t flags, void* workspace) {
+// Every argument of a forward call except the workspace.
+static int check_forward_args(const moe_q2_layer* layer, const void* x, int32_t x_dtype, int32_t T,
+                              const int32_t* ids, const float* w, int32_t k, const void* residual,
+                              const void* out, int32_t out_dtype, uint32_t flags) {
   int st = check_layer(layer, k);
   if (st) return st;
   if (!x || !ids || !w || !out) return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, topk_w and out are required");
@@ -287,12 +288,51 @@ static int check_forward(const moe_q2_layer* layer, const void* x, int32_t x_dty
     if (residual && residual != out && overlaps(residual, ob, out, ob))
       return fail(MOE_ERR_INVALID_ARG, "residual must be out itself or not overlap it");
   }
-  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is required");
-  if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(residual, 16) || !aligned(ids, 4) || !aligned(w, 4))
     return fail(MOE_ERR_INVALID_ARG,
                 "x, out and residual must be 16-byte aligned, topk_ids and topk_w 4-byte aligned");
   return MOE_OK;
+}
+
+static int check_workspace(void* workspace) {
+  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is required");
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return MOE_OK;
+}
+
+static int check_forward(const moe_q2_layer* layer, const void* x, int32_t x_dtype, int32_t T,
+                         const int32_t* ids, const float* w, int32_t k, const void* residual, const void* out,
+                         int32_t out_dtype, uint32_t flags, void* workspace) {
+  int st = check_forward_args(layer, x, x_dtype, T, ids, w, k, residual, out, out_dtype, flags);
+  return st ? st : check_workspace(workspace);
+}
+
+// The arguments of the routed decode call except the workspace.
+static int check_routed_args(const moe_q2_layer* layer, const void* x, int32_t x_dtype, int32_t T,
+                             const float* logits, int32_t k, const int32_t* topk_ids, const float* topk_w,
+                             const void* residual, const void* out, int32_t out_dtype, uint32_t flags) {
+  if (!logits) return fail(MOE_ERR_INVALID_ARG, "logits is required");
+  if ((topk_ids == nullptr) != (topk_w == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "topk_ids and topk_w: both or neither");
+  if (!aligned(logits, 4) || (topk_ids && (!aligned(topk_ids, 4) || !aligned(topk_w, 4))))
+    return fail(MOE_ERR_INVALID_ARG, "logits, topk_ids and topk_w must be 4-byte aligned");
+  // the routing outputs are optional here, so check the rest with stand-ins
+  int st = check_forward_args(layer, x, x_dtype, T, reinterpret_cast<const int32_t*>(logits), logits, k,
+                              residual, out, out_dtype, flags);
+  if (st) return st;
+  if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "decode takes at most 8 tokens");
+  return MOE_OK;
+}
+
+static int launch_routed(const moe_q2_layer* layer, const void* x, int32_t x_dtype, int32_t T,
+                         const float* logits, int32_t k, int32_t* topk_ids, float* topk_w,
+                         const void* residual, void* out, int32_t out_dtype, uint32_t flags,
+                         void* workspace, void* stream) {
+  const hipError_t e = launch_decode(layer_args(layer), x, x_dtype == MOE_BF16, T, nullptr, nullptr,
+                                     logits, topk_ids, topk_w, k, residual, out,
+                                     out_dtype == MOE_BF16, (flags & MOE_FLAG_PRENORM_RMS) ? 1 : 0,
+                                     workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "decode launch");
 }
 
 int moe_expert_forward_decode(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
@@ -316,23 +356,29 @@ int moe_expert_forward_decode_routed(const moe_q2_layer* layer, const void* x, i
                                      float* topk_w, const void* residual, void* out,
                                      int32_t out_dtype, uint32_t flags, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-  if (!logits) return fail(MOE_ERR_INVALID_ARG, "logits is required");
-  if ((topk_ids == nullptr) != (topk_w == nullptr))
-    return fail(MOE_ERR_INVALID_ARG, "topk_ids and topk_w: both or neither");
-  if (!aligned(logits, 4) || (topk_ids && (!aligned(topk_ids, 4) || !aligned(topk_w, 4))))
-    return fail(MOE_ERR_INVALID_ARG, "logits, topk_ids and topk_w must be 4-byte aligned");
-  // the routing outputs are optional here, so check the rest with stand-ins
-  int st = check_forward(layer, x, x_dtype, T, reinterpret_cast<const int32_t*>(logits), logits, k,
-                         residual, out, out_dtype, flags, workspace);
-  if (st) return st;
-  if (T > MOE_MAX_DECODE_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "decode takes at most 8 tokens");
+  int st = check_routed_args(layer, x, x_dtype, T, logits, k, topk_ids, topk_w, residual, out, out_dtype, flags);
+  if (st || (st = check_workspace(workspace))) return st;
   const size_t need = decode_workspace_bytes(T, k, layer->hidden, layer->inter);
   if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
-  const hipError_t e = launch_decode(layer_args(layer), x, x_dtype == MOE_BF16, T, nullptr, nullptr,
-                                     logits, topk_ids, topk_w, k, residual, out,
-                                     out_dtype == MOE_BF16, (flags & MOE_FLAG_PRENORM_RMS) ? 1 : 0,
-                                     workspace, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "decode launch");
+  return launch_routed(layer, x, x_dtype, T, logits, k, topk_ids, topk_w, residual, out, out_dtype, flags,
+                       workspace, stream);
+}
+
+int moe_expert_forward_decode_routed_noalloc(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
+                                             int32_t T, const float* logits, int32_t k,
+                                             int32_t* topk_ids, float* topk_w, const void* residual,
+                                             void* out, int32_t out_dtype, uint32_t flags, void* stream) {
+  int st = check_routed_args(layer, x, x_dtype, T, logits, k, topk_ids, topk_w, residual, out, out_dtype, flags);
+  if (st) return st;
+  const size_t need = decode_workspace_bytes(T, k, layer->hidden, layer->inter);
+  if (need > decode_static_scratch_bytes())
+    return fail(MOE_ERR_UNSUPPORTED, "the call needs %lld bytes of scratch, the static scratch holds %lld",
+                (long long)need, (long long)decode_static_scratch_bytes());
+  void* scratch = nullptr;
+  const hipError_t e = decode_static_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "static decode scratch");
+  return launch_routed(layer, x, x_dtype, T, logits, k, topk_ids, topk_w, residual, out, out_dtype, flags,
+                       scratch, stream);
 }
 
 int moe_expert_forward_prefill(const moe_q2_layer* layer, const void* x, int32_t x_dtype,

@@ -939,4 +939,38 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
                        0u, s, L, T, k, residual, out, out_bf16, static_cast<const uint8_t*>(ws));
 }
 
+// ------------------------------------------------ scratch without allocation --
+// The decode workspace for callers that cannot allocate: one file-scope
+// device array per GPU, sized for the largest decode call the library
+// accepts (T = 8, k = 16, I = 8192).  In host code `scratch` only names the
+// symbol; its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device and kept.
+constexpr size_t kStaticScratchBytes =
+    kHeaderBytes + (static_cast<size_t>(MOE_MAX_DECODE_TOKENS) * (MOE_MAX_TOPK + 1) * MOE_MAX_DIM * 2 + 255) / 256 * 256 +
+    (static_cast<size_t>(MOE_MAX_DECODE_TOKENS) * (MOE_MAX_TOPK + 1) * (MOE_MAX_DIM / kTileRows) + 255) / 256 * 256;
+static_assert(kStaticScratchBytes == MOE_DECODE_STATIC_SCRATCH_BYTES, "static scratch size");
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+size_t decode_static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t decode_static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with device `dev` current
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace moeq2

@@ -92,6 +92,10 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
                          int32_t* ids_out, float* w_out, int k, const void* residual,
                          void* out, int out_bf16, int prenorm, void* ws, hipStream_t s);
 size_t decode_workspace_bytes(int T, int k, int H, int I);
+// The device address of this GPU's static decode scratch (resolved once per
+// device, with that device current) and its size.
+hipError_t decode_static_scratch(void** ptr);
+size_t decode_static_scratch_bytes();
 
 // ---------------------------------------------------------------- prefill --
 constexpr int kGroupRows = 64;          // rows (token-expert pairs) per work item

@@ -202,6 +202,29 @@ int moe_expert_forward_decode_routed(const moe_q2_layer* layer, const void* x, i
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_expert_forward_decode_routed without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The workspace is a
+ * static device array inside the library, one per GPU, of
+ * MOE_DECODE_STATIC_SCRATCH_BYTES (2,306,048 bytes: the largest decode call,
+ * T = 8, k = 16, I = 8192), held from the first call on that GPU until the
+ * process ends.  Its address is resolved on the first call on each device
+ * (hipGetSymbolAddress with that device current); no call allocates or
+ * frees anything.  Nothing in it needs to start at zero.
+ * Every call on one GPU uses the same array: calls that may overlap on one
+ * GPU (other streams, other host threads) race and must be serialised by
+ * the caller, e.g. all on one stream.
+ * Arguments, results and errors: as moe_expert_forward_decode_routed, plus
+ * UNSUPPORTED if a call would need more scratch than the array holds, and
+ * HIP if the array's address cannot be resolved.
+ */
+#define MOE_DECODE_STATIC_SCRATCH_BYTES 2306048
+int moe_expert_forward_decode_routed_noalloc(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
+                                             int32_t T, const float* logits, int32_t k,
+                                             int32_t* topk_ids, float* topk_w, const void* residual,
+                                             void* out, int32_t out_dtype, uint32_t flags, void* stream);
+
+/*
  * Prefill-time expert layer for a chunk of T tokens, grouped by expert from
  * the routing histogram (prompts are read in chunks and the experts are
  * processed block by block: strata-mlx README, section 它是什么; chunk sizes
