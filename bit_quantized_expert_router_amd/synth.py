@@ -92,7 +92,8 @@ def constant_expert_blob(E: int, H: int, I: int, code: int, scale: float) -> np.
 def device_expert_blob(E: int, H: int, I: int, seed: int, device="cuda",
                        scale_lo: float = 0.01, scale_hi: float = 0.05):
     """Same recipe, generated with torch's RNG straight into device memory
-    (used for the multi-GB stacked workloads).  Returns a uint8 tensor."""
+    (used for the multi-GB stacked workloads), every expert's codes in one
+    draw and every scale in another.  Returns a uint8 tensor."""
     import torch
     stride = expert_stride(H, I)
     nb = expert_nbytes(H, I)
@@ -100,14 +101,13 @@ def device_expert_blob(E: int, H: int, I: int, seed: int, device="cuda",
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     buf = torch.empty(E * stride, dtype=torch.uint8, device=device)
-    view = buf.view(E, stride)[:, :nb].reshape(E, nrec, TILE_BYTES)
-    for e in range(E):
-        v = view[e]
-        v[:, :SCALE_OFFSET] = torch.randint(0, 256, (nrec, SCALE_OFFSET), dtype=torch.uint8,
-                                            device=device, generator=g)
-        sc = (torch.rand((nrec, 128), device=device, generator=g, dtype=torch.float32)
-              * (scale_hi - scale_lo) + scale_lo).to(torch.float16)
-        v[:, SCALE_OFFSET:] = sc.view(torch.uint8)
+    view = buf.view(E, stride)[:, :nb].view(E, nrec, TILE_BYTES)
+    view[:, :, :SCALE_OFFSET] = torch.randint(0, 256, (E, nrec, SCALE_OFFSET), dtype=torch.uint8,
+                                              device=device, generator=g)
+    sc = (torch.rand((E, nrec, 128), device=device, generator=g, dtype=torch.float32)
+          * (scale_hi - scale_lo) + scale_lo).to(torch.float16)
+    view[:, :, SCALE_OFFSET:] = sc.view(torch.uint8)
+    del sc
     if stride > nb:
         buf.view(E, stride)[:, nb:].zero_()
     return buf
