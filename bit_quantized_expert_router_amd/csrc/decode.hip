@@ -39,6 +39,7 @@
 // from the last arrival at 264 workgroups -- more than the gap between two
 // kernels.
 #include <mutex>
+#include <type_traits>
 
 #include "launch.h"
 #include "q2_device.h"
@@ -579,16 +580,65 @@ __device__ __forceinline__ int max_i8x16(const u32x4& v) {
 
 // ------------------------------------------------------------ the kernels --
 
+// A block of the shared expert's row tiles when its groups have blocks of
+// their own (SPLIT launch, one token): the shared expert needs no routing,
+// so the block loads x, issues its weight loads at once, stages x and
+// multiplies, while the routed blocks are still taking the top-k.  Row
+// tiles sb * RTW + group of the shared expert (its pairs T*k + t, weight 1).
+template <int KTW, bool BF16, int RTW>
+__device__ void shared_gateup(const LayerArgs& L, const void* __restrict__ x, int T, int k, int prenorm,
+                              uint8_t* __restrict__ ws, int sb, _Float16* xs, DecodeSlots& S,
+                              float (*s_stat)[kMaxT][2], f32x4 (*s_red)[2][32], float* s_smul) {
+  constexpr int NT = 256 * RTW, NW = 4 * RTW, XC = x_reg_chunks<NT>();
+  const int H = L.H, I = L.I;
+  const int RTI = I / kTileRows;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = wave_id();
+  const int kq = wid & 3;
+  const int rtu = sb * RTW + (wid >> 2);
+  const bool active = rtu < RTI;
+  const int rt = active ? rtu : 0;
+  const int nch = T * H / 8;
+  const bool xreg = nch <= NT * XC;
+  u32x4 xr[XC][2];
+  issue_x<BF16, XC>(x, nch, xreg, xr, threadIdx.x, NT);
+  GateUpTiles<KTW> R;
+  load_gateup<KTW>(L.shared, active, H, I, rt, kq, lane, R);
+  token_partials<BF16, XC>(x, T, H, xreg, xr, s_stat, threadIdx.x, NT);
+  if (threadIdx.x < kMaxT) {
+    const int t = threadIdx.x;
+    S.pidx[k][t] = t < T ? T * k + t : -1;
+    if (t < T) S.wpair[T * k + t] = 1.0f;
+  }
+  __syncthreads();
+  {
+    float rmul[kMaxT], smul[kMaxT];
+    token_derive<NW>(T, H, prenorm, s_stat, rmul, smul);
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int t = 0; t < kMaxT; ++t) s_smul[t] = smul[t];
+    }
+    stage_x<BF16, XC>(x, T, H, xreg, xr, rmul, smul, xs, threadIdx.x, NT);
+  }
+  __syncthreads();
+  int8_t* hexp = reinterpret_cast<int8_t*>(ws + kHeaderBytes + decode_h_bytes(T, k, I));
+  gateup_compute<KTW>(R, xs, T, H, I, rt, kq, k, active, S, s_smul, s_red,
+                      reinterpret_cast<_Float16*>(ws + kHeaderBytes), hexp);
+}
+
 // Kernel 1: RTW groups of 4 waves; group q of block b takes row tile
 // g = b + gridDim.x * q of the flattened (slot, row tile) list, so that one
 // block per CU covers all of them (a second block on a CU would double that
 // CU's share and finish last).  Block 0 also writes the header that kernel 2
 // reads.
-template <int KTW, bool BF16, int RPER, int RTW>
+// SPLIT: blocks [0, n_rwg) take the routed row tiles only (group q of block
+// b: routed row tile b + n_rwg * q) and blocks from n_rwg on the shared
+// expert's (shared_gateup).
+template <int KTW, bool BF16, int RPER, int RTW, bool SPLIT>
 __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
     LayerArgs L, const void* __restrict__ x, int T, const int32_t* __restrict__ ids,
     const float* __restrict__ w, const float* __restrict__ logits, int32_t* __restrict__ ids_out,
-    float* __restrict__ w_out, int k, int prenorm, uint8_t* __restrict__ ws) {
+    float* __restrict__ w_out, int k, int prenorm, uint8_t* __restrict__ ws, int n_rwg) {
   constexpr int NT = 256 * RTW, NW = 4 * RTW, XC = x_reg_chunks<NT>();
   extern __shared__ __align__(16) uint8_t dyn[];
   _Float16* xs = reinterpret_cast<_Float16*>(dyn);              // [T][H]
@@ -600,12 +650,18 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
   __shared__ int s_slot_of[MOE_MAX_EXPERTS];
   __shared__ float s_smul[kMaxT];
 
+  if constexpr (SPLIT) {
+    if (static_cast<int>(blockIdx.x) >= n_rwg) {
+      shared_gateup<KTW, BF16, RTW>(L, x, T, k, prenorm, ws, blockIdx.x - n_rwg, xs, S, s_stat, s_red, s_smul);
+      return;
+    }
+  }
   const int H = L.H, I = L.I;
   const int RTI = I / kTileRows;                 // row tiles of one gate (or up) matrix
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = wave_id();
   const int kq = wid & 3;
-  const int g = blockIdx.x + gridDim.x * (wid >> 2);
+  const int g = blockIdx.x + (SPLIT ? n_rwg : static_cast<int>(gridDim.x)) * (wid >> 2);
 
   // Waves 0..T-1 route (one token each); meanwhile the other waves load x,
   // sum its statistics and, after one barrier, stage its fp16 copy while
@@ -651,7 +707,7 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
     if (wid >= xw0) stage_x<BF16, XC>(x, T, H, xreg, xr, rmul, smul, xs, xt, nxt);
   }
   __syncthreads();
-  const int n_rows = S.n * RTI;
+  const int n_rows = (SPLIT ? S.n - 1 : S.n) * RTI;   // SPLIT: the routed slots only
   if (static_cast<int>(blockIdx.x) >= n_rows && blockIdx.x != 0) return;   // no active group
   const bool active = g < n_rows;
   const int slot = active ? g / RTI : 0;
@@ -687,7 +743,7 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
 // Kernel 2: down row tile blockIdx.x.
 constexpr int kExpPre = 2;               // exponent vectors per lane loaded at kernel entry
 
-template <bool STAGED>
+template <bool STAGED, int DB>
 __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     LayerArgs L, int T, int k, const void* __restrict__ residual, void* __restrict__ out,
     int out_bf16, const uint8_t* __restrict__ ws) {
@@ -779,8 +835,6 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   __syncthreads();
   const int nitems = s_n * KTd;
 
-  DownTiles<kDownBatch> D;
-  load_down<kDownBatch>(L, s_expert, nitems, KTd, rt, 0, lane, D);
   if constexpr (STAGED) {
     // h~ into LDS, each 8-value chunk (one pair, half of a 16-row tile of I)
     // rescaled from its tile's exponent (ex) to its token's E_t
@@ -807,15 +861,19 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
         if (ch0 + kThreads * u < hch) put(ch0 + kThreads * u, r[u], ex[u]);
     }
   }
+  // the weight loads go out after the staging: a wave's instructions wait
+  // behind the issue of its loads once the CU has many in flight
+  DownTiles<DB> D;
+  load_down<DB>(L, s_expert, nitems, KTd, rt, 0, lane, D);
   __syncthreads();
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int per_wave = (nitems + kWaves - 1) / kWaves;
   const _Float16* hsrc = STAGED ? hs : hin;
-  mma_down<kDownBatch, STAGED>(D, nitems, KTd, 0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
-  for (int j0 = kDownBatch; j0 < per_wave; j0 += kDownBatch) {
-    load_down<kDownBatch>(L, s_expert, nitems, KTd, rt, j0, lane, D);
-    mma_down<kDownBatch, STAGED>(D, nitems, KTd, j0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
+  mma_down<DB, STAGED>(D, nitems, KTd, 0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
+  for (int j0 = DB; j0 < per_wave; j0 += DB) {
+    load_down<DB>(L, s_expert, nitems, KTd, rt, j0, lane, D);
+    mma_down<DB, STAGED>(D, nitems, KTd, j0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
   }
   down_store(acc, s_red, rt, T, L.H, s_et, residual, out, out_bf16);
 }
@@ -839,12 +897,12 @@ struct DecodeArgs {
 
 constexpr size_t kHStageLimit = 144 * 1024;  // largest h~ staged in LDS (one block per CU)
 
-template <int KTW, bool BF16, int RPER, int RTW>
+template <int KTW, bool BF16, int RPER, int RTW, bool SPLIT = false>
 hipError_t launch_gateup4(const LayerArgs& L, int grid, uint32_t lds, hipStream_t s,
-                          const DecodeArgs& a) {
-  return launch_kernel(K_DECODE_GATEUP, decode_gateup_kernel<KTW, BF16, RPER, RTW>, dim3(grid),
+                          const DecodeArgs& a, int n_rwg = 0) {
+  return launch_kernel(K_DECODE_GATEUP, decode_gateup_kernel<KTW, BF16, RPER, RTW, SPLIT>, dim3(grid),
                        dim3(256 * RTW), lds, s, L, a.x, a.T, a.ids, a.w, a.logits, a.ids_out,
-                       a.w_out, a.k, a.prenorm, a.ws);
+                       a.w_out, a.k, a.prenorm, a.ws, n_rwg);
 }
 
 // Row-tile groups per block: 2..4 while KTW <= 4 (the 16-wave block then
@@ -861,7 +919,13 @@ hipError_t launch_gateup3(const LayerArgs& L, int grid, int rtw, uint32_t lds, h
 
 template <int KTW>
 hipError_t launch_gateup(const LayerArgs& L, int grid, int rtw, uint32_t lds, int x_bf16, int rper,
-                         hipStream_t s, const DecodeArgs& a) {
+                         hipStream_t s, const DecodeArgs& a, int n_rwg) {
+  if (n_rwg > 0) {   // routed and shared blocks apart (one token, routing inside)
+    if (x_bf16) return rper == 8 ? launch_gateup4<KTW, true, 8, 2, true>(L, grid, lds, s, a, n_rwg)
+                                 : launch_gateup4<KTW, true, 16, 2, true>(L, grid, lds, s, a, n_rwg);
+    return rper == 8 ? launch_gateup4<KTW, false, 8, 2, true>(L, grid, lds, s, a, n_rwg)
+                     : launch_gateup4<KTW, false, 16, 2, true>(L, grid, lds, s, a, n_rwg);
+  }
   if (x_bf16) {
     if (rper == 0) return launch_gateup3<KTW, true, 0>(L, grid, rtw, lds, s, a);
     if (rper == 8) return launch_gateup3<KTW, true, 8>(L, grid, rtw, lds, s, a);
@@ -913,30 +977,53 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
     // blocks of 8 per CU)
     const int rows = slots_max * (L.I / kTileRows);
     const int cus = device_cus();
-    int grid = (rows + 1) / 2, rtw = 2;
-    if (cus > 0 && ktw <= 4 && grid > cus && (rows + cus - 1) / cus <= 3) {
+    int grid = (rows + 1) / 2, rtw = 2, n_rwg = 0;
+    const int rti = L.I / kTileRows;
+    if (rper > 0 && T == 1 && L.shared && cus > 0 && (k * rti + 1) / 2 <= cus) {
+      // one token, routing inside: blocks of two groups, the routed row
+      // tiles on blocks of their own (at most one per CU) and the shared
+      // expert's on further blocks that need no routing
+      n_rwg = (k * rti + 1) / 2;
+      grid = n_rwg + (rti + 1) / 2;
+    } else if (cus > 0 && ktw <= 4 && grid > cus && (rows + cus - 1) / cus <= 3) {
       rtw = (rows + cus - 1) / cus;
       grid = (rows + rtw - 1) / rtw;
     }
     const uint32_t lds = static_cast<uint32_t>(lds_x);
     switch (ktw) {
-      case 1: e = launch_gateup<1>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
-      case 2: e = launch_gateup<2>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
-      case 3: e = launch_gateup<3>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
-      case 4: e = launch_gateup<4>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
-      case 5: e = launch_gateup<5>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
-      case 6: e = launch_gateup<6>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
-      case 7: e = launch_gateup<7>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
-      default: e = launch_gateup<8>(L, grid, rtw, lds, x_bf16, rper, s, a); break;
+      case 1: e = launch_gateup<1>(L, grid, rtw, lds, x_bf16, rper, s, a, n_rwg); break;
+      case 2: e = launch_gateup<2>(L, grid, rtw, lds, x_bf16, rper, s, a, n_rwg); break;
+      case 3: e = launch_gateup<3>(L, grid, rtw, lds, x_bf16, rper, s, a, n_rwg); break;
+      case 4: e = launch_gateup<4>(L, grid, rtw, lds, x_bf16, rper, s, a, n_rwg); break;
+      case 5: e = launch_gateup<5>(L, grid, rtw, lds, x_bf16, rper, s, a, n_rwg); break;
+      case 6: e = launch_gateup<6>(L, grid, rtw, lds, x_bf16, rper, s, a, n_rwg); break;
+      case 7: e = launch_gateup<7>(L, grid, rtw, lds, x_bf16, rper, s, a, n_rwg); break;
+      default: e = launch_gateup<8>(L, grid, rtw, lds, x_bf16, rper, s, a, n_rwg); break;
     }
   }
   if (e != hipSuccess) return e;
-  if (stage_h)
-    return launch_kernel(K_DECODE_DOWN, decode_down_kernel<true>, dim3(L.H / kTileRows), dim3(kThreads),
-                         static_cast<uint32_t>(lds_h), s, L, T, k, residual, out, out_bf16,
-                         static_cast<const uint8_t*>(ws));
-  return launch_kernel(K_DECODE_DOWN, decode_down_kernel<false>, dim3(L.H / kTileRows), dim3(kThreads),
-                       0u, s, L, T, k, residual, out, out_bf16, static_cast<const uint8_t*>(ws));
+  // down tiles in flight per wave: every item of the largest possible slot
+  // list in one batch when that takes at most kDownBatch (zero-size padding
+  // loads still cost issue slots), else batches of kDownBatch
+  const int per_wave = (slots_max * (L.I / kTileCols) + kThreads / kWave - 1) / (kThreads / kWave);
+  auto down = [&](auto staged, auto db) {
+    constexpr bool ST = decltype(staged)::value;
+    return launch_kernel(K_DECODE_DOWN, decode_down_kernel<ST, decltype(db)::value>, dim3(L.H / kTileRows),
+                         dim3(kThreads), static_cast<uint32_t>(ST ? lds_h : 0), s, L, T, k, residual, out,
+                         out_bf16, static_cast<const uint8_t*>(ws));
+  };
+  auto down_db = [&](auto staged) {
+    switch (per_wave) {
+      case 1: return down(staged, std::integral_constant<int, 1>{});
+      case 2: return down(staged, std::integral_constant<int, 2>{});
+      case 3: return down(staged, std::integral_constant<int, 3>{});
+      case 4: return down(staged, std::integral_constant<int, 4>{});
+      case 5: return down(staged, std::integral_constant<int, 5>{});
+      case 6: return down(staged, std::integral_constant<int, 6>{});
+      default: return down(staged, std::integral_constant<int, kDownBatch>{});
+    }
+  };
+  return stage_h ? down_db(std::true_type{}) : down_db(std::false_type{});
 }
 
 // ------------------------------------------------ scratch without allocation --
