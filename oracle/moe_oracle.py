@@ -42,7 +42,7 @@ __all__ = [
     "dequantize", "quantize_q2", "ExpertBlob",
     "router_logits", "route_topk", "route_weights", "route_histogram",
     "rms_prenorm", "silu", "expert_ffn", "moe_token", "moe_layer", "moe_stack",
-    "RMS_EPS",
+    "RMS_EPS", "usage_counts", "residency_plan",
 ]
 
 # --------------------------------------------------------------------------
@@ -334,3 +334,54 @@ def moe_stack(x, layers, k, prenorm=True):
         ids, w = route_topk(logits_fn(x), k)
         x = moe_layer(x, ids, w, blob, prenorm=prenorm, residual=x)
     return x
+
+
+# --------------------------------------------------------------------------
+# Expert residency (NEXT row f4): a fixed number of expert slots in fast
+# memory hold the experts the recent routing used most; the refresh replaces
+# the rest ("RTX PRO 4500 单卡跑 125B MoE", section 最重要机制, item 2: the
+# resident expert set is refreshed every few rounds with the experts the
+# conversation uses most).
+# --------------------------------------------------------------------------
+def usage_counts(ids: np.ndarray, E: int, counts=None) -> np.ndarray:
+    """counts[e] (+=) the number of (token, slot) pairs routed to expert e;
+    ids outside [0, E) are not counted."""
+    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    flat = flat[(flat >= 0) & (flat < E)]
+    add = np.bincount(flat, minlength=E).astype(np.uint64)
+    base = np.zeros(E, dtype=np.uint64) if counts is None else np.asarray(counts, dtype=np.uint64)
+    return base + add
+
+
+def residency_plan(counts: np.ndarray, S: int, expert_of_slot) -> tuple:
+    """The S experts to hold: the S largest counts, equal counts going to the
+    lower expert id.  An expert already in a slot and still chosen keeps its
+    slot; the other chosen experts fill the remaining slots, lowest slot
+    first, in ascending expert id.  expert_of_slot: the current occupant of
+    each of the S slots (-1 = empty).  Returns (new_expert_of_slot [S],
+    slot_of [E] with -1 for experts not held, changed slots [sorted])."""
+    counts = np.asarray(counts, dtype=np.int64)
+    E = counts.size
+    if not 0 <= S <= E:
+        raise ValueError("need 0 <= S <= E")
+    cur = np.asarray(expert_of_slot, dtype=np.int64).reshape(-1)
+    if cur.size != S:
+        raise ValueError("expert_of_slot must have S entries")
+    order = np.lexsort((np.arange(E), -counts))      # count descending, then id ascending
+    chosen = set(int(e) for e in order[:S])
+    new = np.full(S, -1, dtype=np.int64)
+    kept = set()
+    for s in range(S):
+        e = int(cur[s])
+        if e in chosen and e not in kept:
+            new[s] = e
+            kept.add(e)
+    incoming = sorted(chosen - kept)
+    free = [s for s in range(S) if new[s] < 0]
+    for s, e in zip(free, incoming):
+        new[s] = e
+    slot_of = np.full(E, -1, dtype=np.int64)
+    for s in range(S):
+        slot_of[new[s]] = s
+    changed = [s for s in range(S) if new[s] != cur[s]]
+    return new.astype(np.int32), slot_of.astype(np.int32), np.array(changed, dtype=np.int32)
