@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="",
                     help="decode1|decode1_two_calls|decode1_gemv|decode2|decode3|prefill|prefill32768|"
-                         "windows|stack (profiling runs)")
+                         "tiered|windows|stack (profiling runs)")
     ap.add_argument("--stack-layers", type=int, default=48,
                     help="layers of the stacked decode/prefill runs (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -431,6 +431,84 @@ def main():
         return {"routing": "zipf(1.1)", "launch": "hip_graph", "windows": rows,
                 "grouped_first_faster_at_T": handover}
 
+    # ------------------------------------------------------- residency tier
+    def tiered_case(n_steps, warmup, arena_kind, n_layers, frac=18119 / 24576, learn=256):
+        """One token per step, Zipf(1.1) routing with one popularity order
+        per run.  Each layer's tier holds the round(frac * E) experts its
+        usage histogram over `learn` earlier tokens ranks highest (the
+        resident share of the pages' configuration); the arena holds all
+        512 (device memory, or pinned host memory read over PCIe).  The
+        same rows run untiered on the same layers for comparison; every
+        tiered step also adds to the usage histogram."""
+        S = int(round(frac * E))
+        tl = layers[:n_layers]
+        total = rows_needed(n_steps, warmup)
+        rng = synth.rng_for(4, 0, 1)
+        xd, _ = synth.activations(rng, 64, H, "bf16")
+        xs = torch.from_numpy(xd.view(np.int16)).view(torch.bfloat16).to(dev)
+        lg = torch.from_numpy(synth.zipf_logits(rng, learn + total, E)).to(dev)
+        out = torch.empty((1, H), dtype=torch.float32, device=dev)
+        ws = B.workspace(B.MOE_OP_DECODE, 1, E, K, H, I, dev)
+        ids = torch.empty((learn + total, K), dtype=torch.int32, device=dev)
+        tiers, usage = [], []
+        for L in tl:
+            if arena_kind == "host":
+                arena = torch.empty(L.experts.numel(), dtype=torch.uint8, pin_memory=True)
+                arena.copy_(L.experts)
+            else:
+                arena = L.experts
+            tiers.append(B.TieredLayer(torch.empty(S * L.expert_stride, dtype=torch.uint8, device=dev),
+                                       torch.full((E,), -1, dtype=torch.int32, device=dev), arena, L.shared,
+                                       S, E, H, I, L.expert_stride))
+            usage.append(torch.zeros(E, dtype=torch.int64, device=dev))
+        # learning window: usage only (every expert still read from the arena)
+        wl = torch.empty((1, K), dtype=torch.float32, device=dev)
+        for i in range(learn):
+            l = i % n_layers
+            B.moe_expert_forward_decode_tiered(tiers[l], xs[i % 64].view(1, H), lg[i].view(1, E), K, out,
+                                               ids[i].view(1, K), wl, None, 0, usage[l], ws)
+        torch.cuda.synchronize()
+        t0 = time.time()
+        for l in range(n_layers):
+            occ = np.full(S, -1, dtype=np.int32)
+            new, _, _ = B.moe_residency_plan(usage[l].cpu().numpy().astype(np.uint64), S, occ)
+            B.moe_residency_apply(tiers[l], occ, new)
+        torch.cuda.synchronize()
+        apply_s = (time.time() - t0) / n_layers
+        slot_of = np.stack([t.slot_of.cpu().numpy() for t in tiers])
+        wts = torch.empty((total, K), dtype=torch.float32, device=dev)
+
+        def step_t(i):
+            l = i % n_layers
+            B.moe_expert_forward_decode_tiered(tiers[l], xs[i % 64].view(1, H), lg[learn + i].view(1, E), K,
+                                               out, ids[learn + i].view(1, K), wts[i].view(1, K), None, 0,
+                                               usage[l], ws)
+
+        def step_u(i):
+            B.moe_expert_forward_decode_routed(tl[i % n_layers], xs[i % 64].view(1, H), lg[learn + i].view(1, E),
+                                               K, out, None, None, None, 0, ws)
+
+        plan, ms, ms_eager, pct, kern = run_phases(step_t, n_steps, warmup)
+        plan_u, ms_u, ms_eager_u, pct_u, _ = run_phases(step_u, n_steps, warmup)
+        idh = ids[learn:].cpu().numpy()
+        rows = list(plan["graph_timed"])
+        hit = np.array([(slot_of[i % n_layers][idh[i]] >= 0).mean() for i in rows])
+        miss_bytes = (1.0 - hit.mean()) * K * EXPERT_BYTES
+        gu = kern.get("decode_gateup_kernel", (1, float("nan")))
+        dn = kern.get("decode_down_kernel", (1, float("nan")))
+        del tiers
+        return {
+            "T": 1, "routing": "zipf(1.1), one popularity order", "arena": arena_kind,
+            "resident_slots": S, "experts": E, "layers": n_layers, "learn_tokens": learn,
+            "calls": "decode_tiered (+ usage histogram) vs decode_routed", "launch": "hip_graph",
+            "ms_per_layer": ms, **pct, "ms_per_layer_eager": ms_eager,
+            "ms_per_layer_untiered": ms_u, "ms_per_layer_untiered_eager": ms_eager_u,
+            "tokens_per_s": 1000.0 / ms, "tokens_per_s_untiered": 1000.0 / ms_u,
+            "hit_rate": float(hit.mean()), "miss_bytes_per_step": float(miss_bytes),
+            "apply_s_per_layer": apply_s,
+            "kernel_ms": {"decode_gateup": gu[1] / gu[0], "decode_down": dn[1] / dn[0]},
+        }
+
     only = args.only
     half = case_steps(args.steps)["half"]
     if only in ("", "decode1"):
@@ -456,6 +534,11 @@ def main():
     if only == "prefill32768":   # profiling runs only: one 32768-token chunk, Zipf routing
         results["prefill_T32768"] = prefill_case(32768, max(4, args.prefill_steps // 10), 2, "zipf")
         progress("prefill_T32768")
+    if only in ("", "tiered"):
+        results["decode_T1_tiered_device_arena"] = tiered_case(half, args.warmup, "device", len(layers))
+        progress("decode_T1_tiered_device_arena")
+        results["decode_T1_tiered_host_arena"] = tiered_case(half, args.warmup, "host", min(4, len(layers)))
+        progress("decode_T1_tiered_host_arena")
     if only in ("", "windows"):
         results["verify_windows"] = verify_windows([4, 5, 6, 7, 8], case_steps(args.steps)["windows"],
                                                    max(4, args.warmup // 2))

@@ -25,7 +25,9 @@ MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL, MOE_OP_ROUTE_GEMV = 0, 1, 2, 3
 
 EXPORTS = ["moe_workspace_bytes", "moe_route_topk", "moe_route_topk_gemv", "moe_expert_forward_decode",
            "moe_expert_forward_decode_routed", "moe_expert_forward_decode_routed_noalloc",
-           "moe_expert_forward_prefill", "moe_status_string", "moe_last_error",
+           "moe_expert_forward_prefill", "moe_expert_usage_update", "moe_residency_plan",
+           "moe_residency_apply", "moe_expert_forward_decode_tiered", "moe_expert_forward_prefill_tiered",
+           "moe_status_string", "moe_last_error",
            "moe_profile_enable", "moe_profile_reset", "moe_profile_num_kernels",
            "moe_profile_kernel_name", "moe_profile_query"]
 
@@ -39,6 +41,12 @@ class MoeError(RuntimeError):
 class _Layer(C.Structure):
     _fields_ = [("experts", C.c_void_p), ("shared", C.c_void_p), ("expert_stride", C.c_int64),
                 ("num_experts", C.c_int32), ("hidden", C.c_int32), ("inter", C.c_int32)]
+
+
+class _TieredLayer(C.Structure):
+    _fields_ = [("slots", C.c_void_p), ("slot_of", C.c_void_p), ("arena", C.c_void_p), ("shared", C.c_void_p),
+                ("expert_stride", C.c_int64), ("num_slots", C.c_int32), ("num_experts", C.c_int32),
+                ("hidden", C.c_int32), ("inter", C.c_int32)]
 
 
 def _load():
@@ -65,6 +73,18 @@ def _load():
     lib.moe_expert_forward_prefill.argtypes = [C.POINTER(_Layer), vp, i32, i32, vp, vp, i32, vp, vp,
                                                vp, vp, vp, vp, i32, C.c_uint32, vp, sz, vp]
     lib.moe_expert_forward_prefill.restype = C.c_int
+    lib.moe_expert_usage_update.argtypes = [vp, i64, i32, vp, vp]
+    lib.moe_expert_usage_update.restype = C.c_int
+    lib.moe_residency_plan.argtypes = [vp, i32, i32, vp, vp, vp, vp]
+    lib.moe_residency_plan.restype = C.c_int
+    lib.moe_residency_apply.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp]
+    lib.moe_residency_apply.restype = C.c_int
+    lib.moe_expert_forward_decode_tiered.argtypes = [C.POINTER(_TieredLayer), vp, i32, i32, vp, i32, vp, vp,
+                                                     vp, vp, i32, C.c_uint32, vp, vp, sz, vp]
+    lib.moe_expert_forward_decode_tiered.restype = C.c_int
+    lib.moe_expert_forward_prefill_tiered.argtypes = [C.POINTER(_TieredLayer), vp, i32, i32, vp, vp, i32, vp,
+                                                      vp, vp, vp, vp, vp, i32, C.c_uint32, vp, sz, vp]
+    lib.moe_expert_forward_prefill_tiered.restype = C.c_int
     lib.moe_status_string.argtypes = [C.c_int]
     lib.moe_status_string.restype = C.c_char_p
     lib.moe_last_error.argtypes = []
@@ -199,6 +219,94 @@ def moe_expert_forward_prefill(layer: Layer, x, topk_ids, topk_w, counts, offset
                                           _ptr(sorted_pairs), _ptr(pair_pos), _ptr(residual),
                                           _ptr(out), _dtype_code(out), flags, _ptr(ws),
                                           0 if ws is None else ws.numel(), _stream(stream)))
+
+
+# --------------------------------------------------------- residency tier --
+def _arena_ptr(t: torch.Tensor):
+    """The arena may be device memory or pinned host memory (a CPU tensor
+    made with pin_memory=True); the library maps the latter itself."""
+    if not t.is_contiguous():
+        raise ValueError("the arena must be contiguous")
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError("the arena must be on the GPU or in pinned host memory")
+    return C.c_void_p(t.data_ptr())
+
+
+def _host_i32(a):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(C.c_void_p)
+
+
+@dataclass
+class TieredLayer:
+    """A layer whose experts live in `arena` (all E, device or pinned host
+    memory), S of them copied into `slots` (device); slot_of (device int32
+    [E]) maps expert -> slot or -1."""
+    slots: Optional[torch.Tensor]
+    slot_of: torch.Tensor
+    arena: torch.Tensor
+    shared: Optional[torch.Tensor]
+    num_slots: int
+    num_experts: int
+    hidden: int
+    inter: int
+    expert_stride: int
+
+    def _c(self) -> _TieredLayer:
+        return _TieredLayer(None if self.slots is None else _ptr(self.slots).value, _ptr(self.slot_of).value,
+                            _arena_ptr(self.arena).value,
+                            None if self.shared is None else _ptr(self.shared).value, self.expert_stride,
+                            self.num_slots, self.num_experts, self.hidden, self.inter)
+
+
+def moe_expert_usage_update(ids, E: int, counts, stream=None):
+    """counts (device uint64/int64 [E]) += occurrences of each expert in ids."""
+    _check(lib.moe_expert_usage_update(_ptr(ids), ids.numel(), E, _ptr(counts), _stream(stream)))
+
+
+def moe_residency_plan(counts, S: int, expert_of_slot):
+    """Host plan: (new_expert_of_slot [S], slot_of [E], n_changed)."""
+    import numpy as np
+    c = np.ascontiguousarray(counts, dtype=np.uint64)
+    E = c.size
+    cur, cur_p = _host_i32(np.asarray(expert_of_slot).reshape(-1))
+    new = np.empty(S, dtype=np.int32)
+    slot_of = np.empty(E, dtype=np.int32)
+    n = C.c_int32(0)
+    _check(lib.moe_residency_plan(c.ctypes.data_as(C.c_void_p), E, S, cur_p, new.ctypes.data_as(C.c_void_p),
+                                  slot_of.ctypes.data_as(C.c_void_p), C.byref(n)))
+    return new, slot_of, n.value
+
+
+def moe_residency_apply(layer: TieredLayer, old_expert_of_slot, new_expert_of_slot, stream=None):
+    """Copies the changed slots from the arena and updates layer.slot_of."""
+    old, old_p = _host_i32(old_expert_of_slot)
+    new, new_p = _host_i32(new_expert_of_slot)
+    _check(lib.moe_residency_apply(_arena_ptr(layer.arena), layer.expert_stride, layer.num_experts,
+                                   layer.num_slots, old_p, new_p, _ptr(layer.slots), _ptr(layer.slot_of),
+                                   _stream(stream)))
+
+
+def moe_expert_forward_decode_tiered(layer: TieredLayer, x, logits, k, out, topk_ids=None, topk_w=None,
+                                     residual=None, flags=0, usage_counts=None, ws=None, stream=None):
+    T = logits.shape[0]
+    c = layer._c()
+    _check(lib.moe_expert_forward_decode_tiered(C.byref(c), _ptr(x), _dtype_code(x), T, _ptr(logits), k,
+                                                _ptr(topk_ids), _ptr(topk_w), _ptr(residual), _ptr(out),
+                                                _dtype_code(out), flags, _ptr(usage_counts), _ptr(ws),
+                                                0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def moe_expert_forward_prefill_tiered(layer: TieredLayer, x, topk_ids, topk_w, counts, offsets, sorted_pairs,
+                                      pair_pos, out, residual=None, flags=0, ws=None, stream=None):
+    T, k = topk_ids.shape
+    c = layer._c()
+    _check(lib.moe_expert_forward_prefill_tiered(C.byref(c), _ptr(x), _dtype_code(x), T, _ptr(topk_ids),
+                                                 _ptr(topk_w), k, _ptr(counts), _ptr(offsets),
+                                                 _ptr(sorted_pairs), _ptr(pair_pos), _ptr(residual),
+                                                 _ptr(out), _dtype_code(out), flags, _ptr(ws),
+                                                 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 # ---------------------------------------------------------------- helpers --

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_q2.so")
 CEILINGS = os.path.join(PKG, "moe_ceilings")        # standalone device-ceiling microbenchmarks
-SOURCES = ["route.hip", "decode.hip", "prefill.hip", "api.cpp"]
+SOURCES = ["route.hip", "decode.hip", "prefill.hip", "residency.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: never emit packed fp32 VALU ops (v_pk_{add,mul,fma}_f32).

@@ -3,6 +3,7 @@
 // hipEvent measurement hooks.  No device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -80,7 +81,7 @@ const char* const kKernelNames[K_NUM_KERNELS] = {
     "route_topk_kernel",     "route_scan_kernel",     "route_scatter_kernel",
     "decode_gateup_kernel",  "decode_down_kernel",    "prefill_prep_kernel",
     "prefill_gateup_kernel", "prefill_down_kernel",   "prefill_combine_kernel",
-    "route_gemv_topk_kernel"};
+    "route_gemv_topk_kernel", "usage_update_kernel",  "residency_map_kernel"};
 
 bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_BF16; }
 
@@ -381,12 +382,11 @@ int moe_expert_forward_decode_routed_noalloc(const moe_q2_layer* layer, const vo
                        scratch, stream);
 }
 
-int moe_expert_forward_prefill(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
-                               int32_t T, const int32_t* topk_ids, const float* topk_w, int32_t k,
-                               const int32_t* counts, const int32_t* offsets,
-                               const int32_t* sorted_pairs, const int32_t* pair_pos,
-                               const void* residual, void* out, int32_t out_dtype, uint32_t flags,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+static int check_prefill(const moe_q2_layer* layer, const void* x, int32_t x_dtype, int32_t T,
+                         const int32_t* topk_ids, const float* topk_w, int32_t k, const int32_t* counts,
+                         const int32_t* offsets, const int32_t* sorted_pairs, const int32_t* pair_pos,
+                         const void* residual, const void* out, int32_t out_dtype, uint32_t flags,
+                         void* workspace, size_t workspace_bytes) {
   int st = check_forward(layer, x, x_dtype, T, topk_ids, topk_w, k, residual, out, out_dtype, flags, workspace);
   if (st) return st;
   if (!counts || !offsets || !sorted_pairs || !pair_pos)
@@ -394,10 +394,250 @@ int moe_expert_forward_prefill(const moe_q2_layer* layer, const void* x, int32_t
   if (T > MOE_MAX_TOKENS) return fail(MOE_ERR_UNSUPPORTED, "T must be <= 2^17");
   const size_t need = prefill_workspace_bytes(T, layer->num_experts, k, layer->hidden, layer->inter);
   if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
+  return MOE_OK;
+}
+
+int moe_expert_forward_prefill(const moe_q2_layer* layer, const void* x, int32_t x_dtype,
+                               int32_t T, const int32_t* topk_ids, const float* topk_w, int32_t k,
+                               const int32_t* counts, const int32_t* offsets,
+                               const int32_t* sorted_pairs, const int32_t* pair_pos,
+                               const void* residual, void* out, int32_t out_dtype, uint32_t flags,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_prefill(layer, x, x_dtype, T, topk_ids, topk_w, k, counts, offsets, sorted_pairs, pair_pos,
+                              residual, out, out_dtype, flags, workspace, workspace_bytes);
+  if (st) return st;
   const hipError_t e = launch_prefill(layer_args(layer), x, x_dtype == MOE_BF16, T, topk_ids, topk_w, k,
                                       counts, offsets, sorted_pairs, pair_pos, residual, out,
                                       out_dtype == MOE_BF16, (flags & MOE_FLAG_PRENORM_RMS) ? 1 : 0,
                                       workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "prefill launch");
+}
+
+// ------------------------------------------------------------- residency --
+
+int moe_expert_usage_update(const int32_t* ids, int64_t n, int32_t E, uint64_t* counts, void* stream) {
+  if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E must be <= 1024");
+  if (n < 0 || n > 0x7FFFFFFFLL) return fail(MOE_ERR_INVALID_ARG, "n must be in 0..2^31-1");
+  if (n > 0 && (!ids || !counts)) return fail(MOE_ERR_INVALID_ARG, "ids and counts are required");
+  if (!aligned(ids, 4) || !aligned(counts, 8))
+    return fail(MOE_ERR_INVALID_ARG, "ids must be 4-byte and counts 8-byte aligned");
+  const hipError_t e = launch_usage_update(ids, n, E, reinterpret_cast<unsigned long long*>(counts),
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "usage update launch");
+}
+
+namespace {
+
+// Occupants of S slots: each -1 or an expert in [0, E), no expert twice.
+// slot_of (E entries) receives the inverse map.
+int check_occupants(const int32_t* occ, int32_t E, int32_t S, std::vector<int32_t>& slot_of, const char* name) {
+  slot_of.assign(static_cast<size_t>(E), -1);
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t e = occ[s];
+    if (e < -1 || e >= E) return fail(MOE_ERR_INVALID_ARG, "%s[%d] = %d is not -1 or an expert", name, s, e);
+    if (e >= 0) {
+      if (slot_of[e] >= 0) return fail(MOE_ERR_INVALID_ARG, "%s holds expert %d twice", name, e);
+      slot_of[e] = s;
+    }
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+int moe_residency_plan(const uint64_t* counts, int32_t E, int32_t S, const int32_t* expert_of_slot,
+                       int32_t* new_expert_of_slot, int32_t* slot_of, int32_t* n_changed) {
+  if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E must be <= 1024");
+  if (S < 0 || S > E) return fail(MOE_ERR_INVALID_ARG, "S must be in 0..E");
+  if (!counts) return fail(MOE_ERR_INVALID_ARG, "counts is required");
+  if (S > 0 && (!expert_of_slot || !new_expert_of_slot))
+    return fail(MOE_ERR_INVALID_ARG, "expert_of_slot and new_expert_of_slot are required");
+  std::vector<int32_t> cur_slot;
+  const std::vector<int32_t> cur(expert_of_slot, expert_of_slot + S);
+  int st = check_occupants(cur.data(), E, S, cur_slot, "expert_of_slot");
+  if (st) return st;
+  // the S largest counts, ties to the lower id
+  std::vector<int32_t> order(static_cast<size_t>(E));
+  for (int32_t e = 0; e < E; ++e) order[e] = e;
+  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    return counts[a] != counts[b] ? counts[a] > counts[b] : a < b;
+  });
+  std::vector<char> chosen(static_cast<size_t>(E), 0);
+  for (int32_t i = 0; i < S; ++i) chosen[order[i]] = 1;
+  // chosen experts already held stay where they are
+  std::vector<int32_t> next(static_cast<size_t>(S), -1);
+  for (int32_t s = 0; s < S; ++s)
+    if (cur[s] >= 0 && chosen[cur[s]]) next[s] = cur[s];
+  // the others, in ascending id, into the free slots, lowest first
+  int32_t free_slot = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    if (!chosen[e] || cur_slot[e] >= 0) continue;
+    while (next[free_slot] >= 0) ++free_slot;
+    next[free_slot] = e;
+  }
+  int32_t changed = 0;
+  for (int32_t s = 0; s < S; ++s) changed += next[s] != cur[s];
+  std::copy(next.begin(), next.end(), new_expert_of_slot);
+  if (slot_of) {
+    for (int32_t e = 0; e < E; ++e) slot_of[e] = -1;
+    for (int32_t s = 0; s < S; ++s) slot_of[next[s]] = s;
+  }
+  if (n_changed) *n_changed = changed;
+  return MOE_OK;
+}
+
+int moe_residency_apply(const void* arena, int64_t expert_stride, int32_t E, int32_t S,
+                        const int32_t* old_expert_of_slot, const int32_t* new_expert_of_slot, void* slots,
+                        int32_t* slot_of, void* stream) {
+  if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E must be <= 1024");
+  if (S < 0 || S > E) return fail(MOE_ERR_INVALID_ARG, "S must be in 0..E");
+  if (!arena || !slot_of) return fail(MOE_ERR_INVALID_ARG, "arena and slot_of are required");
+  if (S > 0 && (!slots || !old_expert_of_slot || !new_expert_of_slot))
+    return fail(MOE_ERR_INVALID_ARG, "slots, old_expert_of_slot and new_expert_of_slot are required");
+  if (expert_stride < 256 || expert_stride % 256)
+    return fail(MOE_ERR_INVALID_ARG, "expert_stride must be a positive multiple of 256");
+  if (!aligned(arena, 256) || !aligned(slots, 256) || !aligned(slot_of, 4))
+    return fail(MOE_ERR_INVALID_ARG, "arena and slots must be 256-byte aligned, slot_of 4-byte aligned");
+  std::vector<int32_t> old_slot, new_slot;
+  int st = check_occupants(old_expert_of_slot, E, S, old_slot, "old_expert_of_slot");
+  if (st || (st = check_occupants(new_expert_of_slot, E, S, new_slot, "new_expert_of_slot"))) return st;
+  for (int32_t e = 0; e < E; ++e)
+    if (old_slot[e] >= 0 && new_slot[e] >= 0 && old_slot[e] != new_slot[e])
+      return fail(MOE_ERR_INVALID_ARG, "expert %d moves from slot %d to slot %d", e, old_slot[e], new_slot[e]);
+  // map changes: experts that leave (-> -1) and that enter (-> slot); the
+  // two sets are disjoint, so their order does not matter
+  std::vector<uint32_t> recs;
+  for (int32_t e = 0; e < E; ++e)
+    if (old_slot[e] != new_slot[e]) recs.push_back(static_cast<uint32_t>(e) | (static_cast<uint32_t>(new_slot[e] + 1) << 16));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* dst = static_cast<uint8_t*>(slots);
+  const uint8_t* src = static_cast<const uint8_t*>(arena);
+  for (int32_t q = 0; q < S; ++q) {
+    const int32_t e = new_expert_of_slot[q];
+    if (e < 0 || e == old_expert_of_slot[q]) continue;
+    const hipError_t he = hipMemcpyAsync(dst + q * expert_stride, src + e * expert_stride,
+                                         static_cast<size_t>(expert_stride), hipMemcpyDefault, s);
+    if (he != hipSuccess) return hip_fail(he, "slot copy");
+  }
+  for (size_t i = 0; i < recs.size(); i += kMapRecs) {
+    MapRecs m{};
+    const int n = static_cast<int>(std::min<size_t>(kMapRecs, recs.size() - i));
+    std::copy(recs.begin() + i, recs.begin() + i + n, m.rec);
+    const hipError_t he = launch_residency_map(slot_of, m, n, s);
+    if (he != hipSuccess) return hip_fail(he, "slot map launch");
+  }
+  return MOE_OK;
+}
+
+namespace {
+
+// A tiered layer checked as an untiered one whose experts are the arena.
+moe_q2_layer flat_of(const moe_q2_tiered_layer* t) {
+  moe_q2_layer L;
+  L.experts = t->arena;
+  L.shared = t->shared;
+  L.expert_stride = t->expert_stride;
+  L.num_experts = t->num_experts;
+  L.hidden = t->hidden;
+  L.inter = t->inter;
+  return L;
+}
+
+// Device address of `p`: device memory as it is, pinned host memory through
+// its device mapping; other memory (pageable host memory) is refused.
+int device_view(const void* p, const uint8_t** dev, int* kind) {
+  hipPointerAttribute_t a;
+  const hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();   // not sticky: the next launch checks the error state
+    return fail(MOE_ERR_INVALID_ARG, "arena is neither device memory nor pinned host memory");
+  }
+  *kind = a.type;
+  if (a.type == hipMemoryTypeDevice) {
+    *dev = static_cast<const uint8_t*>(p);
+    return MOE_OK;
+  }
+  if (a.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess || !d) {
+      (void)hipGetLastError();
+      return fail(MOE_ERR_INVALID_ARG, "arena is pinned host memory without a device mapping");
+    }
+    *dev = static_cast<const uint8_t*>(d);
+    return MOE_OK;
+  }
+  return fail(MOE_ERR_INVALID_ARG, "arena is neither device memory nor pinned host memory");
+}
+
+// Everything a tiered call adds to the untiered checks, and its LayerArgs.
+int tier_args(const moe_q2_tiered_layer* t, LayerArgs& a) {
+  if (!t->arena) return fail(MOE_ERR_INVALID_ARG, "layer->arena is NULL");
+  if (!t->slot_of || !aligned(t->slot_of, 4))
+    return fail(MOE_ERR_INVALID_ARG, "layer->slot_of is required (4-byte aligned)");
+  if (t->num_slots < 0 || t->num_slots > t->num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "num_slots must be in 0..num_experts");
+  if (t->num_slots > 0 && (!t->slots || !aligned(t->slots, 256)))
+    return fail(MOE_ERR_INVALID_ARG, "layer->slots is required with num_slots > 0 (256-byte aligned)");
+  // the first and the last byte of the arena are memory the device can read
+  const uint8_t* dev = nullptr;
+  const uint8_t* dev_end = nullptr;
+  int kind = 0, kind_end = 0;
+  int st = device_view(t->arena, &dev, &kind);
+  if (st) return st;
+  const uint8_t* last = static_cast<const uint8_t*>(t->arena) + t->num_experts * t->expert_stride - 1;
+  if ((st = device_view(last, &dev_end, &kind_end))) return st;
+  if (kind_end != kind || dev_end != dev + t->num_experts * t->expert_stride - 1)
+    return fail(MOE_ERR_INVALID_ARG, "the arena's E * expert_stride bytes are not one mapped range");
+  a.experts = static_cast<const uint8_t*>(t->slots);
+  a.slot_of = t->slot_of;
+  a.arena = dev;
+  a.S = t->num_slots;
+  return MOE_OK;
+}
+
+}  // namespace
+
+int moe_expert_forward_decode_tiered(const moe_q2_tiered_layer* layer, const void* x, int32_t x_dtype,
+                                     int32_t T, const float* logits, int32_t k, int32_t* topk_ids,
+                                     float* topk_w, const void* residual, void* out, int32_t out_dtype,
+                                     uint32_t flags, uint64_t* usage_counts, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (!layer) return fail(MOE_ERR_INVALID_ARG, "layer descriptor is NULL");
+  const moe_q2_layer flat = flat_of(layer);
+  int st = check_routed_args(&flat, x, x_dtype, T, logits, k, topk_ids, topk_w, residual, out, out_dtype, flags);
+  if (st || (st = check_workspace(workspace))) return st;
+  if (!aligned(usage_counts, 8)) return fail(MOE_ERR_INVALID_ARG, "usage_counts must be 8-byte aligned");
+  const size_t need = decode_workspace_bytes(T, k, layer->hidden, layer->inter);
+  if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: need %lld bytes", (long long)need);
+  LayerArgs a = layer_args(&flat);
+  if ((st = tier_args(layer, a))) return st;
+  a.usage = reinterpret_cast<unsigned long long*>(usage_counts);
+  const hipError_t e = launch_decode(a, x, x_dtype == MOE_BF16, T, nullptr, nullptr, logits, topk_ids, topk_w, k,
+                                     residual, out, out_dtype == MOE_BF16, (flags & MOE_FLAG_PRENORM_RMS) ? 1 : 0,
+                                     workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "decode launch");
+}
+
+int moe_expert_forward_prefill_tiered(const moe_q2_tiered_layer* layer, const void* x, int32_t x_dtype,
+                                      int32_t T, const int32_t* topk_ids, const float* topk_w, int32_t k,
+                                      const int32_t* counts, const int32_t* offsets,
+                                      const int32_t* sorted_pairs, const int32_t* pair_pos,
+                                      const void* residual, void* out, int32_t out_dtype, uint32_t flags,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!layer) return fail(MOE_ERR_INVALID_ARG, "layer descriptor is NULL");
+  const moe_q2_layer flat = flat_of(layer);
+  int st = check_prefill(&flat, x, x_dtype, T, topk_ids, topk_w, k, counts, offsets, sorted_pairs, pair_pos,
+                         residual, out, out_dtype, flags, workspace, workspace_bytes);
+  if (st) return st;
+  LayerArgs a = layer_args(&flat);
+  if ((st = tier_args(layer, a))) return st;
+  const hipError_t e = launch_prefill(a, x, x_dtype == MOE_BF16, T, topk_ids, topk_w, k, counts, offsets,
+                                      sorted_pairs, pair_pos, residual, out, out_dtype == MOE_BF16,
+                                      (flags & MOE_FLAG_PRENORM_RMS) ? 1 : 0, workspace,
+                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, "prefill launch");
 }
 

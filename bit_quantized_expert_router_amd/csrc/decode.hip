@@ -67,6 +67,7 @@ constexpr int kDownStage = 4;            // h~ chunks per thread loaded ahead in
 struct DecodeHeader {          // start of the workspace, written by block 0 of kernel 1
   int32_t n_slots;
   int32_t pad0[3];
+  const uint8_t* base[kMaxSlots];                  // weights of each slot's expert
   int32_t expert[kMaxSlots];                       // -1 = shared expert
   int32_t pidx[kMaxSlots][kMaxT];                  // pair of (slot, token) or -1
 };
@@ -201,8 +202,14 @@ __device__ __forceinline__ int token_of_chunk(int c, int cpt) {
   return t;
 }
 
-__device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e) {
-  return e < 0 ? L.shared : L.experts + static_cast<int64_t>(e) * L.stride;
+// Weights of expert e (-1 = the shared expert); with the residency tier,
+// from its slot (slotmap: slot_of in LDS) or the arena.
+__device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e, const int* slotmap) {
+  if (e < 0) return L.shared;
+  if (!L.slot_of) return L.experts + static_cast<int64_t>(e) * L.stride;
+  const int s = slotmap[e];
+  return s >= 0 && s < L.S ? L.experts + static_cast<int64_t>(s) * L.stride
+                           : L.arena + static_cast<int64_t>(e) * L.stride;
 }
 
 // Bytes of one I x H (or H x I) matrix in tile records.
@@ -477,7 +484,7 @@ struct DownTiles {
 // wave w takes items w, w + 8, ...; this loads the wave's items j0..j0+DB-1
 // (an item past nitems gets a zero-size resource: issued, no memory touched).
 template <int DB>
-__device__ __forceinline__ void load_down(const LayerArgs& L, const int* expert, int nitems, int KTd,
+__device__ __forceinline__ void load_down(const LayerArgs& L, const uint8_t* const* base, int nitems, int KTd,
                                           int rt, int j0, int lane, DownTiles<DB>& D) {
   const int wid = wave_id();
   const uint32_t mat = __builtin_amdgcn_readfirstlane(matrix_bytes(L.H, L.I));
@@ -487,8 +494,7 @@ __device__ __forceinline__ void load_down(const LayerArgs& L, const int* expert,
     const bool live = wi < nitems;
     const int slot = live ? wi / KTd : 0;
     const int kt = live ? wi % KTd : 0;
-    const int e = __builtin_amdgcn_readfirstlane(live ? expert[slot] : 0);
-    const __amdgpu_buffer_rsrc_t r = expert_rsrc(expert_base(L, e), live ? 3u * mat : 0u);
+    const __amdgpu_buffer_rsrc_t r = expert_rsrc(base[live ? slot : 0], live ? 3u * mat : 0u);
     const uint32_t off = __builtin_amdgcn_readfirstlane(
         2u * mat + static_cast<uint32_t>(rt * KTd + kt) * kTileBytes);
     D.c[b] = load_codes(r, off, lane);
@@ -648,6 +654,7 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
   __shared__ float s_stat[NW][kMaxT][2];
   __shared__ f32x4 s_red[NW][2][32];
   __shared__ int s_slot_of[MOE_MAX_EXPERTS];
+  __shared__ int s_slotmap[MOE_MAX_EXPERTS];      // residency tier: slot_of
   __shared__ float s_smul[kMaxT];
 
   if constexpr (SPLIT) {
@@ -675,6 +682,8 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
   const bool xreg = nch <= nxt * XC;
   u32x4 xr[XC][2];
   if (wid >= xw0) issue_x<BF16, XC>(x, nch, xreg, xr, xt, nxt);
+  if (L.slot_of)
+    for (int i = threadIdx.x; i < L.E; i += NT) s_slotmap[i] = L.slot_of[i];
   if (wid < T) {
     if constexpr (RPER > 0) {
       int my_e;
@@ -714,14 +723,29 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
   const int rt = active ? g % RTI : 0;
 
   GateUpTiles<KTW> R;
-  load_gateup<KTW>(expert_base(L, active ? S.expert[slot] : 0), active, H, I, rt, kq, lane, R);
+  load_gateup<KTW>(expert_base(L, active ? S.expert[slot] : 0, s_slotmap), active, H, I, rt, kq, lane, R);
   int8_t* hexp = reinterpret_cast<int8_t*>(ws + kHeaderBytes + decode_h_bytes(T, k, I));
   if (blockIdx.x == 0) {
     DecodeHeader* hdr = reinterpret_cast<DecodeHeader*>(ws);
     for (int i = threadIdx.x; i < S.n * kMaxT; i += NT)
       (&hdr->pidx[0][0])[i] = (&S.pidx[0][0])[i];
-    if (threadIdx.x < S.n) hdr->expert[threadIdx.x] = S.expert[threadIdx.x];
+    if (threadIdx.x < S.n) {
+      hdr->expert[threadIdx.x] = S.expert[threadIdx.x];
+      hdr->base[threadIdx.x] = expert_base(L, S.expert[threadIdx.x], s_slotmap);
+    }
     if (threadIdx.x == 0) hdr->n_slots = S.n;
+    if (L.usage) {
+      // usage histogram of the routed pairs (integer atomics, order-free);
+      // one token's top-k has a slot per pair
+      if (RPER > 0 && T == 1) {
+        if (threadIdx.x < k) atomicAdd(&L.usage[S.expert[threadIdx.x]], 1ull);
+      } else {
+        for (int p = threadIdx.x; p < T * k; p += NT) {
+          const int s = S.pslot[p];
+          if (s >= 0) atomicAdd(&L.usage[S.expert[s]], 1ull);
+        }
+      }
+    }
     if constexpr (RPER == 0) {
       // routed pairs that own no h~ row (an id outside [0, E), or a repeat
       // of a token's id; the top-k of the logits never makes one): their
@@ -749,7 +773,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     int out_bf16, const uint8_t* __restrict__ ws) {
   extern __shared__ __align__(16) uint8_t dyn[];
   _Float16* hs = reinterpret_cast<_Float16*>(dyn);     // [T*k + T][I] when staged
-  __shared__ int s_expert[kMaxSlots];
+  __shared__ const uint8_t* s_base[kMaxSlots];
   __shared__ int s_pidx[kMaxSlots][kMaxT];
   __shared__ int s_n;
   __shared__ int s_et[kMaxT];       // E_t of each token
@@ -792,13 +816,13 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     // the header loads are issued together (clamped, unconditional)
     constexpr int kPidxLoads = (kMaxSlots * kMaxT + kThreads - 1) / kThreads;
     const int i = threadIdx.x;
-    const int ev = hdr->expert[min(i, kMaxSlots - 1)];
+    const uint8_t* bv = hdr->base[min(i, kMaxSlots - 1)];
     int pv[kPidxLoads];
 #pragma unroll
     for (int q = 0; q < kPidxLoads; ++q)
       pv[q] = (&hdr->pidx[0][0])[min(i + kThreads * q, kMaxSlots * kMaxT - 1)];
     const int nv = hdr->n_slots;
-    if (i < kMaxSlots) s_expert[i] = ev;
+    if (i < kMaxSlots) s_base[i] = bv;
 #pragma unroll
     for (int q = 0; q < kPidxLoads; ++q)
       if (i + kThreads * q < kMaxSlots * kMaxT) (&s_pidx[0][0])[i + kThreads * q] = pv[q];
@@ -864,7 +888,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   // the weight loads go out after the staging: a wave's instructions wait
   // behind the issue of its loads once the CU has many in flight
   DownTiles<DB> D;
-  load_down<DB>(L, s_expert, nitems, KTd, rt, 0, lane, D);
+  load_down<DB>(L, s_base, nitems, KTd, rt, 0, lane, D);
   __syncthreads();
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -872,7 +896,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   const _Float16* hsrc = STAGED ? hs : hin;
   mma_down<DB, STAGED>(D, nitems, KTd, 0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
   for (int j0 = DB; j0 < per_wave; j0 += DB) {
-    load_down<DB>(L, s_expert, nitems, KTd, rt, j0, lane, D);
+    load_down<DB>(L, s_base, nitems, KTd, rt, j0, lane, D);
     mma_down<DB, STAGED>(D, nitems, KTd, j0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
   }
   down_store(acc, s_red, rt, T, L.H, s_et, residual, out, out_bf16);

@@ -20,6 +20,8 @@ enum KernelId {
   K_PREFILL_DOWN,
   K_PREFILL_COMBINE,
   K_ROUTE_GEMV_TOPK,
+  K_USAGE_UPDATE,
+  K_RESIDENCY_MAP,
   K_NUM_KERNELS
 };
 
@@ -78,10 +80,18 @@ hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const i
 
 // ----------------------------------------------------------------- decode --
 struct LayerArgs {
-  const uint8_t* experts;
+  const uint8_t* experts;   // all E experts, or (with slot_of) the S resident slots
   const uint8_t* shared;
   int64_t stride;
   int E, H, I;
+  // residency tier (slot_of == nullptr otherwise): expert e is in slot
+  // slot_of[e] of `experts` when that lies in [0, S), else at
+  // arena + e * stride
+  const int32_t* slot_of = nullptr;
+  const uint8_t* arena = nullptr;
+  int S = 0;
+  // decode: += pairs routed to each expert (nullptr: not counted)
+  unsigned long long* usage = nullptr;
 };
 
 // With `logits` non-null the routing (ids, w) is taken inside the gate/up
@@ -106,5 +116,17 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
                           const int32_t* pair_pos, const void* residual, void* out,
                           int out_bf16, int prenorm, void* ws, hipStream_t s);
 size_t prefill_workspace_bytes(int T, int E, int k, int H, int I);
+
+// ------------------------------------------------------------ residency --
+// counts[e] += entries of ids[0..n) equal to e (others skipped).
+hipError_t launch_usage_update(const int32_t* ids, long long n, int E, unsigned long long* counts,
+                               hipStream_t s);
+// Changes of the device slot map, carried as kernel arguments: entry i sets
+// slot_of[rec & 0xFFFF] = (rec >> 16) - 1.
+constexpr int kMapRecs = 256;
+struct MapRecs {
+  uint32_t rec[kMapRecs];
+};
+hipError_t launch_residency_map(int32_t* slot_of, const MapRecs& recs, int n, hipStream_t s);
 
 }  // namespace moeq2

@@ -124,8 +124,17 @@ __device__ __forceinline__ int2 work_unit(int bid, const int32_t* hdr, int RB) {
   return u < 0 ? make_int2(-1, 0) : make_int2(u / RB, u % RB);
 }
 
-__device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, int e) {
-  return e >= L.E ? L.shared : L.experts + static_cast<int64_t>(e) * L.stride;
+// Where a work item's expert sits: the w field holds its slot (the expert
+// itself without the residency tier; -1 = in the arena), set by prep.
+__device__ __forceinline__ int item_slot(const LayerArgs& L, int e) {
+  if (e >= L.E || !L.slot_of) return e;
+  const int s = L.slot_of[e];
+  return s >= 0 && s < L.S ? s : -1;
+}
+__device__ __forceinline__ const uint8_t* expert_base(const LayerArgs& L, const int4& it) {
+  if (it.x >= L.E) return L.shared;
+  return it.w >= 0 ? L.experts + static_cast<int64_t>(it.w) * L.stride
+                   : L.arena + static_cast<int64_t>(it.x) * L.stride;
 }
 
 // --------------------------------------------------------------------- prep --
@@ -283,10 +292,11 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
       if (e < nexp) {
         int r0, n;
         rows_of(e, r0, n);
+        const int slot = n > 0 ? item_slot(L, e) : 0;
         for (int g = 0; g * kGroupRows < n; ++g) {
           const int rows = min(kGroupRows, n - g * kGroupRows);
           const int at = pos[cls(rows)]++;
-          if (at < item_cap) ws.items[at] = make_int4(e, r0 + g * kGroupRows, rows, 0);
+          if (at < item_cap) ws.items[at] = make_int4(e, r0 + g * kGroupRows, rows, slot);
         }
       }
     }
@@ -321,8 +331,9 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(
     if (e < nexp) {
       int r0, n;
       rows_of(e, r0, n);
+      const int slot = n > 0 ? item_slot(L, e) : 0;
       for (int g = 0; g * kGroupRows < n && pos < item_cap; ++g)
-        ws.items[pos++] = make_int4(e, r0 + g * kGroupRows, min(kGroupRows, n - g * kGroupRows), 0);
+        ws.items[pos++] = make_int4(e, r0 + g * kGroupRows, min(kGroupRows, n - g * kGroupRows), slot);
     }
   }
   if (threadIdx.x == 255) {
@@ -533,7 +544,7 @@ __device__ __forceinline__ void k_loop_fixed(u32x4 (&b)[RING][NB], LoadB load_b,
 
 // ------------------------------------------------------------------ gate/up --
 template <int NMT, int RING, int KTC>
-__device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs& ws, int T, int e,
+__device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs& ws, int T, const uint8_t* wb,
                                             int row0, int nrows, int rt,
                                             _Float16 (*s_a)[kATileHalves], const uint32_t* s_off,
                                             const float* s_w, const float* s_u) {
@@ -543,7 +554,7 @@ __device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs&
   const int KT = H / kTileCols;
   const uint32_t mat = static_cast<uint32_t>(
       __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(I) * H * 5 / 16)));
-  const __amdgpu_buffer_rsrc_t rs = expert_rsrc(expert_base(L, e), 3 * mat);
+  const __amdgpu_buffer_rsrc_t rs = expert_rsrc(wb, 3 * mat);
   const uint32_t gate = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(rt)) * KT * kTileBytes;
   auto load_b = [&](u32x4 (&b)[4], int kt) {
     const uint32_t o = gate + static_cast<uint32_t>(min(kt, KT - 1)) * kTileBytes;
@@ -610,7 +621,8 @@ __global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, P
   const int item = wu.x;
   const int rb = wu.y;
   const int4 it = ws.items[item];
-  const int e = it.x, row0 = it.y, nrows = it.z;
+  const uint8_t* wb = expert_base(L, it);
+  const int row0 = it.y, nrows = it.z;
   if (threadIdx.x < nrows) {
     const int t = ws.row_tok[row0 + threadIdx.x];
     s_off[threadIdx.x] = static_cast<uint32_t>(t) * static_cast<uint32_t>(L.H) * 2u;   // bytes
@@ -620,10 +632,10 @@ __global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, P
   __syncthreads();
   const int rt = rb * kGemmWaves + static_cast<int>(threadIdx.x >> 6);
   switch ((nrows + 15) / 16) {
-    case 1: gateup_body<1, kGateupRing, KTC>(L, ws, T, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
-    case 2: gateup_body<2, kGateupRing, KTC>(L, ws, T, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
-    case 3: gateup_body<3, kGateupRing, KTC>(L, ws, T, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
-    default: gateup_body<4, kGateupRing, KTC>(L, ws, T, e, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+    case 1: gateup_body<1, kGateupRing, KTC>(L, ws, T, wb, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+    case 2: gateup_body<2, kGateupRing, KTC>(L, ws, T, wb, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+    case 3: gateup_body<3, kGateupRing, KTC>(L, ws, T, wb, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+    default: gateup_body<4, kGateupRing, KTC>(L, ws, T, wb, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
   }
 }
 
@@ -649,7 +661,7 @@ __device__ __forceinline__ void down_ktile(const u32x4 (&b)[2 * kDownRTW], const
 }
 
 template <int NMT, int RING, int KTC>
-__device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& ws, int e, int row0,
+__device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& ws, const uint8_t* wb, int row0,
                                           int nrows, int rt0, _Float16 (*s_a)[kATileHalves],
                                           int* s_erow, int8_t* s_hx) {
   const int H = L.H, I = L.I;
@@ -659,7 +671,7 @@ __device__ __forceinline__ void down_body(const LayerArgs& L, const PrefillWs& w
   const int RTI = I / kTileRows;
   const uint32_t mat = static_cast<uint32_t>(
       __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(I) * H * 5 / 16)));
-  const __amdgpu_buffer_rsrc_t rs = expert_rsrc(expert_base(L, e), 3 * mat);
+  const __amdgpu_buffer_rsrc_t rs = expert_rsrc(wb, 3 * mat);
   const uint32_t down = 2 * mat + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(rt0)) * KT * kTileBytes;
   constexpr int NB = 2 * kDownRTW;   // codes and scales of each row tile
   auto load_b = [&](u32x4 (&b)[NB], int kt) {
@@ -784,13 +796,14 @@ __global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, Pre
   const int item = wu.x;
   const int rb = wu.y;
   const int4 it = ws.items[item];
-  const int e = it.x, row0 = it.y, nrows = it.z;
+  const uint8_t* wb = expert_base(L, it);
+  const int row0 = it.y, nrows = it.z;
   const int rt0 = (rb * kGemmWaves + static_cast<int>(threadIdx.x >> 6)) * kDownRTW;
   switch ((nrows + 15) / 16) {
-    case 1: down_body<1, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow, s_hx); break;
-    case 2: down_body<2, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow, s_hx); break;
-    case 3: down_body<3, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow, s_hx); break;
-    default: down_body<4, kDownRing, KTC>(L, ws, e, row0, nrows, rt0, s_a, s_erow, s_hx); break;
+    case 1: down_body<1, kDownRing, KTC>(L, ws, wb, row0, nrows, rt0, s_a, s_erow, s_hx); break;
+    case 2: down_body<2, kDownRing, KTC>(L, ws, wb, row0, nrows, rt0, s_a, s_erow, s_hx); break;
+    case 3: down_body<3, kDownRing, KTC>(L, ws, wb, row0, nrows, rt0, s_a, s_erow, s_hx); break;
+    default: down_body<4, kDownRing, KTC>(L, ws, wb, row0, nrows, rt0, s_a, s_erow, s_hx); break;
   }
 }
 

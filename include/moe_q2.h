@@ -19,14 +19,18 @@
  *                              or 32768 tokens), grouped by expert
  * and moe_expert_forward_decode_routed does the first two for decode in one
  * call; moe_route_topk_gemv computes the router logits themselves and their
- * top-k for decode.
+ * top-k for decode.  The residency tier (moe_expert_usage_update,
+ * moe_residency_plan, moe_residency_apply and the *_tiered forward calls)
+ * keeps the most used experts in device slots and reads the others from an
+ * arena in device or pinned host memory.
  *
  * Conventions for every entry point
  *   - Pointers marked [device] are device addresses (hipMalloc'd memory or
  *     torch tensors); [host] pointers are read during the call only.
  *   - The caller owns all memory, including `workspace`.  The library never
  *     allocates, frees or synchronises, and never reads device data on the
- *     host.  Each call only enqueues kernels on `stream` (a hipStream_t passed
+ *     host (the tiered calls only ask the runtime what kind of memory the
+ *     arena is).  Each call only enqueues kernels on `stream` (a hipStream_t passed
  *     as void*, NULL = the null stream), in stream order.
  *   - Every argument is validated before anything is enqueued: a non-zero
  *     status means nothing was enqueued (except MOE_ERR_HIP, which reports a
@@ -241,6 +245,113 @@ int moe_expert_forward_prefill(const moe_q2_layer* layer, const void* x, int32_t
                                const void* residual, void* out, int32_t out_dtype,
                                uint32_t flags, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * Residency tier: the hottest experts in device memory, the rest read from
+ * an arena that holds all of them ("RTX PRO 4500 单卡跑 125B MoE",
+ * lcz.me/topic/2169, section 最重要机制: the table of what sits in VRAM,
+ * RAM and SSD, and items 1 and 2 -- experts the GPU does not hold are
+ * computed where they are, and the resident set is re-chosen every few
+ * rounds from the experts the conversation uses most).  On MI355X the GPU
+ * itself reads a non-resident expert: from device memory, or from pinned
+ * host memory mapped into the device's address space (hipHostMalloc), over
+ * PCIe; no CPU pipeline is involved.
+ *
+ * The layer descriptor of a tiered call:
+ */
+typedef struct {
+  const void* slots;      /* [device] S resident experts: slot s at slots + s*expert_stride;
+                             256-byte aligned (may be NULL when S = 0)          */
+  const int32_t* slot_of; /* [device] int32 [E]: the slot holding expert e, or -1; a
+                             value outside [0, S) reads e from the arena         */
+  const void* arena;      /* every expert: e at arena + e*expert_stride; device memory or
+                             mapped pinned host memory (validated), 256-B aligned */
+  const void* shared;     /* [device] the shared expert, or NULL                 */
+  int64_t expert_stride;  /* bytes, >= 3*I*H*5/16, multiple of 256               */
+  int32_t num_slots;      /* S, 0..E                                            */
+  int32_t num_experts;    /* E, 1..1024                                          */
+  int32_t hidden;         /* H, multiple of 256, <= 8192                         */
+  int32_t inter;          /* I, multiple of 256, <= 8192                         */
+} moe_q2_tiered_layer;
+
+/*
+ * Usage histogram: counts[e] += the number of entries of ids[0..n) equal to
+ * e (entries outside [0, E) are skipped).  Integer atomics: the result does
+ * not depend on order.  The caller clears counts to start a window.
+ *   ids    [device] int32 [n] (e.g. topk_ids of a prefill chunk), n >= 0.
+ *   counts [device] uint64 [E], 8-byte aligned.
+ * Errors: INVALID_ARG (NULL pointers with n > 0, E < 1, n > 2^31 - 1),
+ * UNSUPPORTED (E > 1024).
+ */
+int moe_expert_usage_update(const int32_t* ids, int64_t n, int32_t E, uint64_t* counts, void* stream);
+
+/*
+ * Residency plan (host only; no device memory, nothing enqueued): the S
+ * experts to hold are those with the S largest counts, equal counts going
+ * to the lower expert id.  A chosen expert already in a slot keeps it; the
+ * other chosen experts fill the remaining slots, lowest slot first, in
+ * ascending expert id.
+ *   counts             [host] uint64 [E] usage counts.
+ *   expert_of_slot     [host] int32 [S] current occupant of each slot, -1 =
+ *                      empty; distinct experts in [0, E).
+ *   new_expert_of_slot [host] int32 [S] out: the plan (may alias
+ *                      expert_of_slot only if it is not needed afterwards).
+ *   slot_of            [host] int32 [E] out, or NULL: slot of each expert
+ *                      under the plan, -1 if not held.
+ *   n_changed          [host] out, or NULL: slots whose occupant changes.
+ * Errors: INVALID_ARG (NULL counts or outputs with S > 0, E < 1, S outside
+ * 0..E, an occupant out of range or held twice), UNSUPPORTED (E > 1024).
+ */
+int moe_residency_plan(const uint64_t* counts, int32_t E, int32_t S, const int32_t* expert_of_slot,
+                       int32_t* new_expert_of_slot, int32_t* slot_of, int32_t* n_changed);
+
+/*
+ * Move the tier from one plan to the next on `stream`: for each slot whose
+ * occupant changes to an expert, its expert_stride bytes are copied from the
+ * arena (hipMemcpyAsync), then the device map slot_of is updated for the
+ * experts that leave and enter (a small kernel whose changes travel as
+ * kernel arguments, so the host arrays are read during the call only).
+ *   arena, expert_stride, E, S   as in moe_q2_tiered_layer.
+ *   old_expert_of_slot [host] int32 [S]: the occupants slot_of describes now
+ *                      (all -1, with slot_of all -1, before the first plan).
+ *   new_expert_of_slot [host] int32 [S]: the occupants to move to; an expert
+ *                      held in both keeps its slot (as moe_residency_plan
+ *                      guarantees).
+ *   slots   [device] the S slots (written).  slot_of [device] int32 [E].
+ * Calls that read the tier must be ordered after this one (the same stream,
+ * or an event); calls ordered before it read the old state.
+ * Errors: INVALID_ARG (NULL pointers, bad alignment or stride, S outside
+ * 0..E, occupants out of range or repeated, an expert that changes slot),
+ * UNSUPPORTED (E > 1024), HIP (a copy or launch failed).
+ */
+int moe_residency_apply(const void* arena, int64_t expert_stride, int32_t E, int32_t S,
+                        const int32_t* old_expert_of_slot, const int32_t* new_expert_of_slot,
+                        void* slots, int32_t* slot_of, void* stream);
+
+/*
+ * moe_expert_forward_decode_routed and moe_expert_forward_prefill on a
+ * tiered layer: each selected expert is read from its slot, or from the
+ * arena when slot_of gives none.  The outputs are those of the untiered
+ * calls on the arena's experts, bit for bit, whatever the plan.
+ *   usage_counts [device] uint64 [E] or NULL (decode only): += the pairs
+ *                routed to each expert, as moe_expert_usage_update on
+ *                topk_ids, inside the expert kernels (no extra launch).
+ * Errors: as for the untiered calls, plus INVALID_ARG for a NULL arena or
+ * slot_of, S outside 0..E, NULL slots with S > 0, an arena that is neither
+ * device memory nor pinned host memory, or misaligned pointers.
+ */
+int moe_expert_forward_decode_tiered(const moe_q2_tiered_layer* layer, const void* x, int32_t x_dtype,
+                                     int32_t T, const float* logits, int32_t k, int32_t* topk_ids,
+                                     float* topk_w, const void* residual, void* out, int32_t out_dtype,
+                                     uint32_t flags, uint64_t* usage_counts, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+int moe_expert_forward_prefill_tiered(const moe_q2_tiered_layer* layer, const void* x, int32_t x_dtype,
+                                      int32_t T, const int32_t* topk_ids, const float* topk_w, int32_t k,
+                                      const int32_t* counts, const int32_t* offsets,
+                                      const int32_t* sorted_pairs, const int32_t* pair_pos,
+                                      const void* residual, void* out, int32_t out_dtype,
+                                      uint32_t flags, void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /* Text of a status code; detail of the last error on this thread. */
 const char* moe_status_string(int status);

@@ -122,6 +122,24 @@ def forward(lib, which, **kw):
              ids=FAKE, w=FAKE, k=4, res=None, out=FAKE + (1 << 34), od=0, flags=0, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     L = _Layer(a["experts"], a["shared"], a["stride"], a["E"], a["H"], a["I"])
+    if which.endswith("tiered"):
+        from bit_quantized_expert_router_amd.binding import _TieredLayer
+        TL = _TieredLayer(a.get("slots", FAKE + (1 << 35)), a.get("slot_of", FAKE), a["experts"], a["shared"],
+                          a["stride"], a.get("S", 8), a["E"], a["H"], a["I"])
+        if which == "decode_tiered":
+            return lib.moe_expert_forward_decode_tiered(C.byref(TL), C.c_void_p(a["x"]), a["xd"], a["T"],
+                                                        C.c_void_p(a.get("logits", FAKE)), a["k"],
+                                                        C.c_void_p(a["ids"]), C.c_void_p(a["w"]),
+                                                        C.c_void_p(a["res"]), C.c_void_p(a["out"]), a["od"],
+                                                        a["flags"], C.c_void_p(a.get("usage")),
+                                                        C.c_void_p(a["ws"]), a["wsb"], None)
+        return lib.moe_expert_forward_prefill_tiered(C.byref(TL), C.c_void_p(a["x"]), a["xd"], a["T"],
+                                                     C.c_void_p(a["ids"]), C.c_void_p(a["w"]), a["k"],
+                                                     C.c_void_p(a.get("counts", FAKE)),
+                                                     C.c_void_p(a.get("offsets", FAKE)),
+                                                     C.c_void_p(a.get("sp", FAKE)), C.c_void_p(a.get("pp", FAKE)),
+                                                     C.c_void_p(a["res"]), C.c_void_p(a["out"]), a["od"],
+                                                     a["flags"], C.c_void_p(a["ws"]), a["wsb"], None)
     if which == "routed":
         return lib.moe_expert_forward_decode_routed(C.byref(L), C.c_void_p(a["x"]), a["xd"], a["T"],
                                                     C.c_void_p(a.get("logits", FAKE)), a["k"],
@@ -142,7 +160,7 @@ def forward(lib, which, **kw):
                                           a["flags"], C.c_void_p(a["ws"]), a["wsb"], None)
 
 
-@pytest.mark.parametrize("which", ["decode", "routed", "prefill"])
+@pytest.mark.parametrize("which", ["decode", "routed", "prefill", "decode_tiered", "prefill_tiered"])
 def test_forward_validation(lib, which):
     assert forward(lib, which, experts=None) == -1
     assert forward(lib, which, x=None) == -1
@@ -171,16 +189,81 @@ def test_forward_validation(lib, which):
     # residual partly over out (residual == out itself is allowed)
     assert forward(lib, which, res=FAKE + (1 << 34) + 1024) == -1
     assert b"residual" in lib.moe_last_error()
-    if which in ("decode", "routed"):
+    if which in ("decode", "routed", "decode_tiered"):
         assert forward(lib, which, T=9) == -2
-    if which == "routed":
+    if which in ("routed", "decode_tiered"):
         assert forward(lib, which, logits=None) == -1
         assert forward(lib, which, ids=None) == -1            # only one routing output
         assert forward(lib, which, logits=FAKE + 2) == -1     # unaligned
         assert forward(lib, which, ids=None, w=None, wsb=100) == -3   # outputs are optional
-    elif which == "prefill":
+    elif which in ("prefill", "prefill_tiered"):
         assert forward(lib, which, counts=None) == -1
         assert forward(lib, which, T=(1 << 17) + 1) == -2
+
+
+@pytest.mark.parametrize("which", ["decode_tiered", "prefill_tiered"])
+def test_tier_validation(lib, which):
+    """The tier's own arguments are checked after the untiered ones and
+    before the arena's memory type is looked up."""
+    assert forward(lib, which, experts=None) == -1       # the arena
+    assert forward(lib, which, slot_of=None) == -1
+    assert b"slot_of" in lib.moe_last_error()
+    assert forward(lib, which, slot_of=FAKE + 2) == -1   # unaligned
+    assert forward(lib, which, S=-1) == -1
+    assert forward(lib, which, S=65) == -1               # more slots than experts
+    assert b"num_slots" in lib.moe_last_error()
+    assert forward(lib, which, slots=None) == -1
+    assert forward(lib, which, slots=FAKE + 128) == -1   # unaligned slots
+    if which == "decode_tiered":
+        assert forward(lib, which, usage=FAKE + 4) == -1
+        assert b"usage_counts" in lib.moe_last_error()
+
+
+def test_usage_update_validation(lib):
+    f = lib.moe_expert_usage_update
+    assert f(C.c_void_p(FAKE), 8, 0, C.c_void_p(FAKE), None) == -1
+    assert f(C.c_void_p(FAKE), 8, 2000, C.c_void_p(FAKE), None) == -2
+    assert f(C.c_void_p(FAKE), -1, 64, C.c_void_p(FAKE), None) == -1
+    assert f(C.c_void_p(FAKE), 1 << 31, 64, C.c_void_p(FAKE), None) == -1
+    assert f(None, 8, 64, C.c_void_p(FAKE), None) == -1
+    assert f(C.c_void_p(FAKE), 8, 64, None, None) == -1
+    assert f(C.c_void_p(FAKE + 2), 8, 64, C.c_void_p(FAKE), None) == -1
+    assert f(C.c_void_p(FAKE), 8, 64, C.c_void_p(FAKE + 4), None) == -1
+    assert f(None, 0, 64, None, None) == 0               # nothing to count: no launch
+
+
+def apply(lib, **kw):
+    import numpy as np
+    a = dict(arena=FAKE, stride=245760, E=8, S=3, old=[-1, -1, -1], new=[1, 2, 3], slots=FAKE + (1 << 35),
+             slot_of=FAKE + (1 << 36))
+    a.update(kw)
+    old = None if a["old"] is None else np.asarray(a["old"], dtype=np.int32)
+    new = None if a["new"] is None else np.asarray(a["new"], dtype=np.int32)
+    return lib.moe_residency_apply(C.c_void_p(a["arena"]), a["stride"], a["E"], a["S"],
+                                   old.ctypes.data_as(C.c_void_p) if a["old"] is not None else None,
+                                   new.ctypes.data_as(C.c_void_p) if a["new"] is not None else None,
+                                   C.c_void_p(a["slots"]), C.c_void_p(a["slot_of"]), None)
+
+
+def test_residency_apply_validation(lib):
+    assert apply(lib, E=0) == -1
+    assert apply(lib, E=2000) == -2
+    assert apply(lib, S=9) == -1
+    assert apply(lib, arena=None) == -1
+    assert apply(lib, slot_of=None) == -1
+    assert apply(lib, slots=None) == -1
+    assert apply(lib, old=None) == -1
+    assert apply(lib, stride=1000) == -1
+    assert apply(lib, arena=FAKE + 16) == -1
+    assert apply(lib, slot_of=FAKE + 2) == -1
+    assert apply(lib, new=[1, 1, 3]) == -1               # an expert twice
+    assert b"twice" in lib.moe_last_error()
+    assert apply(lib, new=[1, 8, 3]) == -1               # not an expert
+    assert apply(lib, old=[-2, -1, -1]) == -1
+    assert apply(lib, old=[2, -1, -1], new=[1, 2, 3]) == -1   # expert 2 changes slot
+    assert b"moves" in lib.moe_last_error()
+    # S = 0 with no arrays is valid and enqueues nothing
+    assert apply(lib, S=0, old=None, new=None, slots=None) == 0
 
 
 def test_profile_hooks_host_only(lib):
