@@ -451,19 +451,28 @@ struct HTile {
   }
 };
 
-// One K tile of the gate/up product for NMT 16-row M tiles.
-template <int NMT>
-__device__ __forceinline__ void gateup_ktile(const u32x4 (&b)[4], const _Float16* abuf, int lane,
-                                             f32x4 (&acc_g)[4], f32x4 (&acc_u)[4]) {
+// One K tile of the gate/up product for NMT 16-row M tiles and RTW row
+// tiles of gate and of up: each activation fragment read from LDS feeds
+// 2 * RTW MFMAs.
+template <int NMT, int RTW>
+__device__ __forceinline__ void gateup_ktile(const u32x4 (&b)[4 * RTW], const _Float16* abuf, int lane,
+                                             f32x4 (&acc_g)[RTW][4], f32x4 (&acc_u)[RTW][4]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const f16x8 bg = tile_block_weights(b[0], b[1], j);
-    const f16x8 bu = tile_block_weights(b[2], b[3], j);
+    f16x8 bg[RTW], bu[RTW];
+#pragma unroll
+    for (int q = 0; q < RTW; ++q) {
+      bg[q] = tile_block_weights(b[4 * q], b[4 * q + 1], j);
+      bu[q] = tile_block_weights(b[4 * q + 2], b[4 * q + 3], j);
+    }
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       const f16x8 a = a_frag(abuf, j, mt, lane);
-      acc_g[mt] = mfma16(a, bg, acc_g[mt]);
-      acc_u[mt] = mfma16(a, bu, acc_u[mt]);
+#pragma unroll
+      for (int q = 0; q < RTW; ++q) {
+        acc_g[q][mt] = mfma16(a, bg[q], acc_g[q][mt]);
+        acc_u[q][mt] = mfma16(a, bu[q], acc_u[q][mt]);
+      }
     }
   }
 }
@@ -543,9 +552,15 @@ __device__ __forceinline__ void k_loop_fixed(u32x4 (&b)[RING][NB], LoadB load_b,
 }
 
 // ------------------------------------------------------------------ gate/up --
-template <int NMT, int RING, int KTC>
+// Row tiles of gate (and of up) per wave for a chunk of T tokens.
+inline int gateup_row_tiles_per_wave(int T) { return T > 2 * kSizeOrderMaxTokens ? 2 : 1; }
+
+
+// Wave w of row block rb takes the RTW row tiles rt0 .. rt0 + RTW - 1 of
+// gate and of up, rt0 = (rb * kGemmWaves + w) * RTW.
+template <int NMT, int RING, int KTC, int RTW>
 __device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs& ws, int T, const uint8_t* wb,
-                                            int row0, int nrows, int rt,
+                                            int row0, int nrows, int rt0,
                                             _Float16 (*s_a)[kATileHalves], const uint32_t* s_off,
                                             const float* s_w, const float* s_u) {
   const int H = L.H, I = L.I;
@@ -555,15 +570,19 @@ __device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs&
   const uint32_t mat = static_cast<uint32_t>(
       __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(I) * H * 5 / 16)));
   const __amdgpu_buffer_rsrc_t rs = expert_rsrc(wb, 3 * mat);
-  const uint32_t gate = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(rt)) * KT * kTileBytes;
-  auto load_b = [&](u32x4 (&b)[4], int kt) {
+  const uint32_t gate = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(rt0)) * KT * kTileBytes;
+  const uint32_t tile_row = static_cast<uint32_t>(KT) * kTileBytes;     // one row tile, all K tiles
+  auto load_b = [&](u32x4 (&b)[4 * RTW], int kt) {
     const uint32_t o = gate + static_cast<uint32_t>(min(kt, KT - 1)) * kTileBytes;
-    b[0] = load_codes(rs, o, lane);
-    b[1] = load_scales(rs, o, lane);
-    b[2] = load_codes(rs, o + mat, lane);
-    b[3] = load_scales(rs, o + mat, lane);
+#pragma unroll
+    for (int q = 0; q < RTW; ++q) {
+      b[4 * q] = load_codes(rs, o + q * tile_row, lane);
+      b[4 * q + 1] = load_scales(rs, o + q * tile_row, lane);
+      b[4 * q + 2] = load_codes(rs, o + q * tile_row + mat, lane);
+      b[4 * q + 3] = load_scales(rs, o + q * tile_row + mat, lane);
+    }
   };
-  u32x4 b[RING][4];
+  u32x4 b[RING][4 * RTW];
 #pragma unroll
   for (int u = 0; u < RING; ++u) load_b(b[u], u);   // clamped: no tile past the last is read
   ATile<NMT> A;
@@ -575,47 +594,54 @@ __device__ __forceinline__ void gateup_body(const LayerArgs& L, const PrefillWs&
   A.template store<0>(s_a[0], 0);
   __syncthreads();
 
-  f32x4 acc_g[4], acc_u[4];
+  f32x4 acc_g[RTW][4], acc_u[RTW][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { acc_g[i] = f32x4{0.f, 0.f, 0.f, 0.f}; acc_u[i] = acc_g[i]; }
+  for (int q = 0; q < RTW; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { acc_g[q][i] = f32x4{0.f, 0.f, 0.f, 0.f}; acc_u[q][i] = acc_g[q][i]; }
 
-  auto mul = [&](const u32x4 (&bs)[4], const _Float16* abuf) {
-    gateup_ktile<NMT>(bs, abuf, lane, acc_g, acc_u);
+  auto mul = [&](const u32x4 (&bs)[4 * RTW], const _Float16* abuf) {
+    gateup_ktile<NMT, RTW>(bs, abuf, lane, acc_g, acc_u);
   };
   if constexpr (KTC > 0)
     k_loop_fixed<KTC, RING>(b, load_b, A, s_a, mul, std::make_integer_sequence<int, KTC>{});
   else
     k_loop<RING>(KT, b, load_b, A, s_a, mul);
 
-  // h rows of this wave's 16-row tile of I: one exponent per (row, tile)
-  const int col = rt * 16 + m;
+  // h rows of this wave's 16-row tiles of I: one exponent per (row, tile)
   const int RTI = I / kTileRows;
 #pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) {
+  for (int q = 0; q < RTW; ++q) {
+    const int rt = rt0 + q;
+    const int col = rt * 16 + m;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rl = mt * 16 + 4 * g + r;            // uniform in each 16-lane row
-      const bool ok = rl < nrows;
-      const float u = ok ? s_u[rl] : 1.0f;
-      const float h = ok ? s_w[rl] * silu(acc_g[mt][r] * u) * (acc_u[mt][r] * u) : 0.0f;
-      const int e = block_exponent(row16_max(fabsf(h)));
-      if (ok) {
-        ws.h[static_cast<size_t>(row0 + rl) * I + col] = static_cast<_Float16>(ldexpf(h, -e));
-        if (m == 0) ws.hexp[static_cast<size_t>(row0 + rl) * RTI + rt] = static_cast<int8_t>(e);
+    for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = mt * 16 + 4 * g + r;            // uniform in each 16-lane row
+        const bool ok = rl < nrows;
+        const float u = ok ? s_u[rl] : 1.0f;
+        const float h = ok ? s_w[rl] * silu(acc_g[q][mt][r] * u) * (acc_u[q][mt][r] * u) : 0.0f;
+        const int e = block_exponent(row16_max(fabsf(h)));
+        if (ok) {
+          ws.h[static_cast<size_t>(row0 + rl) * I + col] = static_cast<_Float16>(ldexpf(h, -e));
+          if (m == 0) ws.hexp[static_cast<size_t>(row0 + rl) * RTI + rt] = static_cast<int8_t>(e);
+        }
       }
     }
   }
 }
 
 // KTC: the number of 256-column K tiles (H / 256) when fixed at compile
-// time, 0 for the runtime loop.
-template <int KTC>
+// time, 0 for the runtime loop.  RTW: row tiles of gate and of up per wave
+// (a block covers 16 * kGemmWaves * RTW rows of I).
+template <int KTC, int RTW>
 __global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, PrefillWs ws, int T) {
   __shared__ __align__(16) _Float16 s_a[2][kATileHalves];
   __shared__ uint32_t s_off[kGroupRows];
   __shared__ float s_w[kGroupRows];
   __shared__ float s_u[kGroupRows];
-  const int RB = L.I / kGateupRowsPerBlock;
+  const int RB = L.I / (kGateupRowsPerBlock * RTW);
   const int2 wu = work_unit(blockIdx.x, ws.hdr, RB);
   if (wu.x < 0) return;
   const int item = wu.x;
@@ -630,12 +656,12 @@ __global__ __launch_bounds__(kThreads) void prefill_gateup_kernel(LayerArgs L, P
     s_u[threadIdx.x] = ws.unscale[t];
   }
   __syncthreads();
-  const int rt = rb * kGemmWaves + static_cast<int>(threadIdx.x >> 6);
+  const int rt0 = (rb * kGemmWaves + static_cast<int>(threadIdx.x >> 6)) * RTW;
   switch ((nrows + 15) / 16) {
-    case 1: gateup_body<1, kGateupRing, KTC>(L, ws, T, wb, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
-    case 2: gateup_body<2, kGateupRing, KTC>(L, ws, T, wb, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
-    case 3: gateup_body<3, kGateupRing, KTC>(L, ws, T, wb, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
-    default: gateup_body<4, kGateupRing, KTC>(L, ws, T, wb, row0, nrows, rt, s_a, s_off, s_w, s_u); break;
+    case 1: gateup_body<1, kGateupRing, KTC, RTW>(L, ws, T, wb, row0, nrows, rt0, s_a, s_off, s_w, s_u); break;
+    case 2: gateup_body<2, kGateupRing, KTC, RTW>(L, ws, T, wb, row0, nrows, rt0, s_a, s_off, s_w, s_u); break;
+    case 3: gateup_body<3, kGateupRing, KTC, RTW>(L, ws, T, wb, row0, nrows, rt0, s_a, s_off, s_w, s_u); break;
+    default: gateup_body<4, kGateupRing, KTC, RTW>(L, ws, T, wb, row0, nrows, rt0, s_a, s_off, s_w, s_u); break;
   }
 }
 
@@ -807,6 +833,193 @@ __global__ __launch_bounds__(kThreads) void prefill_down_kernel(LayerArgs L, Pre
   }
 }
 
+// --------------------------------------------------------- down, A resident --
+// For I <= 768 (at most three 256-column K tiles of h): the block stages its
+// item's h rows, rescaled to the row exponents, into LDS once and then runs
+// NCB chunks of 256 output rows of H one after the other (wave w: the two
+// 16-row tiles 2 (8 c + w) and 2 (8 c + w) + 1 of chunk c).  With A resident
+// the chunk loop needs no block barrier: a wave issues the weight loads of
+// chunk i + 2 as soon as chunk i's registers are free, and its epilogue goes
+// through a transposition buffer of its own.  So one staging of A, and one
+// exponent table, serve NCB times the work of the per-chunk kernel above.
+constexpr int kDownResMaxKT = 3;
+constexpr int kDownChunkRows = 16 * kDownRTW * kGemmWaves;   // 256
+static_assert(kDownRTW == 2, "two row tiles per wave and chunk");
+
+// f(integral_constant<int, i>) for i = IS... in order.
+template <typename F, int... IS>
+__device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int, IS...>) {
+  (f(std::integral_constant<int, IS>{}), ...);
+}
+
+// Row r, column c (0..15) of a wave's 64 x 16 fp32 transposition buffer:
+// the two 8-float halves of a row swap places every four rows, which spreads
+// an accumulator write (rows 4g + r of 16 columns) over both halves.
+__device__ __forceinline__ int res_at(int row, int col) {
+  return row * 16 + ((((col >> 3) ^ (row >> 2)) & 1) << 3) + (col & 7);
+}
+
+template <int NMT, int KT, int NCB>
+__device__ __forceinline__ void down_res_body(const LayerArgs& L, const PrefillWs& ws, const uint8_t* wb,
+                                              int row0, int nrows, int c0, _Float16 (*s_a)[kATileHalves],
+                                              float* s_t, int* s_erow, int8_t* s_hx) {
+  const int H = L.H, I = L.I;                     // I == 256 * KT
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  constexpr int RTI = KT * (kTileCols / kTileRows);
+  const uint32_t mat = static_cast<uint32_t>(
+      __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(I) * H * 5 / 16)));
+  const __amdgpu_buffer_rsrc_t rs = expert_rsrc(wb, 3 * mat);
+  constexpr int NB = 2 * kDownRTW * KT;           // codes and scales of the wave's tiles, all K tiles
+  // the wave's two row tiles are consecutive, and so are their K tiles
+  auto load_chunk = [&](u32x4 (&b)[NB], int c) {
+    const uint32_t o = 2 * mat + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+                                     (c * kGemmWaves + w) * kDownRTW)) * KT * kTileBytes;
+#pragma unroll
+    for (int t = 0; t < kDownRTW * KT; ++t) {
+      b[2 * t] = load_codes(rs, o + t * kTileBytes, lane);
+      b[2 * t + 1] = load_scales(rs, o + t * kTileBytes, lane);
+    }
+  };
+  // requests in the order they are waited for: the item's tile exponents,
+  // the first two chunks' weights, the h fragments
+  const u32x4* ev_src = reinterpret_cast<const u32x4*>(
+      ws.hexp + static_cast<size_t>(row0 + min(static_cast<int>(threadIdx.x), nrows - 1)) * RTI);
+  u32x4 ev[KT];
+#pragma unroll
+  for (int q = 0; q < KT; ++q) ev[q] = ev_src[q];
+  u32x4 b[2][NB];
+  load_chunk(b[0], c0);
+  if constexpr (NCB > 1) load_chunk(b[1], c0 + 1);
+  const uint32_t row_bytes = static_cast<uint32_t>(I) * 2u;
+  const __amdgpu_buffer_rsrc_t hr = expert_rsrc(reinterpret_cast<const uint8_t*>(ws.h + static_cast<size_t>(row0) * I),
+                                                static_cast<uint32_t>(nrows) * row_bytes);
+  u32x4 ar[KT][NMT];           // fragment (kt, block j = w, M tile mt) of the item's h rows
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+      ar[kt][mt] = __builtin_amdgcn_raw_buffer_load_b128(
+          hr, static_cast<uint32_t>(min(mt * 16 + m, nrows - 1)) * row_bytes + 2u * static_cast<uint32_t>(32 * w + 8 * g),
+          static_cast<uint32_t>(kt) * (2 * kTileCols), 0);
+  // the tile exponents into LDS, tile-major, and E_row, each row's largest
+  if (static_cast<int>(threadIdx.x) < nrows) {
+    const int row = threadIdx.x;
+    int mx = kZeroExp;
+#pragma unroll
+    for (int q = 0; q < KT; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+          const int ex = static_cast<int8_t>(ev[q][c] >> (8 * sb));
+          s_hx[(16 * q + 4 * c + sb) * kGroupRows + row] = static_cast<int8_t>(ex);
+          mx = max(mx, ex);
+        }
+    s_erow[row] = mx;
+  }
+  __syncthreads();
+  // every fragment rescaled from its tile's exponent to its row's; rows at or
+  // beyond nrows repeat the last row with stale exponents and are never stored
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int d = static_cast<int>(s_hx[(kt * 16 + 2 * w + (g >> 1)) * kGroupRows + mt * 16 + m]) -
+                    s_erow[mt * 16 + m];
+      *reinterpret_cast<f16x8*>(&s_a[kt][((4 * w + mt) * 64 + lane) * 8]) =
+          scale_pow2(__builtin_bit_cast(f16x8, ar[kt][mt]), min(d, 0));
+    }
+  __syncthreads();
+
+  float* tb = s_t + w * (kGroupRows * 16);
+  const int NYG = H / kYGroup;
+  auto chunk = [&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const u32x4 (&bs)[NB] = b[i & 1];
+    f32x4 acc[kDownRTW][4];
+#pragma unroll
+    for (int q = 0; q < kDownRTW; ++q)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        f16x8 bq[kDownRTW];
+#pragma unroll
+        for (int q = 0; q < kDownRTW; ++q) bq[q] = tile_block_weights(bs[2 * (q * KT + kt)], bs[2 * (q * KT + kt) + 1], j);
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) {
+          const f16x8 a = a_frag(s_a[kt], j, mt, lane);
+#pragma unroll
+          for (int q = 0; q < kDownRTW; ++q) acc[q][mt] = mfma16(a, bq[q], acc[q][mt]);
+        }
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (i + 2 < NCB) load_chunk(b[i & 1], c0 + i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    // y = acc * 2^E_row, one exponent per (row, 8 columns), one row tile at
+    // a time through the wave's buffer: a lane then holds 8 consecutive
+    // columns of one row
+    const int rt0 = ((c0 + i) * kGemmWaves + w) * kDownRTW;
+#pragma unroll
+    for (int q = 0; q < kDownRTW; ++q) {
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tb[res_at(mt * 16 + 4 * g + r, m)] = acc[q][mt][r];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int st = 0; st < (NMT * 16 + 31) / 32; ++st) {      // 32 rows x 2 halves per step
+        const int rl = st * 32 + (lane >> 1), ch = lane & 1;
+        if (rl < nrows && rl < NMT * 16) {
+          const f32x4* src4 = reinterpret_cast<const f32x4*>(tb + res_at(rl, 8 * ch));
+          const f32x4 lo = src4[0], hi = src4[1];
+          float mx = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(lo[e]), fabsf(hi[e])));
+          const int er = s_erow[rl];
+          const int f = block_exponent(mx);
+          const int F = f == kZeroExp ? kZeroExp : max(-126, min(127, f + er));
+          f16x8 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] = static_cast<_Float16>(ldexpf(lo[e], er - F));
+            o[4 + e] = static_cast<_Float16>(ldexpf(hi[e], er - F));
+          }
+          const int col = (rt0 + q) * 16 + ch * 8;
+          *reinterpret_cast<f16x8*>(ws.y + static_cast<size_t>(row0 + rl) * H + col) = o;
+          ws.yexp[static_cast<size_t>(row0 + rl) * NYG + col / kYGroup] = static_cast<int8_t>(F);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  };
+  for_each_index(chunk, std::make_integer_sequence<int, NCB>{});
+}
+
+template <int KT, int NCB>
+__global__ __launch_bounds__(kThreads) void prefill_down_res_kernel(LayerArgs L, PrefillWs ws) {
+  __shared__ __align__(16) _Float16 s_a[KT][kATileHalves];
+  __shared__ __align__(16) float s_t[kGemmWaves * kGroupRows * 16];
+  __shared__ int8_t s_hx[kGroupRows * KT * (kTileCols / kTileRows)];
+  __shared__ int s_erow[kGroupRows];
+  const int RB = L.H / (kDownChunkRows * NCB);
+  const int2 wu = work_unit(blockIdx.x, ws.hdr, RB);
+  if (wu.x < 0) return;
+  const int4 it = ws.items[wu.x];
+  const uint8_t* wb = expert_base(L, it);
+  const int row0 = it.y, nrows = it.z;
+  const int c0 = wu.y * NCB;
+  switch ((nrows + 15) / 16) {
+    case 1: down_res_body<1, KT, NCB>(L, ws, wb, row0, nrows, c0, s_a, s_t, s_erow, s_hx); break;
+    case 2: down_res_body<2, KT, NCB>(L, ws, wb, row0, nrows, c0, s_a, s_t, s_erow, s_hx); break;
+    case 3: down_res_body<3, KT, NCB>(L, ws, wb, row0, nrows, c0, s_a, s_t, s_erow, s_hx); break;
+    default: down_res_body<4, KT, NCB>(L, ws, wb, row0, nrows, c0, s_a, s_t, s_erow, s_hx); break;
+  }
+}
+
 // ------------------------------------------------------------------ combine --
 // One thread per (token, 8-column chunk): the token's k rows of y~ (and the
 // shared row) are all requested before the first is summed, in 16-byte loads,
@@ -919,19 +1132,51 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
   }
   if (e != hipSuccess) return e;
   {
-    const long long nb = (static_cast<long long>(grid_items) + 7) / 8 * 8 * (L.I / kGateupRowsPerBlock);
+    // long chunks (full 64-row items): two row tiles per wave, so each
+    // activation fragment read from LDS feeds four MFMAs; I is a multiple of
+    // 256, so the wider row block divides it
+    const int rtw = gateup_row_tiles_per_wave(T);
+    const long long nb = (static_cast<long long>(grid_items) + 7) / 8 * 8 * (L.I / (kGateupRowsPerBlock * rtw));
     const int grid = static_cast<int>(nb);
     const dim3 g(grid), b(kThreads);
-    switch (L.H / kTileCols) {   // fully unrolled K loops for the common widths
-      case 4: e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel<4>, g, b, 0, s, L, ws, T); break;
-      case 8: e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel<8>, g, b, 0, s, L, ws, T); break;
-      case 12: e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel<12>, g, b, 0, s, L, ws, T); break;
-      case 16: e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel<16>, g, b, 0, s, L, ws, T); break;
-      default: e = launch_kernel(K_PREFILL_GATEUP, prefill_gateup_kernel<0>, g, b, 0, s, L, ws, T); break;
-    }
+    auto gu = [&](auto ktc, auto rtwc) {
+      return launch_kernel(K_PREFILL_GATEUP,
+                           prefill_gateup_kernel<decltype(ktc)::value, decltype(rtwc)::value>, g, b, 0, s, L,
+                           ws, T);
+    };
+    auto by_width = [&](auto rtwc) {
+      switch (L.H / kTileCols) {   // fully unrolled K loops for the common widths
+        case 4: return gu(std::integral_constant<int, 4>{}, rtwc);
+        case 8: return gu(std::integral_constant<int, 8>{}, rtwc);
+        case 12: return gu(std::integral_constant<int, 12>{}, rtwc);
+        case 16: return gu(std::integral_constant<int, 16>{}, rtwc);
+        default: return gu(std::integral_constant<int, 0>{}, rtwc);
+      }
+    };
+    e = rtw == 2 ? by_width(std::integral_constant<int, 2>{}) : by_width(std::integral_constant<int, 1>{});
   }
   if (e != hipSuccess) return e;
-  {
+  const int ktd = L.I / kTileCols;
+  const int nc = L.H / kDownChunkRows;
+  if (ktd <= kDownResMaxKT) {
+    // A resident: chunks per block, 3 where they divide H / 256 (then 2, 1)
+    const int ncb = nc % 3 == 0 ? 3 : (nc % 2 == 0 ? 2 : 1);
+    const long long nb = (static_cast<long long>(grid_items) + 7) / 8 * 8 * (nc / ncb);
+    const dim3 g(static_cast<int>(nb)), b(kThreads);
+    auto dr = [&](auto ktc, auto ncbc) {
+      return launch_kernel(K_PREFILL_DOWN,
+                           prefill_down_res_kernel<decltype(ktc)::value, decltype(ncbc)::value>, g, b, 0, s,
+                           L, ws);
+    };
+    auto by_ncb = [&](auto ktc) {
+      if (ncb == 3) return dr(ktc, std::integral_constant<int, 3>{});
+      if (ncb == 2) return dr(ktc, std::integral_constant<int, 2>{});
+      return dr(ktc, std::integral_constant<int, 1>{});
+    };
+    if (ktd == 1) e = by_ncb(std::integral_constant<int, 1>{});
+    else if (ktd == 2) e = by_ncb(std::integral_constant<int, 2>{});
+    else e = by_ncb(std::integral_constant<int, 3>{});
+  } else {
     const long long nb = (static_cast<long long>(grid_items) + 7) / 8 * 8 * (L.H / kDownRowsPerBlock);
     const int grid = static_cast<int>(nb);
     const dim3 g(grid), b(kThreads);

@@ -410,6 +410,20 @@ def test_prefill_small(B, T):
     check_out(to_np(out), O.moe_layer(xv, ids, w, L.ref), f"prefill small T={T}")
 
 
+@pytest.mark.parametrize("I", [512, 1024, 2048])
+def test_prefill_intermediate_widths(B, I):
+    """Every token at I = 512 (h resident in LDS), 1024 and 2048 (h streamed
+    through the down GEMM tile by tile): 8 experts top-3, H 512."""
+    L = Layer(B, 13, 8, 512, I)
+    T = 90
+    rng = synth.rng_for(13, T, I)
+    xd, xv = synth.activations(rng, T, 512, "bf16")
+    lg = rng.standard_normal((T, 8)).astype(np.float32)
+    ids, w, r = route_both(B, lg, 3, True)
+    out = run_prefill(B, L, dev_x(xd, "bf16"), r)
+    check_out(to_np(out), O.moe_layer(xv, ids, w, L.ref), f"prefill I={I}")
+
+
 def test_prefill_small_config_all_tokens(B, layer_small):
     L = layer_small
     rng = synth.rng_for(0, 1, 0)
