@@ -50,8 +50,9 @@ def parse():
                     help="layers of the stacked decode/prefill runs (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
-    ap.add_argument("--counters", action="store_true",
-                    help="eager 1-token decode steps only (hardware-counter runs)")
+    ap.add_argument("--counters", nargs="?", const="decode1", default=None,
+                    choices=["decode1", "prefill1024", "prefill32768"],
+                    help="eager steps of one case only, 1-token decode by default (hardware-counter runs)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the device-ceiling microbenchmarks (moe_ceilings)")
     return ap.parse_args()
@@ -773,9 +774,11 @@ def cpu_baseline(seconds: float, prefill_tokens: int = 1024):
 
 
 def counters_run(args):
-    """Eager 1-token decode steps only (no graph capture, no measurement
-    hooks, no ceilings, no oracle), for hardware-counter collection: every
-    dispatch is an ordinary stream launch."""
+    """Eager steps of one case only (no graph capture, no measurement hooks,
+    no ceilings, no oracle), for hardware-counter collection: every dispatch
+    is an ordinary stream launch.  decode1: 1-token routed decode; prefill1024
+    / prefill32768: routing + prefill of one chunk (biased router logits,
+    resp. Zipf(1.1) ids) per step."""
     import torch
     from bit_quantized_expert_router_amd import binding as B
     from bit_quantized_expert_router_amd import synth
@@ -795,6 +798,25 @@ def counters_run(args):
         ex = synth.device_expert_blob(E, H, I, synth.torch_seed(1, l, 1), dev)
         sh = synth.device_expert_blob(1, H, I, synth.torch_seed(1, l, 2), dev)
         layers.append(B.Layer(ex, sh, E, H, I, synth.expert_stride(H, I)))
+    if args.counters != "decode1":
+        T = 1024 if args.counters == "prefill1024" else 32768
+        rng = synth.rng_for(3, 0, T)
+        xd, xv = synth.activations(rng, T, H, "bf16")
+        x = torch.from_numpy(xd.view(np.int16)).view(torch.bfloat16).to(dev)
+        lg = (synth.biased_logits(rng, synth.router_logits(rng, xv, E)) if T == 1024 else
+              synth.zipf_logits(rng, T, E))
+        r = B.route(torch.from_numpy(lg).to(dev), K, histogram=True)
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+        ws = B.workspace(B.MOE_OP_PREFILL, T, E, K, H, I, dev)
+        torch.cuda.synchronize()
+        t0 = time.time()
+        for i in range(args.steps):
+            B.moe_expert_forward_prefill(layers[i % len(layers)], x, r["topk_ids"], r["topk_w"], r["counts"],
+                                         r["offsets"], r["sorted_pairs"], r["pair_pos"], out, None, 0, ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": f"prefill_T{T} eager", "steps": args.steps,
+                          "wall_s": round(time.time() - t0, 4), "out_finite": bool(torch.isfinite(out).all().item())}))
+        return
     rng = synth.rng_for(1, 101, 0)
     n = args.steps
     xd, xv = synth.activations(rng, n, H, "bf16")
