@@ -859,10 +859,16 @@ __device__ __forceinline__ int res_at(int row, int col) {
   return row * 16 + ((((col >> 3) ^ (row >> 2)) & 1) << 3) + (col & 7);
 }
 
-template <int NMT, int KT, int NCB>
+// MT: M tiles the LDS holds (4, or 2 for half items); PF: chunks of weights
+// in flight per wave (2: the next-but-one chunk is requested as soon as a
+// chunk's registers are free; 1: the next chunk, fewer registers).
+template <int NMT, int KT, int NCB, int MT, int PF>
 __device__ __forceinline__ void down_res_body(const LayerArgs& L, const PrefillWs& ws, const uint8_t* wb,
-                                              int row0, int nrows, int c0, _Float16 (*s_a)[kATileHalves],
+                                              int row0, int nrows, int c0, _Float16* s_a,
                                               float* s_t, int* s_erow, int8_t* s_hx) {
+  static_assert(NMT <= MT, "an item part fits the LDS tiles");
+  constexpr int AH = 8 * MT * kFragHalves;        // halves of one K tile of A
+  constexpr int MR = MT * 16;                     // rows of the exponent table and the buffer
   const int H = L.H, I = L.I;                     // I == 256 * KT
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int m = lane & 15, g = lane >> 4;
@@ -882,15 +888,15 @@ __device__ __forceinline__ void down_res_body(const LayerArgs& L, const PrefillW
     }
   };
   // requests in the order they are waited for: the item's tile exponents,
-  // the first two chunks' weights, the h fragments
+  // the first PF chunks' weights, the h fragments
   const u32x4* ev_src = reinterpret_cast<const u32x4*>(
       ws.hexp + static_cast<size_t>(row0 + min(static_cast<int>(threadIdx.x), nrows - 1)) * RTI);
   u32x4 ev[KT];
 #pragma unroll
   for (int q = 0; q < KT; ++q) ev[q] = ev_src[q];
-  u32x4 b[2][NB];
+  u32x4 b[PF][NB];
   load_chunk(b[0], c0);
-  if constexpr (NCB > 1) load_chunk(b[1], c0 + 1);
+  if constexpr (PF > 1 && NCB > 1) load_chunk(b[1], c0 + 1);
   const uint32_t row_bytes = static_cast<uint32_t>(I) * 2u;
   const __amdgpu_buffer_rsrc_t hr = expert_rsrc(reinterpret_cast<const uint8_t*>(ws.h + static_cast<size_t>(row0) * I),
                                                 static_cast<uint32_t>(nrows) * row_bytes);
@@ -913,7 +919,7 @@ __device__ __forceinline__ void down_res_body(const LayerArgs& L, const PrefillW
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
           const int ex = static_cast<int8_t>(ev[q][c] >> (8 * sb));
-          s_hx[(16 * q + 4 * c + sb) * kGroupRows + row] = static_cast<int8_t>(ex);
+          s_hx[(16 * q + 4 * c + sb) * MR + row] = static_cast<int8_t>(ex);
           mx = max(mx, ex);
         }
     s_erow[row] = mx;
@@ -925,18 +931,18 @@ __device__ __forceinline__ void down_res_body(const LayerArgs& L, const PrefillW
   for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
-      const int d = static_cast<int>(s_hx[(kt * 16 + 2 * w + (g >> 1)) * kGroupRows + mt * 16 + m]) -
+      const int d = static_cast<int>(s_hx[(kt * 16 + 2 * w + (g >> 1)) * MR + mt * 16 + m]) -
                     s_erow[mt * 16 + m];
-      *reinterpret_cast<f16x8*>(&s_a[kt][((4 * w + mt) * 64 + lane) * 8]) =
+      *reinterpret_cast<f16x8*>(&s_a[kt * AH + ((MT * w + mt) * 64 + lane) * 8]) =
           scale_pow2(__builtin_bit_cast(f16x8, ar[kt][mt]), min(d, 0));
     }
   __syncthreads();
 
-  float* tb = s_t + w * (kGroupRows * 16);
+  float* tb = s_t + w * (MR * 16);
   const int NYG = H / kYGroup;
   auto chunk = [&](auto ic) {
     constexpr int i = decltype(ic)::value;
-    const u32x4 (&bs)[NB] = b[i & 1];
+    const u32x4 (&bs)[NB] = b[i % PF];
     f32x4 acc[kDownRTW][4];
 #pragma unroll
     for (int q = 0; q < kDownRTW; ++q)
@@ -951,13 +957,13 @@ __device__ __forceinline__ void down_res_body(const LayerArgs& L, const PrefillW
         for (int q = 0; q < kDownRTW; ++q) bq[q] = tile_block_weights(bs[2 * (q * KT + kt)], bs[2 * (q * KT + kt) + 1], j);
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) {
-          const f16x8 a = a_frag(s_a[kt], j, mt, lane);
+          const f16x8 a = *reinterpret_cast<const f16x8*>(s_a + kt * AH + ((MT * j + mt) * 64 + lane) * 8);
 #pragma unroll
           for (int q = 0; q < kDownRTW; ++q) acc[q][mt] = mfma16(a, bq[q], acc[q][mt]);
         }
       }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (i + 2 < NCB) load_chunk(b[i & 1], c0 + i + 2);
+    if constexpr (i + PF < NCB) load_chunk(b[i % PF], c0 + i + PF);
     __builtin_amdgcn_sched_barrier(0);
     // y = acc * 2^E_row, one exponent per (row, 8 columns), one row tile at
     // a time through the wave's buffer: a lane then holds 8 consecutive
@@ -999,24 +1005,34 @@ __device__ __forceinline__ void down_res_body(const LayerArgs& L, const PrefillW
   for_each_index(chunk, std::make_integer_sequence<int, NCB>{});
 }
 
-template <int KT, int NCB>
+// HALVES = 2: a work unit takes 32 rows of an item (MT = 2), so the
+// resident h tiles take half the LDS and two workgroups fit on a CU.
+template <int KT, int NCB, int MT, int PF, int HALVES>
 __global__ __launch_bounds__(kThreads) void prefill_down_res_kernel(LayerArgs L, PrefillWs ws) {
-  __shared__ __align__(16) _Float16 s_a[KT][kATileHalves];
-  __shared__ __align__(16) float s_t[kGemmWaves * kGroupRows * 16];
-  __shared__ int8_t s_hx[kGroupRows * KT * (kTileCols / kTileRows)];
-  __shared__ int s_erow[kGroupRows];
+  static_assert(MT * 16 * HALVES == kGroupRows, "the parts of an item cover its rows");
+  __shared__ __align__(16) _Float16 s_a[KT * 8 * MT * kFragHalves];
+  __shared__ __align__(16) float s_t[kGemmWaves * MT * 16 * 16];
+  __shared__ int8_t s_hx[MT * 16 * KT * (kTileCols / kTileRows)];
+  __shared__ int s_erow[MT * 16];
   const int RB = L.H / (kDownChunkRows * NCB);
-  const int2 wu = work_unit(blockIdx.x, ws.hdr, RB);
+  const int2 wu = work_unit(blockIdx.x, ws.hdr, RB * HALVES);
   if (wu.x < 0) return;
   const int4 it = ws.items[wu.x];
+  const int part = wu.y / RB;
+  const int row0 = it.y + part * MT * 16;
+  const int nrows = min(it.z - part * MT * 16, MT * 16);
+  if (nrows <= 0) return;
   const uint8_t* wb = expert_base(L, it);
-  const int row0 = it.y, nrows = it.z;
-  const int c0 = wu.y * NCB;
+  const int c0 = (wu.y % RB) * NCB;
   switch ((nrows + 15) / 16) {
-    case 1: down_res_body<1, KT, NCB>(L, ws, wb, row0, nrows, c0, s_a, s_t, s_erow, s_hx); break;
-    case 2: down_res_body<2, KT, NCB>(L, ws, wb, row0, nrows, c0, s_a, s_t, s_erow, s_hx); break;
-    case 3: down_res_body<3, KT, NCB>(L, ws, wb, row0, nrows, c0, s_a, s_t, s_erow, s_hx); break;
-    default: down_res_body<4, KT, NCB>(L, ws, wb, row0, nrows, c0, s_a, s_t, s_erow, s_hx); break;
+    case 1: down_res_body<1, KT, NCB, MT, PF>(L, ws, wb, row0, nrows, c0, s_a, s_t, s_erow, s_hx); break;
+    case 2: down_res_body<2, KT, NCB, MT, PF>(L, ws, wb, row0, nrows, c0, s_a, s_t, s_erow, s_hx); break;
+    case 3:
+      if constexpr (MT >= 3) down_res_body<3, KT, NCB, MT, PF>(L, ws, wb, row0, nrows, c0, s_a, s_t, s_erow, s_hx);
+      break;
+    default:
+      if constexpr (MT >= 4) down_res_body<4, KT, NCB, MT, PF>(L, ws, wb, row0, nrows, c0, s_a, s_t, s_erow, s_hx);
+      break;
   }
 }
 
@@ -1159,14 +1175,17 @@ hipError_t launch_prefill(const LayerArgs& L, const void* x, int x_bf16, int T,
   const int ktd = L.I / kTileCols;
   const int nc = L.H / kDownChunkRows;
   if (ktd <= kDownResMaxKT) {
-    // A resident: chunks per block, 3 where they divide H / 256 (then 2, 1)
+    // A resident: chunks per block, 3 where they divide H / 256 (then 2, 1).
+    // Chunks up to kSizeOrderMaxTokens (mostly short items): half items, two
+    // workgroups per CU
     const int ncb = nc % 3 == 0 ? 3 : (nc % 2 == 0 ? 2 : 1);
-    const long long nb = (static_cast<long long>(grid_items) + 7) / 8 * 8 * (nc / ncb);
+    const bool halves = T <= kSizeOrderMaxTokens;
+    const long long nb = (static_cast<long long>(grid_items) + 7) / 8 * 8 * (nc / ncb) * (halves ? 2 : 1);
     const dim3 g(static_cast<int>(nb)), b(kThreads);
     auto dr = [&](auto ktc, auto ncbc) {
-      return launch_kernel(K_PREFILL_DOWN,
-                           prefill_down_res_kernel<decltype(ktc)::value, decltype(ncbc)::value>, g, b, 0, s,
-                           L, ws);
+      constexpr int KTv = decltype(ktc)::value, NCBv = decltype(ncbc)::value;
+      return halves ? launch_kernel(K_PREFILL_DOWN, prefill_down_res_kernel<KTv, NCBv, 2, 1, 2>, g, b, 0, s, L, ws)
+                    : launch_kernel(K_PREFILL_DOWN, prefill_down_res_kernel<KTv, NCBv, 4, 2, 1>, g, b, 0, s, L, ws);
     };
     auto by_ncb = [&](auto ktc) {
       if (ncb == 3) return dr(ktc, std::integral_constant<int, 3>{});
