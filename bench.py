@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", default="",
                     help="decode1|decode1_two_calls|decode1_gemv|decode2|decode3|prefill|prefill32768|"
-                         "tiered|windows|stack (profiling runs)")
+                         "tiered|tiered_device|tiered_host|windows|stack (profiling runs)")
     ap.add_argument("--stack-layers", type=int, default=48,
                     help="layers of the stacked decode/prefill runs (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -506,6 +506,8 @@ def main():
             "ms_per_layer_untiered": ms_u, "ms_per_layer_untiered_eager": ms_eager_u,
             "tokens_per_s": 1000.0 / ms, "tokens_per_s_untiered": 1000.0 / ms_u,
             "hit_rate": float(hit.mean()), "miss_bytes_per_step": float(miss_bytes),
+            # the misses' cost over the untiered call on the same rows, as a rate
+            "miss_GBps_over_untiered": (float(miss_bytes / ((ms - ms_u) * 1e6)) if ms > ms_u else None),
             "apply_s_per_layer": apply_s,
             "kernel_ms": {"decode_gateup": gu[1] / gu[0], "decode_down": dn[1] / dn[0]},
         }
@@ -535,9 +537,10 @@ def main():
     if only == "prefill32768":   # profiling runs only: one 32768-token chunk, Zipf routing
         results["prefill_T32768"] = prefill_case(32768, max(4, args.prefill_steps // 10), 2, "zipf")
         progress("prefill_T32768")
-    if only in ("", "tiered"):
+    if only in ("", "tiered", "tiered_device"):
         results["decode_T1_tiered_device_arena"] = tiered_case(half, args.warmup, "device", len(layers))
         progress("decode_T1_tiered_device_arena")
+    if only in ("", "tiered", "tiered_host"):
         results["decode_T1_tiered_host_arena"] = tiered_case(half, args.warmup, "host", min(4, len(layers)))
         progress("decode_T1_tiered_host_arena")
     if only in ("", "windows"):

@@ -22,6 +22,13 @@
       that a reader can tell whether the kernel has changed since the
       counters were taken.
 
+  python -m bit_quantized_expert_router_amd.profsum segments DIR --kernel NAME
+          --split N1,N2,... [--labels L1,L2,...]
+      the dispatches of kernel NAME from `*kernel_trace.csv`, in start-time
+      order, cut into consecutive runs of N1, N2, ... dispatches (the phases
+      of a program whose dispatch counts are known), with the count and the
+      average / min / max duration of each run.
+
 Reads CSV only; runs nothing.
 """
 from __future__ import annotations
@@ -59,6 +66,24 @@ def stats(root: str, match: str = "moeq2") -> list[dict]:
                     "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
                     "max_us": float(r["MaxNs"]) / 1e3,
                     "total_ms": float(r["TotalDurationNs"]) / 1e6})
+    return out
+
+
+def segments(root: str, kernel: str, split: list[int]) -> list[dict]:
+    """Durations (us) of kernel's dispatches in start order, cut into
+    consecutive runs of the given sizes."""
+    rows = [r for r in csv.DictReader(open(_one("*kernel_trace.csv", root)))
+            if _short(r["Kernel_Name"]).split("<")[0] == kernel]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    if sum(split) != len(rows):
+        sys.exit(f"profsum: {kernel} has {len(rows)} dispatches, the split covers {sum(split)}")
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    out, i = [], 0
+    for n in split:
+        part = dur[i:i + n]
+        i += n
+        out.append({"calls": n, "avg_us": statistics.mean(part) if part else float("nan"),
+                    "min_us": min(part) if part else float("nan"), "max_us": max(part) if part else float("nan")})
     return out
 
 
@@ -158,6 +183,11 @@ def main(argv=None):
     c = sub.add_parser("counters")
     c.add_argument("dir")
     c.add_argument("--match", default="prefill")
+    g = sub.add_parser("segments")
+    g.add_argument("dir")
+    g.add_argument("--kernel", required=True)
+    g.add_argument("--split", required=True)
+    g.add_argument("--labels", default="")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
@@ -172,6 +202,15 @@ def main(argv=None):
             print(f"{r['kernel']}  grid {r['grid']}  dispatches {r['dispatches']}  avg_us {r['avg_us']:.2f}{derived}")
             for cn, v in sorted(r["counters"].items()):
                 print(f"    {cn}: {v:.6g}")
+        return
+
+    if a.cmd == "segments":
+        split = [int(v) for v in a.split.split(",")]
+        labels = a.labels.split(",") if a.labels else [f"part{i}" for i in range(len(split))]
+        print(f"{a.kernel}")
+        print(f"{'segment':<24} {'calls':>7} {'avg_us':>9} {'min_us':>9} {'max_us':>9}")
+        for lab, r in zip(labels, segments(a.dir, a.kernel, split)):
+            print(f"{lab[:24]:<24} {r['calls']:>7} {r['avg_us']:>9.2f} {r['min_us']:>9.2f} {r['max_us']:>9.2f}")
         return
 
     if a.cmd == "stats":

@@ -73,3 +73,20 @@ def test_counters_summary(tmp_path):
     assert abs(r["clock_GHz"] - 2.4) < 1e-9
     assert abs(r["mfma_busy_pct"] - 25.0) < 1e-9
     assert abs(r["valu_issue_pct"] - 12.5) < 1e-9
+
+
+def test_segments_cut_dispatches_in_start_order(tmp_path):
+    from bit_quantized_expert_router_amd.profsum import segments
+    d = tmp_path / "run"
+    d.mkdir()
+    lines = ['"Kind","Kernel_Name","Start_Timestamp","End_Timestamp"']
+    # dispatches of k listed out of order; durations 1, 2, 3, 10, 20 us by start time; another kernel between
+    for start, dur, name in ((3000, 3000, "void moeq2::k<1>(int)"), (0, 1000, "void moeq2::k<1>(int)"),
+                             (500, 99000, "void moeq2::other(int)"), (1000, 2000, "void moeq2::k<1>(int)"),
+                             (9000, 10000, "void moeq2::k<1>(int)"), (30000, 20000, "void moeq2::k<1>(int)")):
+        lines.append(f'"KERNEL_DISPATCH","{name}",{start},{start + dur}')
+    (d / "x_kernel_trace.csv").write_text("\n".join(lines) + "\n")
+    parts = segments(str(tmp_path), "k", [3, 2])
+    assert [p["calls"] for p in parts] == [3, 2]
+    assert parts[0]["avg_us"] == 2.0 and parts[0]["max_us"] == 3.0
+    assert parts[1]["avg_us"] == 15.0 and parts[1]["min_us"] == 10.0
