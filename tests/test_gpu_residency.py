@@ -174,8 +174,10 @@ def test_decode_tiered_full_size_pinned(B):
 
 
 @pytest.mark.parametrize("n,arena,S", [(37, "device", 5), (300, "device", 16), (300, "pinned", 40),
-                                       (1000, "device", 0)])
+                                       (1000, "device", 0), (9000, "device", 20)])
 def test_prefill_tiered_bitwise(B, n, arena, S):
+    """Up to 4096 tokens: items in size order, half items in the down GEMM;
+    9000 tokens: expert order, full items, two row tiles per gate/up wave."""
     print(f"tiered prefill T={n} arena={arena} S={S}", flush=True)
     E, H, I, k = 64, 1024, 256, 4
     T = Tier(B, 75, E, H, I, S, arena)
