@@ -506,8 +506,10 @@ def main():
             "ms_per_layer_untiered": ms_u, "ms_per_layer_untiered_eager": ms_eager_u,
             "tokens_per_s": 1000.0 / ms, "tokens_per_s_untiered": 1000.0 / ms_u,
             "hit_rate": float(hit.mean()), "miss_bytes_per_step": float(miss_bytes),
-            # the misses' cost over the untiered call on the same rows, as a rate
-            "miss_GBps_over_untiered": (float(miss_bytes / ((ms - ms_u) * 1e6)) if ms > ms_u else None),
+            # host arena: the misses' cost over the untiered call on the same
+            # rows, as a PCIe rate (a device arena reads them from HBM)
+            "miss_GBps_over_untiered": (float(miss_bytes / ((ms - ms_u) * 1e6))
+                                        if arena_kind == "host" and ms > ms_u else None),
             "apply_s_per_layer": apply_s,
             "kernel_ms": {"decode_gateup": gu[1] / gu[0], "decode_down": dn[1] / dn[0]},
         }
