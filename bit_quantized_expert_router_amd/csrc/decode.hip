@@ -483,14 +483,14 @@ struct DownTiles {
 // Work items of down row tile rt: item i = (slot i / KTd, K tile i % KTd),
 // wave w takes items w, w + 8, ...; this loads the wave's items j0..j0+DB-1
 // (an item past nitems gets a zero-size resource: issued, no memory touched).
-template <int DB>
+template <int DB, int NW = kWaves>
 __device__ __forceinline__ void load_down(const LayerArgs& L, const uint8_t* const* base, int nitems, int KTd,
                                           int rt, int j0, int lane, DownTiles<DB>& D) {
   const int wid = wave_id();
   const uint32_t mat = __builtin_amdgcn_readfirstlane(matrix_bytes(L.H, L.I));
 #pragma unroll
   for (int b = 0; b < DB; ++b) {
-    const int wi = wid + kWaves * (j0 + b);
+    const int wi = wid + NW * (j0 + b);
     const bool live = wi < nitems;
     const int slot = live ? wi / KTd : 0;
     const int kt = live ? wi % KTd : 0;
@@ -512,7 +512,7 @@ __device__ __forceinline__ int pair_token(int p, int T, int k) {
 // rescaled to each token's exponent; otherwise hsrc is the workspace copy
 // and each fragment is rescaled here: its 8 values lie in one 16-row tile
 // of I, whose exponent is hexp[p][tile].
-template <int DB, bool STAGED>
+template <int DB, bool STAGED, int NW = kWaves>
 __device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int KTd, int j0,
                                          int lane, const _Float16* hsrc,
                                          const int (*pidx)[kMaxT], int T, int I,
@@ -523,7 +523,7 @@ __device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int
   const int my_et = STAGED ? 0 : s_et[m < T ? m : 0];
 #pragma unroll
   for (int b = 0; b < DB; ++b) {
-    const int wi = wid + kWaves * (j0 + b);
+    const int wi = wid + NW * (j0 + b);
     if (wi < nitems) {
       const int slot = wi / KTd;
       const int kt = wi % KTd;
@@ -545,6 +545,7 @@ __device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int
 
 // Sum of the 8 waves' accumulators (wave order) and the output rows of tile
 // rt: out = acc * 2^E_t (+ residual).
+template <int NW = kWaves>
 __device__ void down_store(const f32x4& acc, f32x4 (*s_red)[32], int rt, int T, int H,
                            const int* s_et, const void* residual,
                            void* out, int out_bf16) {
@@ -554,7 +555,7 @@ __device__ void down_store(const f32x4& acc, f32x4 (*s_red)[32], int rt, int T, 
   __syncthreads();
   if (wid == 0 && lane < 32) {
     f32x4 Y = s_red[0][lane];
-    for (int q = 1; q < kWaves; ++q) Y += s_red[q][lane];
+    for (int q = 1; q < NW; ++q) Y += s_red[q][lane];
     const int row = rt * kTileRows + (lane & 15);
     const bool hi = lane >= 16;
 #pragma unroll
@@ -767,8 +768,10 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
 // Kernel 2: down row tile blockIdx.x.
 constexpr int kExpPre = 2;               // exponent vectors per lane loaded at kernel entry
 
-template <bool STAGED, int DB>
-__global__ __launch_bounds__(kThreads) void decode_down_kernel(
+// NTD threads: 8 waves for one token, 16 for more (each wave's chain of
+// dependent loads shorter when the slots are many).
+template <bool STAGED, int DB, int NTD>
+__global__ __launch_bounds__(NTD) void decode_down_kernel(
     LayerArgs L, int T, int k, const void* __restrict__ residual, void* __restrict__ out,
     int out_bf16, const uint8_t* __restrict__ ws) {
   extern __shared__ __align__(16) uint8_t dyn[];
@@ -777,7 +780,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   __shared__ int s_pidx[kMaxSlots][kMaxT];
   __shared__ int s_n;
   __shared__ int s_et[kMaxT];       // E_t of each token
-  __shared__ f32x4 s_red[kWaves][32];
+  __shared__ f32x4 s_red[NTD / kWave][32];
   const DecodeHeader* hdr = reinterpret_cast<const DecodeHeader*>(ws);
   const _Float16* hin = reinterpret_cast<const _Float16*>(ws + kHeaderBytes);
   const int I = L.I;
@@ -798,7 +801,7 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
   if constexpr (STAGED) {
 #pragma unroll
     for (int q = 0; q < kDownStage; ++q) {
-      const int ch = min(static_cast<int>(threadIdx.x) + kThreads * q, hch - 1);
+      const int ch = min(static_cast<int>(threadIdx.x) + NTD * q, hch - 1);
       hreg[q] = *reinterpret_cast<const u32x4*>(hin + 8 * ch);
       hx[q] = *chunk_exp(ch);
     }
@@ -814,18 +817,18 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
 
   {
     // the header loads are issued together (clamped, unconditional)
-    constexpr int kPidxLoads = (kMaxSlots * kMaxT + kThreads - 1) / kThreads;
+    constexpr int kPidxLoads = (kMaxSlots * kMaxT + NTD - 1) / NTD;
     const int i = threadIdx.x;
     const uint8_t* bv = hdr->base[min(i, kMaxSlots - 1)];
     int pv[kPidxLoads];
 #pragma unroll
     for (int q = 0; q < kPidxLoads; ++q)
-      pv[q] = (&hdr->pidx[0][0])[min(i + kThreads * q, kMaxSlots * kMaxT - 1)];
+      pv[q] = (&hdr->pidx[0][0])[min(i + NTD * q, kMaxSlots * kMaxT - 1)];
     const int nv = hdr->n_slots;
     if (i < kMaxSlots) s_base[i] = bv;
 #pragma unroll
     for (int q = 0; q < kPidxLoads; ++q)
-      if (i + kThreads * q < kMaxSlots * kMaxT) (&s_pidx[0][0])[i + kThreads * q] = pv[q];
+      if (i + NTD * q < kMaxSlots * kMaxT) (&s_pidx[0][0])[i + NTD * q] = pv[q];
     if (i == 0) s_n = nv;
   }
 
@@ -868,38 +871,38 @@ __global__ __launch_bounds__(kThreads) void decode_down_kernel(
     };
 #pragma unroll
     for (int q = 0; q < kDownStage; ++q) {
-      const int ch = threadIdx.x + kThreads * q;
+      const int ch = threadIdx.x + NTD * q;
       if (ch < hch) put(ch, hreg[q], hx[q]);
     }
-    for (int ch0 = threadIdx.x + kThreads * kDownStage; ch0 < hch; ch0 += 4 * kThreads) {
+    for (int ch0 = threadIdx.x + NTD * kDownStage; ch0 < hch; ch0 += 4 * NTD) {
       u32x4 r[4];
       int ex[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int ch = min(ch0 + kThreads * u, hch - 1);
+        const int ch = min(ch0 + NTD * u, hch - 1);
         r[u] = *reinterpret_cast<const u32x4*>(hin + 8 * ch);
         ex[u] = *chunk_exp(ch);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (ch0 + kThreads * u < hch) put(ch0 + kThreads * u, r[u], ex[u]);
+        if (ch0 + NTD * u < hch) put(ch0 + NTD * u, r[u], ex[u]);
     }
   }
   // the weight loads go out after the staging: a wave's instructions wait
   // behind the issue of its loads once the CU has many in flight
   DownTiles<DB> D;
-  load_down<DB>(L, s_base, nitems, KTd, rt, 0, lane, D);
+  load_down<DB, NTD / kWave>(L, s_base, nitems, KTd, rt, 0, lane, D);
   __syncthreads();
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int per_wave = (nitems + kWaves - 1) / kWaves;
+  const int per_wave = (nitems + NTD / kWave - 1) / (NTD / kWave);
   const _Float16* hsrc = STAGED ? hs : hin;
-  mma_down<DB, STAGED>(D, nitems, KTd, 0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
+  mma_down<DB, STAGED, NTD / kWave>(D, nitems, KTd, 0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
   for (int j0 = DB; j0 < per_wave; j0 += DB) {
-    load_down<DB>(L, s_base, nitems, KTd, rt, j0, lane, D);
-    mma_down<DB, STAGED>(D, nitems, KTd, j0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
+    load_down<DB, NTD / kWave>(L, s_base, nitems, KTd, rt, j0, lane, D);
+    mma_down<DB, STAGED, NTD / kWave>(D, nitems, KTd, j0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
   }
-  down_store(acc, s_red, rt, T, L.H, s_et, residual, out, out_bf16);
+  down_store<NTD / kWave>(acc, s_red, rt, T, L.H, s_et, residual, out, out_bf16);
 }
 
 // -------------------------------------------------------------- launching --
@@ -1029,12 +1032,19 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
   // down tiles in flight per wave: every item of the largest possible slot
   // list in one batch when that takes at most kDownBatch (zero-size padding
   // loads still cost issue slots), else batches of kDownBatch
-  const int per_wave = (slots_max * (L.I / kTileCols) + kThreads / kWave - 1) / (kThreads / kWave);
+  const int down_threads = T == 1 ? kThreads : 2 * kThreads;
+  const int down_waves = down_threads / kWave;
+  const int per_wave = (slots_max * (L.I / kTileCols) + down_waves - 1) / down_waves;
   auto down = [&](auto staged, auto db) {
     constexpr bool ST = decltype(staged)::value;
-    return launch_kernel(K_DECODE_DOWN, decode_down_kernel<ST, decltype(db)::value>, dim3(L.H / kTileRows),
-                         dim3(kThreads), static_cast<uint32_t>(ST ? lds_h : 0), s, L, T, k, residual, out,
-                         out_bf16, static_cast<const uint8_t*>(ws));
+    constexpr int DBv = decltype(db)::value;
+    const uint32_t lds = static_cast<uint32_t>(ST ? lds_h : 0);
+    const uint8_t* w8 = static_cast<const uint8_t*>(ws);
+    return down_threads == kThreads
+               ? launch_kernel(K_DECODE_DOWN, decode_down_kernel<ST, DBv, kThreads>, dim3(L.H / kTileRows),
+                               dim3(kThreads), lds, s, L, T, k, residual, out, out_bf16, w8)
+               : launch_kernel(K_DECODE_DOWN, decode_down_kernel<ST, DBv, 2 * kThreads>, dim3(L.H / kTileRows),
+                               dim3(2 * kThreads), lds, s, L, T, k, residual, out, out_bf16, w8);
   };
   auto down_db = [&](auto staged) {
     switch (per_wave) {
