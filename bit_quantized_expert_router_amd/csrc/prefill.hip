@@ -14,7 +14,8 @@
 //            workgroup turns `counts` into the work-item list, the others
 //            write each sorted row's token and routing weight.
 //   gateup   work item x 128-row block of I, 8 waves (one 16-row tile of
-//            gate and of up each): A = the item's gathered x rows (fp16,
+//            gate and of up each; two of each and 256-row blocks for chunks
+//            of more than 8192 tokens): A = the item's gathered x rows (fp16,
 //            staged in LDS, double buffered per 256-column K tile), B = the
 //            expert's gate and up tiles dequantized in registers (each weight
 //            is dequantized once per item and used by every M tile; two
@@ -24,12 +25,16 @@
 //            in float32, stored (sorted-row order) as fp16 h * 2^-e with one
 //            exponent e per (row, 16-row tile of I) in a byte array, so that
 //            |h~| < 1 and fp16 cannot overflow whatever the weights' scales.
-//   down     work item x 256-row block of H, 8 waves x 2 row tiles: A = h
-//            rows rescaled to one exponent per row (the row's largest) while
-//            they are moved into LDS, B = down tiles; y = acc * 2^E_row, stored
-//            as fp16 y * 2^-F with one exponent F per (row, 8 columns): each
-//            wave turns its accumulators around through LDS so that a lane
-//            holds 8 consecutive columns of one row.
+//   down     A = h rows rescaled to one exponent per row (the row's
+//            largest) while they are moved into LDS, B = down tiles, 8 waves x
+//            2 row tiles of H; y = acc * 2^E_row, stored as fp16 y * 2^-F
+//            with one exponent F per (row, 8 columns): each wave turns its
+//            accumulators around through LDS so that a lane holds 8
+//            consecutive columns of one row.  For I <= 768 the item's h rows
+//            stay in LDS while the workgroup runs three 256-row chunks of H
+//            (half items of 32 rows for chunks of up to 4096 tokens, so that
+//            two workgroups fit on a CU); wider I stages h per K tile for
+//            each 256-row block.
 //   combine  token t: out = sum_j y~[pair_pos[t,j]] * 2^F + y~[shared row]
 //            * 2^F (+ residual), j ascending: fixed order, no atomics.
 // Workgroup ids are remapped so that every XCD gets an equal share of the
@@ -60,7 +65,7 @@ constexpr int kDownRing = 2;
 
 struct PrefillWs {
   int32_t* hdr;        // [0] = number of work items
-  int4* items;         // {expert, row0, nrows, 0}
+  int4* items;         // {expert, row0, nrows, slot: the expert itself, or its residency slot, -1 = arena}
   float* unscale;      // [T]  1 / s_t
   int32_t* row_tok;    // [rows] token of each sorted row
   float* row_w;        // [rows] routing weight of each sorted row (1 for the shared expert)
@@ -554,7 +559,6 @@ __device__ __forceinline__ void k_loop_fixed(u32x4 (&b)[RING][NB], LoadB load_b,
 // ------------------------------------------------------------------ gate/up --
 // Row tiles of gate (and of up) per wave for a chunk of T tokens.
 inline int gateup_row_tiles_per_wave(int T) { return T > 2 * kSizeOrderMaxTokens ? 2 : 1; }
-
 
 // Wave w of row block rb takes the RTW row tiles rt0 .. rt0 + RTW - 1 of
 // gate and of up, rt0 = (rb * kGemmWaves + w) * RTW.
