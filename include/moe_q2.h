@@ -30,8 +30,9 @@
  *   - The caller owns all memory, including `workspace`.  The library never
  *     allocates, frees or synchronises, and never reads device data on the
  *     host (the tiered calls only ask the runtime what kind of memory the
- *     arena is).  Each call only enqueues kernels on `stream` (a hipStream_t passed
- *     as void*, NULL = the null stream), in stream order.
+ *     arena is).  Each call only enqueues work -- kernels, and for
+ *     moe_residency_apply slot copies -- on `stream` (a hipStream_t passed as
+ *     void*, NULL = the null stream), in stream order.
  *   - Every argument is validated before anything is enqueued: a non-zero
  *     status means nothing was enqueued (except MOE_ERR_HIP, which reports a
  *     failed launch; moe_last_error() gives the detail).
