@@ -459,6 +459,9 @@ __device__ void gateup_compute(const GateUpTiles<KTW>& R, const _Float16* xs, in
     const int RTI = I / kTileRows;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+      // element r holds tokens r and 4 + r: none of them is in the window
+      // from r = T on (each element's exponent reduction is a DPP chain)
+      if (r >= T) break;
       // one token per 16-lane row: p, and so the branch, is uniform in it
       const int t = (hi ? 4 : 0) + r;
       const int p = t < T ? S.pidx[slot][t] : -1;
