@@ -12,7 +12,7 @@
 //   dequant_mfma  the inner step of the gate/up kernels with its operands in
 //                 registers: Q2 tile dequantization and two MFMAs per
 //                 32-weight block and M tile, for items of one and of four
-//                 M tiles, in weights per second
+//                 M tiles, in 10^12 weights per second
 // Standalone program; it shares only q2_device.h with the library.
 #include <hip/hip_runtime.h>
 
@@ -261,8 +261,8 @@ int main() {
   printf("{\"device\": \"%s\", \"compute_units\": %d, \"stream_read_GBps\": %.1f, \"stream_read_workgroups\": %d, "
          "\"burst_24MiB_us\": %.2f, \"empty_kernel_us_eager\": %.3f, \"empty_kernel_us_graph\": %.3f, "
          "\"mfma_f16_TFLOPs\": %.1f, \"mfma_clock_MHz_loaded\": %.0f, \"mfma_clock_MHz_one_wave\": %.0f, "
-         "\"mfma_16x16x32_f16_cycles\": %.2f, \"dequant_mfma_Gweights_per_s\": %.1f, "
-         "\"dequant_mfma4_Gweights_per_s\": %.1f}\n",
+         "\"mfma_16x16x32_f16_cycles\": %.2f, \"dequant_mfma_Tweights_per_s\": %.1f, "
+         "\"dequant_mfma4_Tweights_per_s\": %.1f}\n",
          prop.name, prop.multiProcessorCount, best_gbs, best_wgs, burst_us, eager_us, graph_us, mfma_tf, loaded_mhz,
          single_mhz, cycles_per_mfma, dq_mfma, dq_mfma4);
   CK(hipFree(d_out));
