@@ -32,6 +32,12 @@
 //   as h * 2^-E_t (a power-of-two rescale); the MFMA accumulator then sums
 //   W_down(e) h~(e) over all slots in a fixed order, so the weighted combine
 //   is exact, and out = acc * 2^E_t (+ residual).
+// One token with the routing inside (the headline decode step) runs kernels
+// compiled for one token (the per-token loops straight-line), and in its
+// routed workgroups every wave takes part in the top-k: each selects the top
+// k of its own slice of the logits, and after the first barrier every
+// candidate's rank among the 8 * k is counted with ballots; the softmax
+// weights are computed while the weight tiles are in flight.
 // The two halves meet at a kernel boundary.  A grid-wide barrier inside one
 // kernel was measured as no faster on this device: with the workgroups spread
 // over 8 XCDs every cross-XCD signal is a round trip through memory, and the
@@ -57,10 +63,14 @@ constexpr int kThreads = 512;            // 8 waves (kernel 2)
 constexpr int kWaves = kThreads / kWave;
 constexpr int kXRegValues = 12288;       // x is kept in registers when T*H <= this
 
-// x chunks of 8 values per thread kept in registers; at least half of the
-// NT threads hold x
-template <int NT>
-constexpr int x_reg_chunks() { return (kXRegValues / 8 + NT / 2 - 1) / (NT / 2); }
+// x chunks of 8 values per thread kept in registers (x of at most TM tokens
+// of at most MOE_MAX_DIM values, and at most kXRegValues values); at least
+// half of the NT threads hold x
+template <int NT, int TM>
+constexpr int x_reg_chunks() {
+  constexpr int v = TM * MOE_MAX_DIM < kXRegValues ? TM * MOE_MAX_DIM : kXRegValues;
+  return (v / 8 + NT / 2 - 1) / (NT / 2);
+}
 constexpr int kDownBatch = 8;            // down tiles in flight per wave in kernel 2
 constexpr int kDownStage = 4;            // h~ chunks per thread loaded ahead in kernel 2
 
@@ -194,11 +204,13 @@ __device__ void slots_one_token(DecodeSlots& S, int e, float wt, int k, bool has
   if (lane == 0) S.n = k + (has_shared ? 1 : 0);
 }
 
-// Token of x chunk c (chunks of 8 values, cpt chunks per token).
+// Token of x chunk c (chunks of 8 values, cpt chunks per token; at most TM
+// tokens).
+template <int TM>
 __device__ __forceinline__ int token_of_chunk(int c, int cpt) {
   int t = 0;
 #pragma unroll
-  for (int q = 1; q < kMaxT; ++q) t += c >= q * cpt;
+  for (int q = 1; q < TM; ++q) t += c >= q * cpt;
   return t;
 }
 
@@ -281,28 +293,142 @@ __device__ __forceinline__ void route_topk_waves(const LayerArgs& L, int T, int 
   }
 }
 
+// One token's top-k on all NW = 8 waves of a block (the routed blocks of the
+// one-token launch).  Wave w takes experts [w * 64 * P, (w + 1) * 64 * P), P
+// per lane (lane l: ids w * 64 * P + l * P + i), and keeps its own top k:
+// the keys above the wave's k-th largest key (found by bisection on the key
+// bits, each step one compare and a population count of its ballot) and,
+// among the keys equal to it, the lowest ids.  The union of the waves' own
+// top k holds the global top k.  After a barrier, topk_rank_candidates counts
+// for every candidate how many of the NW * k beat it: that count is its rank
+// in the global selection order.  Candidates are kept as (key << 32) | ~id:
+// a larger value is the better candidate (equal keys: the lower id), and no
+// two are equal.  s_cand has 16 entries per wave; unused entries hold 0,
+// which no candidate of a valid expert (key > 0) loses to.
+template <int P>
+__device__ __forceinline__ void topk_wave_load(const float* __restrict__ row, int E, int wid, int lane,
+                                               float (&lv)[P]) {
+  const int base = wid * kWave * P + lane * P;
+#pragma unroll
+  for (int i = 0; i < P; ++i) lv[i] = row[min(base + i, E - 1)];
+}
+
+template <int P>
+__device__ __forceinline__ void topk_wave_select(const float (&lv)[P], int E, int k, int wid, int lane,
+                                                 uint64_t (*s_cand)[MOE_MAX_TOPK]) {
+  uint32_t key[P];
+  const int base = wid * kWave * P + lane * P;
+#pragma unroll
+  for (int i = 0; i < P; ++i) key[i] = base + i < E ? float_key(lv[i]) : 0u;
+  // tau = the largest value with at least k keys >= tau: the k-th largest key
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = tau | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) cnt += __popcll(__ballot(key[i] >= c));
+    tau = cnt >= k ? c : tau;
+  }
+  // fewer than k keys lie above tau; the rest of the k are the lowest ids
+  // among the keys equal to tau (ids ascend with (lane, i))
+  int n_gt = 0;
+  uint64_t eq[P], gt[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    gt[i] = __ballot(key[i] > tau);
+    eq[i] = __ballot(key[i] == tau);
+    n_gt += __popcll(gt[i]);
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  int ties_before = 0;     // keys equal to tau in lower lanes
+#pragma unroll
+  for (int i = 0; i < P; ++i) ties_before += __popcll(eq[i] & below);
+  if (lane < MOE_MAX_TOPK && lane >= k) s_cand[wid][lane] = 0ull;
+  {
+    int gt_before = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) gt_before += __popcll(gt[i] & below);
+    int t_lo = ties_before, g_lo = gt_before;   // counts of lower ids, then this lane's earlier entries
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const bool is_gt = key[i] > tau;
+      const bool is_eq = key[i] == tau;
+      const bool take = is_gt || (is_eq && t_lo < k - n_gt);
+      // position: selected entries of lower ids (all the greater ones, and
+      // the equal ones that are taken)
+      const int pos = g_lo + min(t_lo, k - n_gt);
+      if (take) s_cand[wid][pos] = (static_cast<uint64_t>(key[i]) << 32) | static_cast<uint32_t>(~(base + i));
+      g_lo += is_gt ? 1 : 0;
+      t_lo += is_eq ? 1 : 0;
+    }
+  }
+}
+
+// Ranks of the candidates: each lane holds two of the 128 entries (waves
+// 0..3 and 4..7); for each of its wave's 16 entries (read from LDS by every
+// lane) a wave counts the entries that beat it with two ballots, the counts
+// independent of each other, and lane j keeps entry j's count (entries past
+// k hold 0 and rank last).  A candidate of rank r < k becomes slot r (pair r:
+// the slots and pairs of one token's top-k are in selection order), its
+// logit goes to s_logit[r]; the shared expert takes slot k.  The weights
+// (softmax over the k logits) come later, from s_logit.
+template <int NW>
+__device__ __forceinline__ void topk_rank_candidates(int k, int wid, int lane,
+                                                     const uint64_t (*s_cand)[MOE_MAX_TOPK],
+                                                     DecodeSlots& S, float* s_logit, bool has_shared) {
+  static_assert(NW * MOE_MAX_TOPK == 2 * kWave, "two entries per lane");
+  const uint64_t* flat = &s_cand[0][0];
+  const uint64_t c0 = flat[lane], c1 = flat[kWave + lane];
+  const uint64_t mc = s_cand[wid][lane & (MOE_MAX_TOPK - 1)];
+  uint64_t mj[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) mj[j] = s_cand[wid][j];
+  int my_rank = MOE_MAX_TOPK;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    const int r = __popcll(__ballot(c0 > mj[j])) + __popcll(__ballot(c1 > mj[j]));
+    my_rank = lane == j ? r : my_rank;
+  }
+  if (lane < k && my_rank < k) {
+    S.expert[my_rank] = static_cast<int>(~static_cast<uint32_t>(mc));
+    s_logit[my_rank] = key_float(static_cast<uint32_t>(mc >> 32));
+  }
+  if (wid == 0) {
+    if (lane <= k) {
+      S.pidx[lane][0] = (lane < k || has_shared) ? lane : -1;
+#pragma unroll
+      for (int t = 1; t < kMaxT; ++t) S.pidx[lane][t] = -1;
+    }
+    if (lane == 0) {
+      S.expert[k] = -1;
+      if (has_shared) S.wpair[k] = 1.0f;
+      S.n = k + (has_shared ? 1 : 0);
+    }
+  }
+}
+
 // Per-token pre-norm multiplier rmul (1 without the pre-norm) and fp16
 // normaliser smul: every wave writes its partial sums of x^2 and max |x| to
 // s_stat (token_partials), and after a barrier every thread derives the
 // multipliers from them itself (token_derive).
 // (token of chunk c: c / (H/8), by comparisons)
-template <bool BF16, int XC>
+template <bool BF16, int XC, int TM>
 __device__ void token_partials(const void* x, int T, int H, bool xreg, const u32x4 (&xr)[XC][2],
                                float (*s_stat)[kMaxT][2], int xt, int nxt) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = wave_id();
   const int nch = T * H / 8;
   const int cpt = H / 8;
-  float ss[kMaxT], mx[kMaxT];
+  float ss[TM], mx[TM];
 #pragma unroll
-  for (int q = 0; q < kMaxT; ++q) { ss[q] = 0.0f; mx[q] = 0.0f; }
+  for (int q = 0; q < TM; ++q) { ss[q] = 0.0f; mx[q] = 0.0f; }
   auto accum = [&](int c, const float (&v)[8]) {
-    const int t = token_of_chunk(c, cpt);
+    const int t = token_of_chunk<TM>(c, cpt);
     float a = 0.0f, b = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) { a += v[i] * v[i]; b = fmaxf(b, fabsf(v[i])); }
 #pragma unroll
-    for (int q = 0; q < kMaxT; ++q) {
+    for (int q = 0; q < TM; ++q) {
       ss[q] += (q == t) ? a : 0.0f;
       mx[q] = (q == t) ? fmaxf(mx[q], b) : mx[q];
     }
@@ -326,20 +452,23 @@ __device__ void token_partials(const void* x, int T, int H, bool xreg, const u32
       accum(c, v);
     }
   }
-  for (int t = 0; t < T; ++t) {
-    const float a = wave_sum(ss[t]);
-    const float b = wave_max(mx[t]);
-    if (lane == 0) { s_stat[wid][t][0] = a; s_stat[wid][t][1] = b; }
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    if (t < T) {   // uniform
+      const float a = wave_sum(ss[t]);
+      const float b = wave_max(mx[t]);
+      if (lane == 0) { s_stat[wid][t][0] = a; s_stat[wid][t][1] = b; }
+    }
   }
 }
 
-template <int NW>
+template <int NW, int TM>
 __device__ __forceinline__ void token_derive(int T, int H, int prenorm,
                                              const float (*s_stat)[kMaxT][2],
-                                             float (&rmul)[kMaxT],
-                                             float (&smul)[kMaxT]) {
+                                             float (&rmul)[TM],
+                                             float (&smul)[TM]) {
 #pragma unroll
-  for (int t = 0; t < kMaxT; ++t) {
+  for (int t = 0; t < TM; ++t) {
     rmul[t] = 1.0f;
     smul[t] = 1.0f;
     if (t < T) {   // uniform: only the window's tokens pay for the divisions
@@ -353,18 +482,18 @@ __device__ __forceinline__ void token_derive(int T, int H, int prenorm,
 }
 
 // fp16 copy of x_hat * s_t into LDS ([T][H]).
-template <bool BF16, int XC>
+template <bool BF16, int XC, int TM>
 __device__ void stage_x(const void* x, int T, int H, bool xreg, const u32x4 (&xr)[XC][2],
-                        const float (&rmul)[kMaxT],
-                        const float (&smul)[kMaxT], _Float16* xs, int xt,
+                        const float (&rmul)[TM],
+                        const float (&smul)[TM], _Float16* xs, int xt,
                         int nxt) {
   const int nch = T * H / 8;
   const int cpt = H / 8;
   auto put = [&](int c, const float (&v)[8]) {
-    const int t = token_of_chunk(c, cpt);
+    const int t = token_of_chunk<TM>(c, cpt);
     float r = rmul[0], s = smul[0];
 #pragma unroll
-    for (int q = 1; q < kMaxT; ++q) { r = (q == t) ? rmul[q] : r; s = (q == t) ? smul[q] : s; }
+    for (int q = 1; q < TM; ++q) { r = (q == t) ? rmul[q] : r; s = (q == t) ? smul[q] : s; }
     f16x8 h;
 #pragma unroll
     for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>((v[i] * r) * s);
@@ -424,7 +553,7 @@ __device__ __forceinline__ void load_gateup(const uint8_t* expert, bool live, in
 // every (slot, token) pair (not for an inactive group): the 16 values of a
 // pair in this row tile as fp16 h * 2^-e, e = block_exponent of their
 // largest |h|, and e in hexp[pair][rt].
-template <int KTW>
+template <int KTW, int TM>
 __device__ void gateup_compute(const GateUpTiles<KTW>& R, const _Float16* xs, int T, int H, int I,
                                int rt, int kq, int slot, bool active, const DecodeSlots& S,
                                const float* s_smul,
@@ -458,7 +587,7 @@ __device__ void gateup_compute(const GateUpTiles<KTW>& R, const _Float16* xs, in
     const bool hi = lane >= 16;
     const int RTI = I / kTileRows;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < (TM < 4 ? TM : 4); ++r) {
       // element r holds tokens r and 4 + r: none of them is in the window
       // from r = T on (each element's exponent reduction is a DPP chain)
       if (r >= T) break;
@@ -548,7 +677,7 @@ __device__ __forceinline__ void mma_down(const DownTiles<DB>& D, int nitems, int
 
 // Sum of the 8 waves' accumulators (wave order) and the output rows of tile
 // rt: out = acc * 2^E_t (+ residual).
-template <int NW = kWaves>
+template <int NW = kWaves, int TM = kMaxT>
 __device__ void down_store(const f32x4& acc, f32x4 (*s_red)[32], int rt, int T, int H,
                            const int* s_et, const void* residual,
                            void* out, int out_bf16) {
@@ -562,7 +691,7 @@ __device__ void down_store(const f32x4& acc, f32x4 (*s_red)[32], int rt, int T, 
     const int row = rt * kTileRows + (lane & 15);
     const bool hi = lane >= 16;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < (TM < 4 ? TM : 4); ++r) {
       const int t = (hi ? 4 : 0) + r;
       if (t >= T) break;
       float v = ldexpf(Y[r], s_et[t]);
@@ -595,11 +724,11 @@ __device__ __forceinline__ int max_i8x16(const u32x4& v) {
 // so the block loads x, issues its weight loads at once, stages x and
 // multiplies, while the routed blocks are still taking the top-k.  Row
 // tiles sb * RTW + group of the shared expert (its pairs T*k + t, weight 1).
-template <int KTW, bool BF16, int RTW>
+template <int KTW, bool BF16, int RTW, int TM>
 __device__ void shared_gateup(const LayerArgs& L, const void* __restrict__ x, int T, int k, int prenorm,
                               uint8_t* __restrict__ ws, int sb, _Float16* xs, DecodeSlots& S,
                               float (*s_stat)[kMaxT][2], f32x4 (*s_red)[2][32], float* s_smul) {
-  constexpr int NT = 256 * RTW, NW = 4 * RTW, XC = x_reg_chunks<NT>();
+  constexpr int NT = 256 * RTW, NW = 4 * RTW, XC = x_reg_chunks<NT, TM>();
   const int H = L.H, I = L.I;
   const int RTI = I / kTileRows;
   const int lane = threadIdx.x & (kWave - 1);
@@ -614,7 +743,7 @@ __device__ void shared_gateup(const LayerArgs& L, const void* __restrict__ x, in
   issue_x<BF16, XC>(x, nch, xreg, xr, threadIdx.x, NT);
   GateUpTiles<KTW> R;
   load_gateup<KTW>(L.shared, active, H, I, rt, kq, lane, R);
-  token_partials<BF16, XC>(x, T, H, xreg, xr, s_stat, threadIdx.x, NT);
+  token_partials<BF16, XC, TM>(x, T, H, xreg, xr, s_stat, threadIdx.x, NT);
   if (threadIdx.x < kMaxT) {
     const int t = threadIdx.x;
     S.pidx[k][t] = t < T ? T * k + t : -1;
@@ -622,18 +751,18 @@ __device__ void shared_gateup(const LayerArgs& L, const void* __restrict__ x, in
   }
   __syncthreads();
   {
-    float rmul[kMaxT], smul[kMaxT];
-    token_derive<NW>(T, H, prenorm, s_stat, rmul, smul);
+    float rmul[TM], smul[TM];
+    token_derive<NW, TM>(T, H, prenorm, s_stat, rmul, smul);
     if (threadIdx.x == 0) {
 #pragma unroll
-      for (int t = 0; t < kMaxT; ++t) s_smul[t] = smul[t];
+      for (int t = 0; t < TM; ++t) s_smul[t] = smul[t];
     }
-    stage_x<BF16, XC>(x, T, H, xreg, xr, rmul, smul, xs, threadIdx.x, NT);
+    stage_x<BF16, XC, TM>(x, T, H, xreg, xr, rmul, smul, xs, threadIdx.x, NT);
   }
   __syncthreads();
   int8_t* hexp = reinterpret_cast<int8_t*>(ws + kHeaderBytes + decode_h_bytes(T, k, I));
-  gateup_compute<KTW>(R, xs, T, H, I, rt, kq, k, active, S, s_smul, s_red,
-                      reinterpret_cast<_Float16*>(ws + kHeaderBytes), hexp);
+  gateup_compute<KTW, TM>(R, xs, T, H, I, rt, kq, k, active, S, s_smul, s_red,
+                          reinterpret_cast<_Float16*>(ws + kHeaderBytes), hexp);
 }
 
 // Kernel 1: RTW groups of 4 waves; group q of block b takes row tile
@@ -644,12 +773,12 @@ __device__ void shared_gateup(const LayerArgs& L, const void* __restrict__ x, in
 // SPLIT: blocks [0, n_rwg) take the routed row tiles only (group q of block
 // b: routed row tile b + n_rwg * q) and blocks from n_rwg on the shared
 // expert's (shared_gateup).
-template <int KTW, bool BF16, int RPER, int RTW, bool SPLIT>
+template <int KTW, bool BF16, int RPER, int RTW, bool SPLIT, int TM>
 __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
     LayerArgs L, const void* __restrict__ x, int T, const int32_t* __restrict__ ids,
     const float* __restrict__ w, const float* __restrict__ logits, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out, int k, int prenorm, uint8_t* __restrict__ ws, int n_rwg) {
-  constexpr int NT = 256 * RTW, NW = 4 * RTW, XC = x_reg_chunks<NT>();
+  constexpr int NT = 256 * RTW, NW = 4 * RTW, XC = x_reg_chunks<NT, TM>();
   extern __shared__ __align__(16) uint8_t dyn[];
   _Float16* xs = reinterpret_cast<_Float16*>(dyn);              // [T][H]
   __shared__ DecodeSlots S;
@@ -660,10 +789,16 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
   __shared__ int s_slot_of[MOE_MAX_EXPERTS];
   __shared__ int s_slotmap[MOE_MAX_EXPERTS];      // residency tier: slot_of
   __shared__ float s_smul[kMaxT];
+  // one token, routed blocks of the split launch: every wave takes part in
+  // the top-k (topk_wave_select, topk_rank_candidates)
+  constexpr bool kWide = SPLIT && TM == 1 && RPER > 0 && NW == 8;
+  constexpr int P8 = RPER / 8 > 0 ? RPER / 8 : 1;
+  __shared__ uint64_t s_cand[kWide ? NW : 1][MOE_MAX_TOPK];
+  __shared__ float s_logit[MOE_MAX_TOPK];
 
   if constexpr (SPLIT) {
     if (static_cast<int>(blockIdx.x) >= n_rwg) {
-      shared_gateup<KTW, BF16, RTW>(L, x, T, k, prenorm, ws, blockIdx.x - n_rwg, xs, S, s_stat, s_red, s_smul);
+      shared_gateup<KTW, BF16, RTW, TM>(L, x, T, k, prenorm, ws, blockIdx.x - n_rwg, xs, S, s_stat, s_red, s_smul);
       return;
     }
   }
@@ -678,17 +813,22 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
   // sum its statistics and, after one barrier, stage its fp16 copy while
   // wave 0 builds the slots.  So x is ready in LDS when the weight loads are
   // issued, and the MFMA loop can take each tile as it arrives.  With more
-  // than half of the waves routing, all waves take x after routing.
+  // than half of the waves routing, all waves take x after routing.  In the
+  // one-token split launch (kWide) every wave routes a slice of the experts
+  // and every wave takes x.
   const int nch = T * H / 8;
-  const int xw0 = T <= NW / 2 ? T : 0;                         // first x wave
+  const int xw0 = kWide ? 0 : (T <= NW / 2 ? T : 0);          // first x wave
   const int xt = static_cast<int>(threadIdx.x) - kWave * xw0;  // x thread
   const int nxt = NT - kWave * xw0;
   const bool xreg = nch <= nxt * XC;
   u32x4 xr[XC][2];
+  float lv8[P8];
+  if constexpr (kWide) topk_wave_load<P8>(logits, L.E, wid, lane, lv8);
   if (wid >= xw0) issue_x<BF16, XC>(x, nch, xreg, xr, xt, nxt);
   if (L.slot_of)
     for (int i = threadIdx.x; i < L.E; i += NT) s_slotmap[i] = L.slot_of[i];
-  if (wid < T) {
+  if constexpr (kWide) topk_wave_select<P8>(lv8, L.E, k, wid, lane, s_cand);
+  if (!kWide && wid < T) {
     if constexpr (RPER > 0) {
       int my_e;
       float wt;
@@ -699,7 +839,7 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
     }
   }
   if (wid >= xw0) {
-    token_partials<BF16, XC>(x, T, H, xreg, xr, s_stat, xt, nxt);
+    token_partials<BF16, XC, TM>(x, T, H, xreg, xr, s_stat, xt, nxt);
   } else if (lane < kMaxT) {
     s_stat[wid][lane][0] = 0.0f;
     s_stat[wid][lane][1] = 0.0f;
@@ -708,16 +848,18 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
   {
     // the multipliers live in registers only while x is staged; the epilogue
     // and the header read the fp16 normalisers from LDS
-    float rmul[kMaxT], smul[kMaxT];
-    token_derive<NW>(T, H, prenorm, s_stat, rmul, smul);
+    float rmul[TM], smul[TM];
+    token_derive<NW, TM>(T, H, prenorm, s_stat, rmul, smul);
     if (threadIdx.x == 0) {
 #pragma unroll
-      for (int t = 0; t < kMaxT; ++t) s_smul[t] = smul[t];
+      for (int t = 0; t < TM; ++t) s_smul[t] = smul[t];
     }
-    if constexpr (RPER > 0) {
+    if constexpr (kWide) {
+      topk_rank_candidates<NW>(k, wid, lane, s_cand, S, s_logit, L.shared != nullptr);
+    } else if constexpr (RPER > 0) {
       if (wid == 0 && T > 1) build_slots(s_rid, s_rw, T, k, L.E, L.shared != nullptr, S, s_slot_of, false);
     }
-    if (wid >= xw0) stage_x<BF16, XC>(x, T, H, xreg, xr, rmul, smul, xs, xt, nxt);
+    if (wid >= xw0) stage_x<BF16, XC, TM>(x, T, H, xreg, xr, rmul, smul, xs, xt, nxt);
   }
   __syncthreads();
   const int n_rows = (SPLIT ? S.n - 1 : S.n) * RTI;   // SPLIT: the routed slots only
@@ -728,6 +870,21 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
 
   GateUpTiles<KTW> R;
   load_gateup<KTW>(expert_base(L, active ? S.expert[slot] : 0, s_slotmap), active, H, I, rt, kq, lane, R);
+  if constexpr (kWide) {
+    // the routing weights, while the weight tiles are in flight (the
+    // epilogue reads them after the next barrier)
+    if (wid == 0) {
+      const float l = lane < k ? s_logit[lane] : 0.0f;
+      const float wt = topk_weight(l, k, lane);
+      if (lane < k) {
+        S.wpair[lane] = wt;
+        if (blockIdx.x == 0 && ids_out) {
+          ids_out[lane] = S.expert[lane];
+          w_out[lane] = wt;
+        }
+      }
+    }
+  }
   int8_t* hexp = reinterpret_cast<int8_t*>(ws + kHeaderBytes + decode_h_bytes(T, k, I));
   if (blockIdx.x == 0) {
     DecodeHeader* hdr = reinterpret_cast<DecodeHeader*>(ws);
@@ -764,8 +921,8 @@ __global__ __launch_bounds__(256 * RTW) void decode_gateup_kernel(
     }
   }
   if (static_cast<int>(blockIdx.x) >= n_rows) return;
-  gateup_compute<KTW>(R, xs, T, H, I, rt, kq, slot, active, S, s_smul, s_red,
-                      reinterpret_cast<_Float16*>(ws + kHeaderBytes), hexp);
+  gateup_compute<KTW, TM>(R, xs, T, H, I, rt, kq, slot, active, S, s_smul, s_red,
+                          reinterpret_cast<_Float16*>(ws + kHeaderBytes), hexp);
 }
 
 // Kernel 2: down row tile blockIdx.x.
@@ -773,7 +930,7 @@ constexpr int kExpPre = 2;               // exponent vectors per lane loaded at 
 
 // NTD threads: 8 waves for one token, 16 for more (each wave's chain of
 // dependent loads shorter when the slots are many).
-template <bool STAGED, int DB, int NTD>
+template <bool STAGED, int DB, int NTD, int TM>
 __global__ __launch_bounds__(NTD) void decode_down_kernel(
     LayerArgs L, int T, int k, const void* __restrict__ residual, void* __restrict__ out,
     int out_bf16, const uint8_t* __restrict__ ws) {
@@ -838,16 +995,16 @@ __global__ __launch_bounds__(NTD) void decode_down_kernel(
   // E_t: the largest exponent over the token's pairs and row tiles (pairs
   // without a row carry kZeroExp, which never wins); every wave derives it,
   // wave 0 publishes it in LDS (indexed by a per-lane token later)
-  int et[kMaxT];
+  int et[TM];
   {
-    int lm[kMaxT];
+    int lm[TM];
 #pragma unroll
-    for (int t = 0; t < kMaxT; ++t) lm[t] = kZeroExp;
+    for (int t = 0; t < TM; ++t) lm[t] = kZeroExp;
     auto take = [&](int v, const u32x4& e16) {
       const int t = pair_token(v / vpp, T, k);
       const int mx = max_i8x16(e16);
 #pragma unroll
-      for (int q = 0; q < kMaxT; ++q) lm[q] = (q == t) ? max(lm[q], mx) : lm[q];
+      for (int q = 0; q < TM; ++q) lm[q] = (q == t) ? max(lm[q], mx) : lm[q];
     };
 #pragma unroll
     for (int q = 0; q < kExpPre; ++q)
@@ -855,11 +1012,13 @@ __global__ __launch_bounds__(NTD) void decode_down_kernel(
     for (int v = lane + kWave * kExpPre; v < nvec; v += kWave)
       take(v, *reinterpret_cast<const u32x4*>(hexp + 16 * v));
 #pragma unroll
-    for (int t = 0; t < kMaxT; ++t)
+    for (int t = 0; t < TM; ++t)
       et[t] = t < T ? static_cast<int>(__ockl_wfred_max_u32(static_cast<uint32_t>(lm[t] + 256))) - 256 : 0;
     if (threadIdx.x == 0) {
 #pragma unroll
-      for (int t = 0; t < kMaxT; ++t) s_et[t] = et[t];
+      for (int t = 0; t < TM; ++t) s_et[t] = et[t];
+#pragma unroll
+      for (int t = TM; t < kMaxT; ++t) s_et[t] = 0;
     }
   }
   __syncthreads();
@@ -905,7 +1064,7 @@ __global__ __launch_bounds__(NTD) void decode_down_kernel(
     load_down<DB, NTD / kWave>(L, s_base, nitems, KTd, rt, j0, lane, D);
     mma_down<DB, STAGED, NTD / kWave>(D, nitems, KTd, j0, lane, hsrc, s_pidx, T, I, hexp, s_et, acc);
   }
-  down_store<NTD / kWave>(acc, s_red, rt, T, L.H, s_et, residual, out, out_bf16);
+  down_store<NTD / kWave, TM>(acc, s_red, rt, T, L.H, s_et, residual, out, out_bf16);
 }
 
 // -------------------------------------------------------------- launching --
@@ -927,10 +1086,17 @@ struct DecodeArgs {
 
 constexpr size_t kHStageLimit = 144 * 1024;  // largest h~ staged in LDS (one block per CU)
 
+// One token gets kernels compiled for one token (TM = 1): the per-token
+// loops of the x path, the epilogue and the down kernel become straight-line
+// code; verify windows take TM = kMaxT.
 template <int KTW, bool BF16, int RPER, int RTW, bool SPLIT = false>
 hipError_t launch_gateup4(const LayerArgs& L, int grid, uint32_t lds, hipStream_t s,
                           const DecodeArgs& a, int n_rwg = 0) {
-  return launch_kernel(K_DECODE_GATEUP, decode_gateup_kernel<KTW, BF16, RPER, RTW, SPLIT>, dim3(grid),
+  if (a.T == 1)
+    return launch_kernel(K_DECODE_GATEUP, decode_gateup_kernel<KTW, BF16, RPER, RTW, SPLIT, 1>, dim3(grid),
+                         dim3(256 * RTW), lds, s, L, a.x, a.T, a.ids, a.w, a.logits, a.ids_out,
+                         a.w_out, a.k, a.prenorm, a.ws, n_rwg);
+  return launch_kernel(K_DECODE_GATEUP, decode_gateup_kernel<KTW, BF16, RPER, RTW, SPLIT, kMaxT>, dim3(grid),
                        dim3(256 * RTW), lds, s, L, a.x, a.T, a.ids, a.w, a.logits, a.ids_out,
                        a.w_out, a.k, a.prenorm, a.ws, n_rwg);
 }
@@ -1044,10 +1210,11 @@ hipError_t launch_decode(const LayerArgs& L, const void* x, int x_bf16, int T,
     const uint32_t lds = static_cast<uint32_t>(ST ? lds_h : 0);
     const uint8_t* w8 = static_cast<const uint8_t*>(ws);
     return down_threads == kThreads
-               ? launch_kernel(K_DECODE_DOWN, decode_down_kernel<ST, DBv, kThreads>, dim3(L.H / kTileRows),
+               ? launch_kernel(K_DECODE_DOWN, decode_down_kernel<ST, DBv, kThreads, 1>, dim3(L.H / kTileRows),
                                dim3(kThreads), lds, s, L, T, k, residual, out, out_bf16, w8)
-               : launch_kernel(K_DECODE_DOWN, decode_down_kernel<ST, DBv, 2 * kThreads>, dim3(L.H / kTileRows),
-                               dim3(2 * kThreads), lds, s, L, T, k, residual, out, out_bf16, w8);
+               : launch_kernel(K_DECODE_DOWN, decode_down_kernel<ST, DBv, 2 * kThreads, kMaxT>,
+                               dim3(L.H / kTileRows), dim3(2 * kThreads), lds, s, L, T, k, residual, out,
+                               out_bf16, w8);
   };
   auto down_db = [&](auto staged) {
     switch (per_wave) {

@@ -282,6 +282,7 @@ ROUTED_CASES = [
     ((1, 512, 3072, 768), 1, 10, "ties", "bf16"),      # block-wide top-k, ties across slices
     ((7, 1024, 512, 256), 1, 16, "ties", "f32"),
     ((8, 300, 512, 512), 1, 7, "normal", "f32"),       # slices not a multiple of 64
+    ((9, 16, 512, 256), 1, 16, "ties", "f32"),         # k = E: one wave holds every expert
     ((1, 512, 3072, 768), 2, 10, "zipf", "bf16"),
     ((1, 512, 3072, 768), 3, 10, "zipf", "bf16"),
     ((1, 512, 3072, 768), 4, 10, "ties", "bf16"),
