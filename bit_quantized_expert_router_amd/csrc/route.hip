@@ -49,7 +49,11 @@ struct RouteFinish {
 };
 constexpr int kRouteFusedPairs = 16 * MOE_MAX_TOPK;   // one chunk of at most 16 tokens
 
-template <int PER>
+// WIDE: one token on 8 waves (topk_wave_select / topk_rank8): each wave
+// selects from its slice of the logits, the candidates are ranked after a
+// barrier, and wave 0 computes the weights from the ranked logits -- the
+// ids, weights and histogram equal those of one wave taking the whole row.
+template <int PER, bool WIDE>
 __global__ __launch_bounds__(1024) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int chunk_tokens,
     int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ rank,
@@ -58,6 +62,9 @@ __global__ __launch_bounds__(1024) void route_topk_kernel(
   __shared__ int32_t s_cnt[MOE_MAX_EXPERTS];
   __shared__ int32_t s_rank[kRouteFusedPairs];
   __shared__ int32_t s_off[MOE_MAX_EXPERTS];
+  __shared__ uint64_t s_cand[WIDE ? 8 : 1][kTopkCand];
+  __shared__ int32_t s_wid[kTopkCand];
+  __shared__ float s_wlg[kTopkCand];
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const int nwaves = blockDim.x / kWave;
@@ -68,16 +75,44 @@ __global__ __launch_bounds__(1024) void route_topk_kernel(
   if (rank) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) s_cnt[e] = 0;
   }
-  for (int ti = wid; ti < nt; ti += nwaves) {
-    const int t = t0 + ti;
-    int my_e;
-    float l;
-    topk_one_token<PER>(logits + static_cast<size_t>(t) * E, E, k, lane, my_e, l);
-    const float wt = topk_weight(l, k, lane);
-    if (lane < k) {
-      ids[static_cast<size_t>(t) * k + lane] = my_e;
-      w[static_cast<size_t>(t) * k + lane] = wt;
-      if (rank) s_ids[ti * k + lane] = my_e;
+  if constexpr (WIDE) {
+    // T = 1, one chunk, 8 waves
+    static_assert(kTopkCand >= MOE_MAX_TOPK, "candidates per wave");
+    constexpr int P8 = PER / 8 > 0 ? PER / 8 : 1;
+    float lv[P8];
+    topk_wave_load<P8>(logits, E, wid, lane, lv);
+    topk_wave_select<P8>(lv, E, k, wid, lane, s_cand);
+    __syncthreads();
+    int r;
+    uint64_t mc;
+    topk_rank8(s_cand, wid, lane, r, mc);
+    if (lane < k && r < k) {
+      s_wid[r] = static_cast<int>(~static_cast<uint32_t>(mc));
+      s_wlg[r] = key_float(static_cast<uint32_t>(mc >> 32));
+    }
+    __syncthreads();
+    if (wid == 0) {
+      const float l = lane < k ? s_wlg[lane] : 0.0f;
+      const float wt = topk_weight(l, k, lane);
+      if (lane < k) {
+        const int e = s_wid[lane];
+        ids[lane] = e;
+        w[lane] = wt;
+        if (rank) s_ids[lane] = e;
+      }
+    }
+  } else {
+    for (int ti = wid; ti < nt; ti += nwaves) {
+      const int t = t0 + ti;
+      int my_e;
+      float l;
+      topk_one_token<PER>(logits + static_cast<size_t>(t) * E, E, k, lane, my_e, l);
+      const float wt = topk_weight(l, k, lane);
+      if (lane < k) {
+        ids[static_cast<size_t>(t) * k + lane] = my_e;
+        w[static_cast<size_t>(t) * k + lane] = wt;
+        if (rank) s_ids[ti * k + lane] = my_e;
+      }
     }
   }
   if (!rank) return;
@@ -336,11 +371,14 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
   const RouteFinish fin = (rank && counts && route_histogram_fused(T, k))
                               ? RouteFinish{counts, offsets, sorted_pairs, pair_pos}
                               : RouteFinish{nullptr, nullptr, nullptr, nullptr};
-  const int threads = T <= 4 ? 64 * T : 1024;
+  // one token: 8 waves share its top-k; 2..4 tokens: one wave each
+  const int threads = T == 1 ? 8 * kWave : T <= 4 ? 64 * T : 1024;
   const int per = (E + kWave - 1) / kWave;
-#define MOE_ROUTE_LAUNCH(P)                                                                 \
-  launch_kernel(K_ROUTE_TOPK, route_topk_kernel<P>, dim3(n_chunks), dim3(threads), 0, s, logits, \
-                T, E, k, ct, ids, w, rank, local_counts, n_chunks, fin)
+#define MOE_ROUTE_LAUNCH(P)                                                                         \
+  (T == 1 ? launch_kernel(K_ROUTE_TOPK, route_topk_kernel<P, true>, dim3(n_chunks), dim3(threads), 0, s, \
+                          logits, T, E, k, ct, ids, w, rank, local_counts, n_chunks, fin)                  \
+          : launch_kernel(K_ROUTE_TOPK, route_topk_kernel<P, false>, dim3(n_chunks), dim3(threads), 0, s, \
+                          logits, T, E, k, ct, ids, w, rank, local_counts, n_chunks, fin))
   if (per <= 1) return MOE_ROUTE_LAUNCH(1);
   if (per <= 2) return MOE_ROUTE_LAUNCH(2);
   if (per <= 4) return MOE_ROUTE_LAUNCH(4);

@@ -132,6 +132,103 @@ __device__ __forceinline__ void topk_one_token(const float* __restrict__ row, in
   my_l = key_float(my_key);
 }
 
+// Candidates kept per wave by topk_wave_select (at least the largest k).
+constexpr int kTopkCand = 16;
+
+// One token's top-k on the 8 waves of a workgroup (the routed workgroups of
+// the one-token decode launch, and the one-token routing launch).  Wave w
+// takes experts [w * 64 * P, (w + 1) * 64 * P), P per lane (lane l: ids
+// w * 64 * P + l * P + i), and keeps its own top k: the keys above the
+// wave's k-th largest key (found by bisection on the key bits, each step one
+// compare and a population count of its ballot) and, among the keys equal to
+// it, the lowest ids.  The union of the waves' own top k holds the global
+// top k.  After a barrier, topk_rank8 counts for every candidate how many of
+// the 8 * k beat it: that count is its rank in the global selection order.
+// Candidates are kept as (key << 32) | ~id: a larger value is the better
+// candidate (equal keys: the lower id), and no two are equal.  s_cand has
+// 16 entries per wave; unused entries hold 0, which no candidate of a valid
+// expert (key > 0) loses to.
+template <int P>
+__device__ __forceinline__ void topk_wave_load(const float* __restrict__ row, int E, int wid, int lane,
+                                               float (&lv)[P]) {
+  const int base = wid * kWave * P + lane * P;
+#pragma unroll
+  for (int i = 0; i < P; ++i) lv[i] = row[min(base + i, E - 1)];
+}
+
+template <int P>
+__device__ __forceinline__ void topk_wave_select(const float (&lv)[P], int E, int k, int wid, int lane,
+                                                 uint64_t (*s_cand)[kTopkCand]) {
+  uint32_t key[P];
+  const int base = wid * kWave * P + lane * P;
+#pragma unroll
+  for (int i = 0; i < P; ++i) key[i] = base + i < E ? float_key(lv[i]) : 0u;
+  // tau = the largest value with at least k keys >= tau: the k-th largest key
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = tau | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) cnt += __popcll(__ballot(key[i] >= c));
+    tau = cnt >= k ? c : tau;
+  }
+  // fewer than k keys lie above tau; the rest of the k are the lowest ids
+  // among the keys equal to tau (ids ascend with (lane, i))
+  int n_gt = 0;
+  uint64_t eq[P], gt[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    gt[i] = __ballot(key[i] > tau);
+    eq[i] = __ballot(key[i] == tau);
+    n_gt += __popcll(gt[i]);
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  int ties_before = 0;     // keys equal to tau in lower lanes
+#pragma unroll
+  for (int i = 0; i < P; ++i) ties_before += __popcll(eq[i] & below);
+  if (lane < kTopkCand && lane >= k) s_cand[wid][lane] = 0ull;
+  {
+    int gt_before = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) gt_before += __popcll(gt[i] & below);
+    int t_lo = ties_before, g_lo = gt_before;   // counts of lower ids, then this lane's earlier entries
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const bool is_gt = key[i] > tau;
+      const bool is_eq = key[i] == tau;
+      const bool take = is_gt || (is_eq && t_lo < k - n_gt);
+      // position: selected entries of lower ids (all the greater ones, and
+      // the equal ones that are taken)
+      const int pos = g_lo + min(t_lo, k - n_gt);
+      if (take) s_cand[wid][pos] = (static_cast<uint64_t>(key[i]) << 32) | static_cast<uint32_t>(~(base + i));
+      g_lo += is_gt ? 1 : 0;
+      t_lo += is_eq ? 1 : 0;
+    }
+  }
+}
+
+// Ranks of the candidates: each lane holds two of the 128 entries (waves
+// 0..3 and 4..7); for each of its wave's 16 entries (read from LDS by every
+// lane) a wave counts the entries that beat it with two ballots, the counts
+// independent of each other, and lane j (< 16) gets entry j's count in rank
+// and the entry itself in mc (entries past k hold 0 and rank last).
+__device__ __forceinline__ void topk_rank8(const uint64_t (*s_cand)[kTopkCand], int wid, int lane,
+                                           int& rank, uint64_t& mc) {
+  static_assert(8 * kTopkCand == 2 * kWave, "two entries per lane");
+  const uint64_t* flat = &s_cand[0][0];
+  const uint64_t c0 = flat[lane], c1 = flat[kWave + lane];
+  mc = s_cand[wid][lane & (kTopkCand - 1)];
+  uint64_t mj[kTopkCand];
+#pragma unroll
+  for (int j = 0; j < kTopkCand; ++j) mj[j] = s_cand[wid][j];
+  rank = kTopkCand;
+#pragma unroll
+  for (int j = 0; j < kTopkCand; ++j) {
+    const int r = __popcll(__ballot(c0 > mj[j])) + __popcll(__ballot(c1 > mj[j]));
+    rank = lane == j ? r : rank;
+  }
+}
+
 // Weight of slot `lane` (< k) of a token whose selected logits sit in lanes
 // 0..k-1 in descending order: exp(l - l_0) / sum over the k slots.
 __device__ __forceinline__ float topk_weight(float l, int k, int lane) {

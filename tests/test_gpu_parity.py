@@ -90,6 +90,10 @@ ROUTE_CASES = [
     (4096, 512, 10, "biased"), (5000, 64, 4, "normal"), (70000, 64, 4, "normal"),
     # the single-launch histogram at its limit (one chunk, 256 pairs) and just past it
     (16, 64, 16, "ties"), (17, 64, 15, "ties"),
+    # one token on 8 waves: ties across slices, two logits per lane, E not a
+    # multiple of 64, k = E, slices left empty
+    (1, 512, 10, "ties"), (1, 1024, 16, "ties"), (1, 300, 7, "normal"), (1, 16, 16, "ties"),
+    (1, 8, 3, "const"), (1, 512, 10, "const"),
 ]
 
 
